@@ -1,0 +1,201 @@
+/*
+ * moge.h -- C ABI of libmoge, the forward pass of one MoGE (Mixture of Grouped
+ * Experts) layer on an AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (web pages about "Pangu Pro MoE: Mixture of Grouped Experts
+ * for Efficient Sparsity", arXiv 2505.21411):
+ *   [P1] lsdiaocha.cn long-form summary of the paper, section 1 (architecture):
+ *        N experts split evenly into M groups of N/M, one group per device;
+ *        each token takes a softmax over all N experts and then keeps the
+ *        K' = K/M best experts inside every group; the imbalance score is the
+ *        workload gap between the busiest and the idlest device, and is zero
+ *        for MoGE by construction.
+ *   [P5] hyper.ai page with the paper's abstract: tokens activate an equal
+ *        number of experts in each predefined group.
+ *   [P4] reportify.cn digests of Pangu Ultra MoE (dropless training, one
+ *        always-on shared expert).
+ * The expert is a SwiGLU feed-forward block without biases:
+ *   FFN_e(x) = W_down[e] . ( silu(W_gate[e] . x) * (W_up[e] . x) ).
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees device memory and keeps no global state.
+ *   - Dense tensors are row-major and contiguous.  Weights use the
+ *     (out_features, in_features) layout of a linear layer:
+ *       w_router [N][d];  w_gate, w_up [E][F][d];  w_down [E][d][F]
+ *     where E is the number of experts the array holds (see moge_grouped_ffn).
+ *   - dtype MOGE_BF16: x, weights, x_perm, h and expert outputs are bf16
+ *     (uint16 bit patterns); logits, gates and y are float32; bf16 matrix
+ *     products use MFMA with float32 accumulation.
+ *     dtype MOGE_F32: every tensor is float32 and products use plain float32
+ *     vector arithmetic.
+ *   - Every call validates its arguments on the host BEFORE any launch and
+ *     returns a status; on error nothing is launched and moge_last_error()
+ *     (per thread) describes the problem.  On success the work is enqueued on
+ *     `stream` and the call returns without waiting for it.
+ *   - Calls on different streams are independent; the library is re-entrant.
+ */
+#ifndef MOGE_H
+#define MOGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOGE_OK = 0,
+  MOGE_ERR_ARG = 1,        /* an argument is out of range (mode, expert range, ...) */
+  MOGE_ERR_SHAPE = 2,      /* the shape breaks a rule listed at moge_shape_t */
+  MOGE_ERR_NULL = 3,       /* a required pointer is NULL */
+  MOGE_ERR_WORKSPACE = 4,  /* workspace missing or smaller than moge_workspace_size() */
+  MOGE_ERR_DTYPE = 5,      /* unknown dtype */
+  MOGE_ERR_HIP = 6,        /* a HIP launch failed (message has the HIP error) */
+  MOGE_ERR_CAPACITY = 7    /* rows_cap is below the row bound of the call */
+} moge_status_t;
+
+typedef enum { MOGE_BF16 = 0, MOGE_F32 = 1 } moge_dtype_t;
+
+/* MOGE_ROUTE_GROUPED: MoGE, top-K' inside each of the M groups ([P1] section 1).
+ * MOGE_ROUTE_GLOBAL:  the conventional router, top-K over all N experts with
+ *                     K = M*K' ([P1] section 1 contrasts MoGE with it). */
+typedef enum { MOGE_ROUTE_GROUPED = 0, MOGE_ROUTE_GLOBAL = 1 } moge_route_mode_t;
+
+/* Workspace stages for moge_workspace_size(). */
+typedef enum { MOGE_STAGE_DISPATCH = 1 } moge_stage_t;
+
+/*
+ * Layer shape.  Rules checked by moge_validate():
+ *   T >= 1 tokens; d >= 8 hidden, d % 8 == 0; 1 <= M <= N experts, N % M == 0;
+ *   1 <= k_per_group (K') <= N/M; K = M*K' slots per token;
+ *   F expert width: F == 0 (routing only) or F >= 8 with F % 8 == 0;
+ *   T*K < 2^31;  N <= 256 (both dtypes);  dtype in moge_dtype_t.
+ * Groups are contiguous blocks of expert ids: group(e) = e / (N/M).
+ */
+typedef struct {
+  int32_t T;
+  int32_t d;
+  int32_t N;
+  int32_t M;
+  int32_t k_per_group;
+  int32_t F;
+  int32_t dtype;
+} moge_shape_t;
+
+/* Host-only shape check (no device call; usable without a GPU). */
+moge_status_t moge_validate(const moge_shape_t* shape);
+
+/* Largest number of rows that (t, slot) pairs of experts in [e_lo, e_hi) can
+ * produce under `mode`: GROUPED -> T * sum_g min(K', |[e_lo,e_hi) & group g|);
+ * GLOBAL -> T * min(K, e_hi - e_lo).  Returns -1 on invalid arguments.
+ * Buffers x_perm, h and expert outputs need this many rows. */
+int64_t moge_rows_bound(const moge_shape_t* shape, int32_t mode, int32_t e_lo, int32_t e_hi);
+
+/* Bytes of device workspace a stage needs (0 if none; (size_t)-1 if invalid). */
+size_t moge_workspace_size(const moge_shape_t* shape, int32_t stage);
+
+/*
+ * moge_route -- router scores, global softmax, top-K' per group ([P1] section 1).
+ *   x        [T][d] (dtype) or NULL; w_router [N][d] (dtype); bias [N] f32 or NULL.
+ *   logits   [T][N] f32.  If x != NULL: scores are computed as x.w_router^T (+bias)
+ *            with float32 accumulation and, when logits != NULL, also stored.
+ *            If x == NULL: logits is the INPUT (bias must then be NULL).
+ *   idx      [T][K] int32 out: chosen expert ids.
+ *   gate     [T][K] f32 out: the chosen experts' probabilities under the softmax
+ *            over all N scores (not renormalised over the chosen experts).
+ * Slot order: GROUPED -> slot = g*K' + rank inside group g; GLOBAL -> slot = rank.
+ * rank orders experts by score, higher first, equal scores -> lower expert id.
+ * Scores must be finite.
+ */
+moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, const void* x, const void* w_router,
+                         const float* bias, float* logits, int32_t* idx, float* gate, hipStream_t stream);
+
+/*
+ * moge_dispatch -- per-expert counts and the token permutation (dropless: every
+ * (token, slot) pair gets a row; [P4]), plus the gather of x into expert order.
+ *   idx      [T][K] int32 from moge_route with the same `mode`.
+ *   x        [T][d] (dtype).
+ *   [e_lo, e_hi) experts whose rows are materialised (a device's share, e.g.
+ *            one group); 0 <= e_lo < e_hi <= N.
+ *   rows_cap rows available in perm / x_perm; must be >= moge_rows_bound().
+ *   counts   [N] int32 out: rows per expert (all N experts).
+ *   offsets  [N+1] int32 out: exclusive prefix sum of counts (all N experts).
+ *   inv      [T][K] int32 out: local row of (t, slot) = offsets[e] - offsets[e_lo]
+ *            + #{t' < t that chose e}; -1 when the expert is outside [e_lo, e_hi).
+ *   perm     [rows_cap] int32 out: token of each local row (rows >= the live
+ *            count offsets[e_hi]-offsets[e_lo] are left untouched).
+ *   x_perm   [rows_cap][d] (dtype) out: x_perm[r] = x[perm[r]].
+ *   ws       device workspace of moge_workspace_size(shape, MOGE_STAGE_DISPATCH) bytes.
+ * Rows of one expert are in ascending token order, so the result is unique and
+ * deterministic.  Expert ids outside [0, N) in idx are ignored (memory-safe).
+ * Lighter forms: x and x_perm both NULL -> no row copies; additionally inv and
+ * perm both NULL -> counts and offsets only (rows_cap is then not checked), e.g.
+ * for the load of the global top-K comparator.
+ */
+moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
+                            int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts, int32_t* offsets,
+                            int32_t* inv, int32_t* perm, void* x_perm, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * moge_grouped_ffn -- the SwiGLU expert applied to every expert's row segment
+ * (a grouped GEMM pair).
+ *   x_perm   [rows_cap][d]; local row r belongs to expert e when
+ *            offsets[e]-offsets[e_lo] <= r < offsets[e+1]-offsets[e_lo].
+ *   offsets  [N+1] int32 device (from moge_dispatch).
+ *   w_gate, w_up [e_hi-e_lo][F][d]; w_down [e_hi-e_lo][d][F]: the arrays hold
+ *            experts e_lo .. e_hi-1 only (a device's share of the weights).
+ *   h        [rows_cap][F] scratch (dtype): silu(x.Wg^T) * (x.Wu^T), rounded to
+ *            dtype before the down projection.
+ *   out      [rows_cap][d] (dtype): FFN_e(x_perm[r]) for every live row.
+ * The always-on shared expert is the same call with a one-expert shape
+ * (N = M = k_per_group = 1, F = shared width), offsets = {0, T} and x_perm = x.
+ */
+moge_status_t moge_grouped_ffn(const moge_shape_t* shape, const void* x_perm, const int32_t* offsets,
+                               int32_t e_lo, int32_t e_hi, int64_t rows_cap, const void* w_gate,
+                               const void* w_up, const void* w_down, void* h, void* out, hipStream_t stream);
+
+/*
+ * The two halves of moge_grouped_ffn, for callers that schedule or time them
+ * separately (same arguments and rules as moge_grouped_ffn):
+ *   moge_expert_gate_up: h   = silu(x_perm . Wg^T) * (x_perm . Wu^T)  per expert segment
+ *   moge_expert_down:    out = h . Wd^T                               per expert segment
+ */
+moge_status_t moge_expert_gate_up(const moge_shape_t* shape, const void* x_perm, const int32_t* offsets,
+                                  int32_t e_lo, int32_t e_hi, int64_t rows_cap, const void* w_gate, const void* w_up,
+                                  void* h, hipStream_t stream);
+moge_status_t moge_expert_down(const moge_shape_t* shape, const void* h, const int32_t* offsets, int32_t e_lo,
+                               int32_t e_hi, int64_t rows_cap, const void* w_down, void* out, hipStream_t stream);
+
+/*
+ * moge_combine -- gate-weighted sum of the expert outputs back in token order.
+ *   y[t] = sum over slots s (in slot order) with inv[t][s] >= 0 of
+ *          gate[t][s] * o[inv[t][s]]   (+ shared_out[t] when not NULL), in float32.
+ *   o [rows_cap][d] (dtype), inv/gate [T][K], shared_out [T][d] (dtype) or NULL,
+ *   y [T][d] f32.  Rows inv >= rows_cap are ignored (memory-safe).
+ */
+moge_status_t moge_combine(const moge_shape_t* shape, const void* o, const int32_t* inv, const float* gate,
+                           int64_t rows_cap, const void* shared_out, float* y, hipStream_t stream);
+
+/*
+ * moge_imbalance -- per-device (per-group) load and the imbalance score ([P1]
+ * section 1: busiest minus idlest device in the batch).
+ *   counts [N] int32 (from moge_dispatch); group_load [M] int32 out =
+ *   sum of counts over the group's experts; is_raw [1] int32 out = max - min;
+ *   is_norm [1] double out = is_raw / T.  All device pointers.
+ */
+moge_status_t moge_imbalance(const moge_shape_t* shape, const int32_t* counts, int32_t* group_load,
+                             int32_t* is_raw, double* is_norm, hipStream_t stream);
+
+/* Library version string and the calling thread's last error message. */
+const char* moge_version(void);
+const char* moge_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOGE_H */

@@ -1,0 +1,10 @@
+"""libmoge: the forward pass of one MoGE (Mixture of Grouped Experts) layer on MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of ``include/moge.h``
+(``libmoge.so``).  This package is the thin Python binding (``_lib``: ctypes marshalling)
+plus ``layer.MoGELayer``, which owns device buffers and issues the ABI calls of one layer
+forward in order.  PyTorch is used only for device memory and streams.
+"""
+from ._lib import (BF16, F32, ROUTE_GLOBAL, ROUTE_GROUPED, STAGE_DISPATCH, EXPORTS, LIB_PATH, MogeError, Shape,  # noqa: F401
+                   combine, dispatch, expert_down, expert_gate_up, grouped_ffn, imbalance, last_error, route, rows_bound, validate, version,
+                   workspace_size)

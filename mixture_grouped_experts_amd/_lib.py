@@ -1,0 +1,218 @@
+"""ctypes binding of libmoge (include/moge.h).
+
+Argument marshalling only: every call checks that the tensors are contiguous CUDA
+(HIP) tensors of the expected dtype and size, passes their device pointers and the
+current stream to the C entry point of the same name, and raises MogeError when the
+library returns an error.  No computation happens here.  If libmoge.so is missing
+this module fails at import time; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoge.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python __graft_entry__.py` (build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK = 0
+STATUS = {0: "MOGE_OK", 1: "MOGE_ERR_ARG", 2: "MOGE_ERR_SHAPE", 3: "MOGE_ERR_NULL", 4: "MOGE_ERR_WORKSPACE",
+          5: "MOGE_ERR_DTYPE", 6: "MOGE_ERR_HIP", 7: "MOGE_ERR_CAPACITY"}
+BF16 = 0
+F32 = 1
+ROUTE_GROUPED = 0
+ROUTE_GLOBAL = 1
+STAGE_DISPATCH = 1
+
+EXPORTS = ("moge_validate", "moge_rows_bound", "moge_workspace_size", "moge_route", "moge_dispatch",
+           "moge_grouped_ffn", "moge_expert_gate_up", "moge_expert_down", "moge_combine", "moge_imbalance",
+           "moge_version", "moge_last_error")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32), ("M", ctypes.c_int32),
+                ("k_per_group", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    @property
+    def K(self) -> int:
+        return self.M * self.k_per_group
+
+    def __repr__(self):
+        return (f"Shape(T={self.T}, d={self.d}, N={self.N}, M={self.M}, k_per_group={self.k_per_group}, "
+                f"F={self.F}, dtype={'bf16' if self.dtype == BF16 else 'f32'})")
+
+
+class MogeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_SP = ctypes.POINTER(Shape)
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+_lib.moge_validate.argtypes = [_SP]
+_lib.moge_validate.restype = ctypes.c_int
+_lib.moge_rows_bound.argtypes = [_SP, _I32, _I32, _I32]
+_lib.moge_rows_bound.restype = _I64
+_lib.moge_workspace_size.argtypes = [_SP, _I32]
+_lib.moge_workspace_size.restype = ctypes.c_size_t
+_lib.moge_route.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _P]
+_lib.moge_route.restype = ctypes.c_int
+_lib.moge_dispatch.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.moge_dispatch.restype = ctypes.c_int
+_lib.moge_grouped_ffn.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P]
+_lib.moge_grouped_ffn.restype = ctypes.c_int
+_lib.moge_expert_gate_up.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P]
+_lib.moge_expert_gate_up.restype = ctypes.c_int
+_lib.moge_expert_down.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P]
+_lib.moge_expert_down.restype = ctypes.c_int
+_lib.moge_combine.argtypes = [_SP, _P, _P, _P, _I64, _P, _P, _P]
+_lib.moge_combine.restype = ctypes.c_int
+_lib.moge_imbalance.argtypes = [_SP, _P, _P, _P, _P, _P]
+_lib.moge_imbalance.restype = ctypes.c_int
+_lib.moge_version.argtypes = []
+_lib.moge_version.restype = ctypes.c_char_p
+_lib.moge_last_error.argtypes = []
+_lib.moge_last_error.restype = ctypes.c_char_p
+
+
+def _check(fn: str, st: int) -> None:
+    if st != OK:
+        raise MogeError(fn, st, _lib.moge_last_error().decode())
+
+
+def _elem_dtype(shape: Shape):
+    return torch.bfloat16 if shape.dtype == BF16 else torch.float32
+
+
+def _ptr(t, name: str, dtype=None, numel: int | None = None, optional: bool = False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def validate(shape: Shape) -> int:
+    return _lib.moge_validate(ctypes.byref(shape))
+
+
+def rows_bound(shape: Shape, mode: int, e_lo: int, e_hi: int) -> int:
+    return int(_lib.moge_rows_bound(ctypes.byref(shape), mode, e_lo, e_hi))
+
+
+def workspace_size(shape: Shape, stage: int = STAGE_DISPATCH) -> int:
+    return int(_lib.moge_workspace_size(ctypes.byref(shape), stage))
+
+
+def version() -> str:
+    return _lib.moge_version().decode()
+
+
+def last_error() -> str:
+    return _lib.moge_last_error().decode()
+
+
+def route(shape: Shape, mode: int, x, w_router, bias, logits, idx, gate, stream=None) -> None:
+    T, N, K, d = shape.T, shape.N, shape.K, shape.d
+    et = _elem_dtype(shape)
+    st = _lib.moge_route(ctypes.byref(shape), mode, _ptr(x, "x", et, T * d, optional=True),
+                         _ptr(w_router, "w_router", et, N * d, optional=x is None),
+                         _ptr(bias, "bias", torch.float32, N, optional=True),
+                         _ptr(logits, "logits", torch.float32, T * N, optional=x is not None),
+                         _ptr(idx, "idx", torch.int32, T * K), _ptr(gate, "gate", torch.float32, T * K),
+                         _stream(stream))
+    _check("moge_route", st)
+
+
+def dispatch(shape: Shape, mode: int, idx, x, e_lo: int, e_hi: int, rows_cap: int, counts, offsets, inv, perm,
+             x_perm, ws, stream=None) -> None:
+    T, N, K, d = shape.T, shape.N, shape.K, shape.d
+    et = _elem_dtype(shape)
+    st = _lib.moge_dispatch(ctypes.byref(shape), mode, _ptr(idx, "idx", torch.int32, T * K),
+                            _ptr(x, "x", et, T * d, optional=True), e_lo, e_hi, rows_cap,
+                            _ptr(counts, "counts", torch.int32, N), _ptr(offsets, "offsets", torch.int32, N + 1),
+                            _ptr(inv, "inv", torch.int32, T * K, optional=True),
+                            _ptr(perm, "perm", torch.int32, rows_cap, optional=True),
+                            _ptr(x_perm, "x_perm", et, rows_cap * d, optional=True), _ptr(ws, "ws", None, None),
+                            ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+    _check("moge_dispatch", st)
+
+
+def grouped_ffn(shape: Shape, x_perm, offsets, e_lo: int, e_hi: int, rows_cap: int, w_gate, w_up, w_down, h, out,
+                stream=None) -> None:
+    d, F = shape.d, shape.F
+    E = e_hi - e_lo
+    et = _elem_dtype(shape)
+    st = _lib.moge_grouped_ffn(ctypes.byref(shape), _ptr(x_perm, "x_perm", et, rows_cap * d),
+                               _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
+                               _ptr(w_gate, "w_gate", et, E * F * d), _ptr(w_up, "w_up", et, E * F * d),
+                               _ptr(w_down, "w_down", et, E * d * F), _ptr(h, "h", et, rows_cap * F),
+                               _ptr(out, "out", et, rows_cap * d), _stream(stream))
+    _check("moge_grouped_ffn", st)
+
+
+def expert_gate_up(shape: Shape, x_perm, offsets, e_lo: int, e_hi: int, rows_cap: int, w_gate, w_up, h,
+                   stream=None) -> None:
+    d, F = shape.d, shape.F
+    E = e_hi - e_lo
+    et = _elem_dtype(shape)
+    st = _lib.moge_expert_gate_up(ctypes.byref(shape), _ptr(x_perm, "x_perm", et, rows_cap * d),
+                                  _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
+                                  _ptr(w_gate, "w_gate", et, E * F * d), _ptr(w_up, "w_up", et, E * F * d),
+                                  _ptr(h, "h", et, rows_cap * F), _stream(stream))
+    _check("moge_expert_gate_up", st)
+
+
+def expert_down(shape: Shape, h, offsets, e_lo: int, e_hi: int, rows_cap: int, w_down, out, stream=None) -> None:
+    d, F = shape.d, shape.F
+    E = e_hi - e_lo
+    et = _elem_dtype(shape)
+    st = _lib.moge_expert_down(ctypes.byref(shape), _ptr(h, "h", et, rows_cap * F),
+                               _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
+                               _ptr(w_down, "w_down", et, E * d * F), _ptr(out, "out", et, rows_cap * d),
+                               _stream(stream))
+    _check("moge_expert_down", st)
+
+
+def combine(shape: Shape, o, inv, gate, rows_cap: int, shared_out, y, stream=None) -> None:
+    T, K, d = shape.T, shape.K, shape.d
+    et = _elem_dtype(shape)
+    st = _lib.moge_combine(ctypes.byref(shape), _ptr(o, "o", et, rows_cap * d), _ptr(inv, "inv", torch.int32, T * K),
+                           _ptr(gate, "gate", torch.float32, T * K), rows_cap,
+                           _ptr(shared_out, "shared_out", et, T * d, optional=True),
+                           _ptr(y, "y", torch.float32, T * d), _stream(stream))
+    _check("moge_combine", st)
+
+
+def imbalance(shape: Shape, counts, group_load, is_raw, is_norm, stream=None) -> None:
+    st = _lib.moge_imbalance(ctypes.byref(shape), _ptr(counts, "counts", torch.int32, shape.N),
+                             _ptr(group_load, "group_load", torch.int32, shape.M),
+                             _ptr(is_raw, "is_raw", torch.int32, 1), _ptr(is_norm, "is_norm", torch.float64, 1),
+                             _stream(stream))
+    _check("moge_imbalance", st)

@@ -1,0 +1,252 @@
+// moge_dispatch: per-expert counts and offsets, the stable token permutation and
+// the gather of token rows into expert order (dropless: every (token, slot) pair
+// gets a row; Pangu Ultra MoE digests on reportify.cn, dropless training).
+//
+// Three launches, no atomics on anything that decides an order:
+//   1. dispatch_hist_kernel   one workgroup per block of 256 tokens counts its
+//                             assignments per expert (LDS integer histogram).
+//   2. dispatch_scan_kernel   one workgroup per expert scans that expert's block
+//                             counts -> per-block starting rows and counts[e].
+//   3. dispatch_permute_kernel one workgroup per token block: offsets from counts,
+//                             then per wave (64 tokens, one per lane) a ballot
+//                             loop over the distinct experts of its tokens gives
+//                             every (token, slot) its row = block/wave base + number
+//                             of lower lanes that chose the same expert, so rows of
+//                             an expert stay in ascending token order; finally each
+//                             token row is read from HBM once and written to all of
+//                             its slots' rows with 16-byte coalesced stores.
+#include "moge_internal.hpp"
+
+namespace moge {
+
+constexpr int kTB = kDispatchTokens;
+
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(int64_t T, int K, int N, int64_t nb,
+                                                            const int32_t* __restrict__ idx,
+                                                            int32_t* __restrict__ bcount) {
+  __shared__ int hist[kMaxExperts];
+  for (int e = threadIdx.x; e < N; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t b = blockIdx.x;
+  const int64_t j0 = b * kTB * K;
+  const int64_t t1 = (b + 1) * kTB < T ? (b + 1) * kTB : T;
+  const int64_t j1 = t1 * K;
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
+    const int e = idx[j];
+    if ((unsigned)e < (unsigned)N) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += 256) bcount[(int64_t)e * nb + b] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int64_t nb, const int32_t* __restrict__ bcount,
+                                                            int32_t* __restrict__ bprefix,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int scratch[4];
+  const int64_t e = blockIdx.x;
+  const int32_t* src = bcount + e * nb;
+  int32_t* dst = bprefix + e * nb;
+  int running = 0;
+  for (int64_t c = 0; c < nb; c += 256) {
+    const int64_t i = c + threadIdx.x;
+    const int v = i < nb ? src[i] : 0;
+    int tot;
+    const int ex = block_exclusive_scan(v, scratch, &tot);
+    if (i < nb) dst[i] = running + ex;
+    running += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = running;
+}
+
+// Dynamic LDS: keys[kTB][KS] | rows[kTB][KS] | offs[N+1] | base[N] | hist[4][N]
+__global__ __launch_bounds__(256) void dispatch_permute_kernel(
+    int64_t T, int K, int N, int64_t nb, const int32_t* __restrict__ idx, const char* __restrict__ x,
+    int64_t row_bytes, int e_lo, int e_hi, int64_t rows_cap, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ bprefix, int32_t* __restrict__ offsets_out, int32_t* __restrict__ inv,
+    int32_t* __restrict__ perm, char* __restrict__ x_perm) {
+  // inv == nullptr: offsets only (launched with one workgroup); x_perm == nullptr: no row copies
+  extern __shared__ int lds[];
+  const int KS = K + 1;  // odd row stride: lanes of a wave hit distinct banks
+  int* keys = lds;
+  int* rows = keys + kTB * KS;
+  int* offs = rows + kTB * KS;
+  int* base = offs + (N + 1);
+  int* hist = base + N;  // [4][N]
+  __shared__ int scratch[4];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t b = blockIdx.x;
+  const int64_t t0 = b * kTB;
+
+  // offsets = exclusive prefix of counts (N <= 256: one pass)
+  {
+    const int e = threadIdx.x;
+    const int v = e < N ? counts[e] : 0;
+    int tot;
+    const int ex = block_exclusive_scan(v, scratch, &tot);
+    if (e < N) offs[e] = ex;
+    if (e == 0) offs[N] = tot;
+    __syncthreads();
+    if (b == 0) {
+      if (e < N) offsets_out[e] = ex;
+      if (e == 0) offsets_out[N] = tot;
+    }
+    if (e < N) base[e] = ex + bprefix[(int64_t)e * nb + b];
+  }
+  if (!inv) return;
+  // stage this block's expert ids; per-wave histograms
+  for (int i = threadIdx.x; i < 4 * N; i += 256) hist[i] = 0;
+  for (int i = threadIdx.x; i < kTB * K; i += 256) {
+    const int tl = i / K, s = i - tl * K;
+    const int64_t t = t0 + tl;
+    int e = -1;
+    if (t < T) {
+      e = idx[t * K + s];
+      if ((unsigned)e >= (unsigned)N) e = -1;
+    }
+    keys[tl * KS + s] = e;
+    rows[tl * KS + s] = -1;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTB * K; i += 256) {
+    const int tl = i / K, s = i - tl * K;
+    const int e = keys[tl * KS + s];
+    if (e >= 0) atomicAdd(&hist[(tl >> 6) * N + e], 1);
+  }
+  __syncthreads();
+  // per-wave starting row of every expert: block base + counts of lower waves
+  // (one thread per expert rewrites that expert's four entries in place)
+  for (int e = threadIdx.x; e < N; e += 256) {
+    int s = base[e];
+    for (int w = 0; w < 4; ++w) {
+      const int c = hist[w * N + e];
+      hist[w * N + e] = s;
+      s += c;
+    }
+  }
+  __syncthreads();
+
+  // rank: one distinct expert per iteration, all of its occurrences at once
+  {
+    const int tl = wave * 64 + lane;
+    const int* my = keys + tl * KS;
+    uint64_t pending = 0;
+    for (int s = 0; s < K; ++s)
+      if (my[s] >= 0) pending |= (1ull << s);
+    const int* wbase = hist + wave * N;
+    while (true) {
+      const uint64_t pm = __ballot(pending != 0);
+      if (pm == 0) break;
+      const int leader = __builtin_ctzll(pm);
+      const int first = pending ? my[__builtin_ctzll(pending)] : 0;
+      const int e = __builtin_amdgcn_readlane(first, leader);
+      int slot = -1;
+      for (int s = 0; s < K; ++s)
+        if (((pending >> s) & 1ull) && my[s] == e) slot = s;
+      const uint64_t m = __ballot(slot >= 0);
+      if (slot >= 0) {
+        rows[tl * KS + slot] = wbase[e] + lanes_below(m);
+        pending &= ~(1ull << slot);
+      }
+    }
+  }
+  __syncthreads();
+
+  // inv / perm, then the row copies (wave w copies its 64 tokens)
+  const int off_lo = offs[e_lo];
+  for (int i = threadIdx.x; i < kTB * K; i += 256) {
+    const int tl = i / K, s = i - tl * K;
+    const int64_t t = t0 + tl;
+    if (t >= T) continue;
+    const int e = keys[tl * KS + s];
+    int r = -1;
+    if (e >= e_lo && e < e_hi) {
+      r = rows[tl * KS + s] - off_lo;
+      if ((int64_t)r >= rows_cap || r < 0) r = -1;
+    }
+    rows[tl * KS + s] = r;
+    inv[t * K + s] = r;
+    if (r >= 0) perm[r] = (int32_t)t;
+  }
+  __syncthreads();
+  if (!x_perm) return;
+
+  const int64_t nch = row_bytes >> 4;  // 16-byte chunks per row
+  for (int j = 0; j < 64; ++j) {
+    const int tl = wave * 64 + j;
+    const int64_t t = t0 + tl;
+    if (t >= T) break;
+    const int* rr = rows + tl * KS;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + t * row_bytes);
+    for (int64_t c0 = 0; c0 < nch; c0 += 64 * 8) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < nch) v[u] = src[c];
+      }
+      for (int s = 0; s < K; ++s) {
+        const int r = rr[s];
+        if (r < 0) continue;
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(x_perm + (int64_t)r * row_bytes);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t c = c0 + u * 64 + lane;
+          if (c < nch) dst[c] = v[u];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace moge
+
+using namespace moge;
+
+extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
+                                       int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts,
+                                       int32_t* offsets, int32_t* inv, int32_t* perm, void* x_perm, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  moge_status_t st = validate_shape(shape);
+  if (st != MOGE_OK) return st;
+  const moge_shape_t& s = *shape;
+  if (mode != MOGE_ROUTE_GROUPED && mode != MOGE_ROUTE_GLOBAL) return fail(MOGE_ERR_ARG, "unknown route mode");
+  if (!idx || !counts || !offsets) return fail(MOGE_ERR_NULL, "idx, counts and offsets are required");
+  if ((x == nullptr) != (x_perm == nullptr)) return fail(MOGE_ERR_NULL, "x and x_perm must be given together");
+  if ((inv == nullptr) != (perm == nullptr)) return fail(MOGE_ERR_NULL, "inv and perm must be given together");
+  if (x && !inv) return fail(MOGE_ERR_NULL, "row copies need inv and perm");
+  if (e_lo < 0 || e_hi > s.N || e_lo >= e_hi) return fail(MOGE_ERR_ARG, "need 0 <= e_lo < e_hi <= N");
+  const int K = s.M * s.k_per_group;
+  if (K > 64) return fail(MOGE_ERR_SHAPE, "dispatch supports K = M*k_per_group <= 64");
+  const int64_t bound = rows_bound(s, mode, e_lo, e_hi);
+  if (inv && rows_cap < bound)
+    return fail(MOGE_ERR_CAPACITY, "rows_cap is below moge_rows_bound() for this expert range");
+  const size_t need = moge_workspace_size(shape, MOGE_STAGE_DISPATCH);
+  if (!ws || ws_bytes < need) return fail(MOGE_ERR_WORKSPACE, "dispatch workspace missing or too small");
+
+  const int64_t nb = dispatch_blocks(s.T);
+  int32_t* bcount = static_cast<int32_t*>(ws);
+  int32_t* bprefix = bcount + (int64_t)s.N * nb;
+  const int64_t row_bytes = (int64_t)s.d * (s.dtype == MOGE_BF16 ? 2 : 4);
+
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nb), dim3(256), 0, stream, (int64_t)s.T, K, s.N, nb, idx,
+                     bcount);
+  if ((st = check_launch("dispatch_hist_kernel")) != MOGE_OK) return st;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3((unsigned)s.N), dim3(256), 0, stream, nb, bcount, bprefix, counts);
+  if ((st = check_launch("dispatch_scan_kernel")) != MOGE_OK) return st;
+
+  const size_t lds = sizeof(int) * ((size_t)2 * kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + 4 * (size_t)s.N);
+  if (lds > 64 * 1024) {
+    static bool raised = false;
+    if (!raised) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(dispatch_permute_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL(dispatch_permute_kernel, dim3(inv ? (unsigned)nb : 1u), dim3(256), lds, stream, (int64_t)s.T, K, s.N, nb,
+                     idx, static_cast<const char*>(x), row_bytes, e_lo, e_hi, rows_cap, counts, bprefix, offsets,
+                     inv, perm, static_cast<char*>(x_perm));
+  st = check_launch("dispatch_permute_kernel");
+  return st == MOGE_OK ? ok() : st;
+}

@@ -1,0 +1,83 @@
+// Internal helpers shared by the libmoge translation units (host validation,
+// error reporting and small device utilities for gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "moge.h"
+
+namespace moge {
+
+// ---------------------------------------------------------------- host side
+moge_status_t fail(moge_status_t st, const std::string& msg);
+moge_status_t ok();
+moge_status_t check_launch(const char* what);
+moge_status_t validate_shape(const moge_shape_t* s);
+int64_t rows_bound(const moge_shape_t& s, int32_t mode, int32_t e_lo, int32_t e_hi);
+
+constexpr int kMaxExperts = 256;
+
+// Dispatch geometry (shared by moge_workspace_size and the dispatch kernels).
+constexpr int kDispatchTokens = 256;  // tokens per dispatch workgroup
+inline int64_t dispatch_blocks(int64_t T) { return (T + kDispatchTokens - 1) / kDispatchTokens; }
+
+// ---------------------------------------------------------------- device side
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// binary32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Number of lanes below the calling lane whose bit is set in `mask`.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Exclusive scan of a 256-wide block; returns this thread's prefix, *total = block sum.
+// (256 threads; all threads of the block must call it)
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch /* >= 4 ints */, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int wbase = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int s = scratch[w];
+    if (w < wave) wbase += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + incl - v;
+}
+
+}  // namespace moge

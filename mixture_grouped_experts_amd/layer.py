@@ -1,0 +1,113 @@
+"""One MoGE layer forward as a sequence of libmoge C-ABI calls on one stream.
+
+Order (Pangu Pro MoE, lsdiaocha.cn summary, section 1; Pangu Ultra MoE digests on
+reportify.cn for the shared expert):
+
+  1. moge_route GROUPED   scores (stored), softmax over all N, top-K' in every group
+  2. moge_dispatch        counts, offsets, stable permutation, rows of [e_lo, e_hi)
+  3. moge_grouped_ffn     SwiGLU experts on their row segments
+  4. moge_grouped_ffn     the always-on shared expert (one-expert shape), if any
+  5. moge_combine         gate-weighted sum (+ shared output) -> y (float32)
+  6. moge_imbalance       per-group load and imbalance score (0 by construction)
+  7. moge_route GLOBAL    the conventional top-K comparator from the stored scores,
+     moge_dispatch        its counts only, and moge_imbalance of that load.
+
+Buffers are allocated once here (torch supplies device memory); ``forward`` only issues
+library calls, so it allocates nothing and does not synchronise.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class MoGELayer:
+    def __init__(self, T: int, d: int, N: int, M: int, Kp: int, F: int, F_shared: int = 0, dtype: str = "bf16",
+                 e_lo: int = 0, e_hi: int | None = None, device="cuda", comparator: bool = True):
+        self.dtype_code = L.BF16 if dtype == "bf16" else L.F32
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.shape = L.Shape(T, d, N, M, Kp, F, self.dtype_code)
+        st = L.validate(self.shape)
+        if st != 0:
+            raise L.MogeError("moge_validate", st, L.last_error())
+        self.T, self.d, self.N, self.M, self.Kp, self.F = T, d, N, M, Kp, F
+        self.K = M * Kp
+        self.e_lo, self.e_hi = e_lo, (N if e_hi is None else e_hi)
+        self.F_shared = F_shared
+        self.comparator = comparator
+        self.routing_only = F == 0
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        K = self.K
+        self.logits = torch.empty(T, N, **f32)
+        self.idx = torch.empty(T, K, **i32)
+        self.gate = torch.empty(T, K, **f32)
+        self.counts = torch.empty(N, **i32)
+        self.offsets = torch.empty(N + 1, **i32)
+        self.ws = torch.empty(max(L.workspace_size(self.shape), 4), dtype=torch.uint8, device=dev)
+        self.group_load = torch.empty(M, **i32)
+        self.is_raw = torch.empty(1, **i32)
+        self.is_norm = torch.empty(1, dtype=torch.float64, device=dev)
+        if comparator:
+            self.gidx = torch.empty(T, K, **i32)
+            self.ggate = torch.empty(T, K, **f32)
+            self.gcounts = torch.empty(N, **i32)
+            self.goffsets = torch.empty(N + 1, **i32)
+            self.g_group_load = torch.empty(M, **i32)
+            self.g_is_raw = torch.empty(1, **i32)
+            self.g_is_norm = torch.empty(1, dtype=torch.float64, device=dev)
+        if not self.routing_only:
+            self.rows_cap = L.rows_bound(self.shape, L.ROUTE_GROUPED, self.e_lo, self.e_hi)
+            R = self.rows_cap
+            self.inv = torch.empty(T, K, **i32)
+            self.perm = torch.empty(R, **i32)
+            self.x_perm = torch.empty(R, d, dtype=self.tdtype, device=dev)
+            self.h = torch.empty(R, F, dtype=self.tdtype, device=dev)
+            self.o = torch.empty(R, d, dtype=self.tdtype, device=dev)
+            self.y = torch.empty(T, d, **f32)
+        if F_shared:
+            self.sshape = L.Shape(T, d, 1, 1, 1, F_shared, self.dtype_code)
+            self.soffsets = torch.tensor([0, T], **i32)
+            self.sh = torch.empty(T, F_shared, dtype=self.tdtype, device=dev)
+            self.so = torch.empty(T, d, dtype=self.tdtype, device=dev)
+
+    def forward(self, x, w_router, bias, w_gate=None, w_up=None, w_down=None, shared=None, stream=None, mark=None):
+        """Enqueues the layer on `stream` (default: current).  Returns y (None for routing only).
+
+        `mark(name)`, if given, is called right after each library call is enqueued (a timing hook:
+        the caller may record a stream event there)."""
+        s = self.shape
+        mk = mark if mark is not None else (lambda name: None)
+        L.route(s, L.ROUTE_GROUPED, x, w_router, bias, self.logits, self.idx, self.gate, stream)
+        mk("route")
+        if self.routing_only:
+            L.dispatch(s, L.ROUTE_GROUPED, self.idx, None, 0, self.N, 0, self.counts, self.offsets, None, None, None,
+                       self.ws, stream)
+            mk("dispatch")
+        else:
+            L.dispatch(s, L.ROUTE_GROUPED, self.idx, x, self.e_lo, self.e_hi, self.rows_cap, self.counts,
+                       self.offsets, self.inv, self.perm, self.x_perm, self.ws, stream)
+            mk("dispatch")
+            L.expert_gate_up(s, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate, w_up, self.h,
+                             stream)
+            mk("gate_up")
+            L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o, stream)
+            mk("down")
+            if self.F_shared:
+                L.grouped_ffn(self.sshape, x, self.soffsets, 0, 1, self.T, shared[0], shared[1], shared[2], self.sh,
+                              self.so, stream)
+                mk("shared")
+            L.combine(s, self.o, self.inv, self.gate, self.rows_cap, self.so if self.F_shared else None, self.y,
+                      stream)
+            mk("combine")
+        L.imbalance(s, self.counts, self.group_load, self.is_raw, self.is_norm, stream)
+        mk("imbalance")
+        if self.comparator:
+            L.route(s, L.ROUTE_GLOBAL, None, None, None, self.logits, self.gidx, self.ggate, stream)
+            L.dispatch(s, L.ROUTE_GLOBAL, self.gidx, None, 0, self.N, 0, self.gcounts, self.goffsets, None, None,
+                       None, self.ws, stream)
+            L.imbalance(s, self.gcounts, self.g_group_load, self.g_is_raw, self.g_is_norm, stream)
+            mk("global_comparator")
+        return None if self.routing_only else self.y

@@ -46,11 +46,18 @@ def _load():
         lib.oracle_dispatch.argtypes = [_I, _I, _I, _P, _I, _I, _P, _P, _P, _P]
         lib.oracle_ffn_row.argtypes = [_I, _I, ctypes.c_int, _P, _P, _P, _P, _P]
         lib.oracle_imbalance.argtypes = [_I, _I, _P, _P, _P]
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         for f in (lib.oracle_logits, lib.oracle_route, lib.oracle_dispatch, lib.oracle_ffn_row,
                   lib.oracle_imbalance):
             f.restype = None
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().oracle_threads())
 
 
 def _dtype_code(a: np.ndarray) -> int:

@@ -20,6 +20,7 @@
  * invariants, library routines (NumPy/SciPy) or brute-force enumeration.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -195,3 +196,6 @@ void oracle_imbalance(int64_t N, int64_t M, const int32_t* counts, int32_t* grou
   }
   *is_raw = hi - lo;
 }
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int oracle_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,107 @@
+"""CPU-only checks of the C ABI: the library loads without a GPU, exports every function that
+include/moge.h declares, and its host-side validation returns the documented status codes.
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_grouped_experts_amd as moge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "moge.h")) as f:
+        txt = f.read()
+    return sorted(set(re.findall(r"^\s*(?:moge_status_t|int64_t|size_t|const char\*)\s+(moge_\w+)\s*\(", txt, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(moge.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moge.EXPORTS)
+
+
+def test_version():
+    assert "gfx950" in moge.version()
+
+
+def S(T=64, d=128, N=8, M=4, Kp=1, F=64, dt=moge.BF16):
+    return moge.Shape(T, d, N, M, Kp, F, dt)
+
+
+@pytest.mark.parametrize("shape,code", [
+    (S(), 0), (S(dt=moge.F32), 0), (S(F=0), 0), (S(M=1, Kp=8), 0), (S(N=256, M=8, Kp=32), 0),
+    (S(T=0), 2), (S(d=100), 2), (S(d=0), 2), (S(M=3), 2), (S(M=16), 2), (S(Kp=0), 2), (S(Kp=3), 2),
+    (S(F=12), 2), (S(F=-8), 2), (S(N=512, M=8), 2), (S(dt=7), 5), (S(T=2 ** 28, M=8, N=64, Kp=1), 2),
+])
+def test_validate(shape, code):
+    assert moge.validate(shape) == code
+    if code:
+        assert moge.last_error()
+
+
+def test_rows_bound_and_workspace():
+    s = S(T=100, N=64, M=8, Kp=2)
+    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 64) == 100 * 16
+    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 8) == 100 * 2        # one group
+    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 7, 9) == 100 * 2        # one expert in each of two groups
+    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 1) == 100
+    assert moge.rows_bound(s, moge.ROUTE_GLOBAL, 0, 8) == 100 * 8
+    assert moge.rows_bound(s, moge.ROUTE_GLOBAL, 0, 64) == 100 * 16
+    assert moge.rows_bound(s, 5, 0, 8) == -1 and moge.rows_bound(s, 0, 8, 8) == -1
+    assert moge.workspace_size(S(T=65536, N=64)) == 2 * 64 * 256 * 4
+    assert moge.workspace_size(S(T=1, N=8)) == 2 * 8 * 1 * 4
+    assert moge.workspace_size(S(T=0)) == 2 ** 64 - 1
+
+
+def _call(fn, *args):
+    return getattr(ctypes.CDLL(moge.LIB_PATH), fn)(*args)
+
+
+def test_null_and_argument_errors_before_any_launch():
+    lib = ctypes.CDLL(moge.LIB_PATH)
+    s = S()
+    sp = ctypes.byref(s)
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: every case fails host validation first
+    lib.moge_route.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [P] * 7
+    assert lib.moge_route(None, 0, fake, fake, None, fake, fake, fake, None) == 3        # NULL shape
+    assert lib.moge_route(sp, 2, fake, fake, None, fake, fake, fake, None) == 1          # bad mode
+    assert lib.moge_route(sp, 0, fake, fake, None, fake, None, fake, None) == 3          # idx NULL
+    assert lib.moge_route(sp, 0, None, None, None, None, fake, fake, None) == 3          # no x, no logits
+    assert lib.moge_route(sp, 0, None, None, fake, fake, fake, fake, None) == 1          # bias with logits-in
+    assert lib.moge_route(sp, 0, fake, None, None, None, fake, fake, None) == 3          # x without w_router
+    lib.moge_dispatch.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                  P, P, P, P, P, P, ctypes.c_size_t, P]
+    ws = moge.workspace_size(s)
+    cap = moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 8)   # 64 tokens x 4 groups x 1
+    assert cap == 256
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap - 1, fake, fake, fake, fake, fake, fake, ws, None) == 7
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, fake, ws - 1, None) == 4
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, None, ws, None) == 4
+    assert lib.moge_dispatch(sp, 0, fake, fake, 3, 3, cap, fake, fake, fake, fake, fake, fake, ws, None) == 1
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 9, cap, fake, fake, fake, fake, fake, fake, ws, None) == 1
+    assert lib.moge_dispatch(sp, 3, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, fake, ws, None) == 1
+    assert lib.moge_dispatch(sp, 0, fake, None, 0, 8, cap, fake, fake, fake, fake, fake, fake, ws, None) == 3
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, None, fake, fake, fake, ws, None) == 3
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, None, None, fake, fake, ws, None) == 3
+    big = S(N=128, M=2, Kp=64)                                                            # K = 128 > 64
+    assert lib.moge_dispatch(ctypes.byref(big), 0, fake, fake, 0, 128, 64 * 128, fake, fake, fake, fake, fake,
+                             fake, 1 << 20, None) == 2
+    lib.moge_grouped_ffn.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64] + [P] * 6
+    assert lib.moge_grouped_ffn(ctypes.byref(S(F=0)), fake, fake, 0, 8, 64, fake, fake, fake, fake, fake, None) == 2
+    assert lib.moge_grouped_ffn(sp, fake, fake, 0, 8, 64, fake, None, fake, fake, fake, None) == 3
+    assert lib.moge_grouped_ffn(sp, fake, fake, -1, 8, 64, fake, fake, fake, fake, fake, None) == 1
+    assert lib.moge_grouped_ffn(sp, fake, fake, 0, 8, 0, fake, fake, fake, fake, fake, None) == 7
+    lib.moge_combine.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P]
+    assert lib.moge_combine(sp, fake, fake, None, 64, None, fake, None) == 3
+    assert lib.moge_combine(sp, fake, fake, fake, 0, None, fake, None) == 7
+    lib.moge_imbalance.argtypes = [P] * 6
+    assert lib.moge_imbalance(sp, fake, fake, None, fake, None) == 3
+    assert lib.moge_imbalance(ctypes.byref(S(M=3)), fake, fake, fake, fake, None) == 2
