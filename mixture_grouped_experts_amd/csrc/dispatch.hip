@@ -237,12 +237,8 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
 
   const size_t lds = sizeof(int) * ((size_t)2 * kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + 4 * (size_t)s.N);
   if (lds > 64 * 1024) {
-    static bool raised = false;
-    if (!raised) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(dispatch_permute_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      raised = true;
-    }
+    st = raise_dynamic_lds(reinterpret_cast<const void*>(dispatch_permute_kernel), lds, "dispatch_permute_kernel");
+    if (st != MOGE_OK) return st;
   }
   hipLaunchKernelGGL(dispatch_permute_kernel, dim3(inv ? (unsigned)nb : 1u), dim3(256), lds, stream, (int64_t)s.T, K, s.N, nb,
                      idx, static_cast<const char*>(x), row_bytes, e_lo, e_hi, rows_cap, counts, bprefix, offsets,

@@ -296,12 +296,9 @@ template <bool SWIGLU>
 static moge_status_t launch_ggemm(const uint16_t* A, const int32_t* offsets, int e_lo, int E, int64_t rows_cap,
                                   const uint16_t* B0, const uint16_t* B1, int NOUT, int KD, uint16_t* C,
                                   hipStream_t stream) {
-  static bool raised = false;
-  if (!raised) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(ggemm_bf16_kernel<SWIGLU>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-    raised = true;
-  }
+  moge_status_t st = raise_dynamic_lds(reinterpret_cast<const void*>(ggemm_bf16_kernel<SWIGLU>), kGemmLds,
+                                       "ggemm_bf16_kernel");
+  if (st != MOGE_OK) return st;
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
   const int64_t NT = (NOUT + BNO - 1) / BNO;
   const int64_t upper = ((rows_cap + kBM - 1) / kBM + E) * NT;  // >= live tiles

@@ -1,8 +1,10 @@
 // Host-side part of the libmoge C ABI: shape validation, row bounds,
-// workspace sizes, version and per-thread error messages.  Nothing here
-// touches the device, so it runs (and is tested) without a GPU.
+// workspace sizes, version and per-thread error messages (all usable without
+// a GPU), plus the one-time dynamic-LDS attribute setup of large kernels.
 #include <stdio.h>
 
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "moge_internal.hpp"
@@ -41,6 +43,19 @@ moge_status_t validate_shape(const moge_shape_t* s) {
     return fail(MOGE_ERR_SHAPE, "F must be 0 (routing only) or a positive multiple of 8");
   const int64_t K = (int64_t)s->M * s->k_per_group;
   if ((int64_t)s->T * K >= (int64_t(1) << 31)) return fail(MOGE_ERR_SHAPE, "T*K must be < 2^31");
+  return MOGE_OK;
+}
+
+moge_status_t raise_dynamic_lds(const void* kernel, size_t bytes, const char* what) {
+  static std::mutex mu;
+  static std::map<const void*, size_t> done;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = done[kernel];
+  if (bytes <= have) return MOGE_OK;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess)
+    return fail(MOGE_ERR_HIP, std::string(what) + ": cannot raise dynamic LDS: " + hipGetErrorString(e));
+  have = bytes;
   return MOGE_OK;
 }
 

@@ -17,6 +17,9 @@ moge_status_t ok();
 moge_status_t check_launch(const char* what);
 moge_status_t validate_shape(const moge_shape_t* s);
 int64_t rows_bound(const moge_shape_t& s, int32_t mode, int32_t e_lo, int32_t e_hi);
+// Lets `kernel` use `bytes` of dynamic LDS (above the 64 KiB default).  Thread-safe;
+// remembers the largest size set per kernel.
+moge_status_t raise_dynamic_lds(const void* kernel, size_t bytes, const char* what);
 
 constexpr int kMaxExperts = 256;
 

@@ -98,4 +98,12 @@ def group0() -> Workload:
                     0.02, 0.02, 0.0, 2.0, 0, 8)
 
 
+def variant(base: Workload, **kw) -> Workload:
+    """A workload derived from `base`; the expert range defaults to all N experts."""
+    if "e_hi" not in kw:
+        kw["e_hi"] = kw.get("N", base.N)
+        kw.setdefault("e_lo", 0)
+    return dataclasses.replace(base, **kw)
+
+
 ALL = {w.name: w for w in (tiny(), routing(), decode(), ultra(), group0())}

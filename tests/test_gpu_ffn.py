@@ -39,11 +39,11 @@ def _dispatch_then_ffn(w, e_lo=None, e_hi=None):
     return w, dv, hi, idx, offsets.cpu().numpy(), perm.cpu().numpy(), xp, hbuf, out
 
 
-MID = dataclasses.replace(W.decode(), name="mid_T300_d256_N16_M4_K2_F200", T=300, d=256, N=16, M=4, Kp=2, F=200,
+MID = W.variant(W.decode(), name="mid_T300_d256_N16_M4_K2_F200", T=300, d=256, N=16, M=4, Kp=2, F=200,
                           std_bias=1.0)
 
 
-@pytest.mark.parametrize("w", [MID, dataclasses.replace(MID, name="mid_F1408_d520", d=520, F=1408, T=97),
+@pytest.mark.parametrize("w", [MID, W.variant(MID, name="mid_F1408_d520", d=520, F=1408, T=97),
                                W.decode()], ids=lambda w: w.name)
 def test_grouped_ffn_vs_torch_matmul(gpu, w):
     print(f"[ffn vs torch] {w.name}", flush=True)
@@ -88,7 +88,7 @@ def test_grouped_ffn_expert_range_and_shared_form(gpu):
     ok, err, bound = H.tol_ok(out[torch.from_numpy(rows).long().cuda()].float().cpu().numpy(), ref)
     assert ok, (err, bound)
     # the shared-expert form: one expert, offsets {0, T}, x_perm = x
-    sw = dataclasses.replace(MID, F_shared=136)
+    sw = W.variant(MID, F_shared=136, std_shared_down=0.02)
     dsh = H.device_inputs(sw).shared
     hsh = H.HostInputs(sw).shared()
     s1 = moge.Shape(sw.T, sw.d, 1, 1, 1, 136, moge.BF16)

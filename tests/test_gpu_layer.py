@@ -64,12 +64,12 @@ def test_layer_tiny_fp32(gpu):
 
 
 def test_layer_mid_ragged(gpu):
-    w = dataclasses.replace(W.decode(), name="mid", T=1000, d=520, N=16, M=4, Kp=2, F=200, std_bias=1.0)
+    w = W.variant(W.decode(), name="mid", T=1000, d=520, N=16, M=4, Kp=2, F=200, std_bias=1.0)
     check_layer(w)
 
 
 def test_layer_mid_shared_and_range(gpu):
-    w = dataclasses.replace(W.decode(), name="mid_shared", T=257, d=256, N=32, M=4, Kp=1, F=136, F_shared=264,
+    w = W.variant(W.decode(), name="mid_shared", T=257, d=256, N=32, M=4, Kp=1, F=136, F_shared=264,
                             e_lo=8, e_hi=16, std_shared_down=0.02)
     check_layer(w)
 
@@ -97,7 +97,7 @@ def test_layer_group0_sampled(gpu):
 
 
 def test_layer_deterministic(gpu):
-    w = dataclasses.replace(W.decode(), name="det", T=600, std_bias=2.0)
+    w = W.variant(W.decode(), name="det", T=600, std_bias=2.0)
     dv = H.device_inputs(w)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, 0, "bf16")
     outs = []

@@ -96,7 +96,7 @@ def test_route_ties_and_edge_shapes(gpu):
     cases = [(1, 8, 4, 1), (33, 64, 8, 2), (100, 16, 1, 5), (70, 12, 3, 4), (129, 256, 8, 1), (64, 256, 4, 8),
              (65, 128, 2, 3)]
     for T, N, M, Kp in cases:
-        w = dataclasses.replace(W.routing(), T=T, N=N, M=M, Kp=Kp)
+        w = W.variant(W.routing(), T=T, N=N, M=M, Kp=Kp)
         lg = rng.integers(-2, 3, size=(T, N)).astype(np.float32)        # heavy ties
         lg[::3] = (rng.standard_normal((len(lg[::3]), N)) * 2).astype(np.float32)
         lg[1::5] = 0.0
@@ -111,7 +111,7 @@ def test_route_ties_and_edge_shapes(gpu):
 @pytest.mark.parametrize("N,M,Kp,d", [(64, 8, 1, 4096), (128, 4, 2, 1024), (256, 8, 1, 7680), (64, 8, 8, 520)])
 def test_route_from_x_shapes(gpu, N, M, Kp, d):
     # other expert counts (one, two and four 64-expert column groups) and a ragged hidden size
-    w = dataclasses.replace(W.decode(), T=300, d=d, N=N, M=M, Kp=Kp, std_bias=1.0)
+    w = W.variant(W.decode(), T=300, d=d, N=N, M=M, Kp=Kp, std_bias=1.0)
     h = H.HostInputs(w)
     lg_ref = H.oracle_logits_all(h)
     dv = H.device_inputs(w)
