@@ -41,7 +41,24 @@ def parse():
     p.add_argument("--workload", default="ultra", choices=["ultra", "group0", "decode", "routing", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch, 3 launches."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": n, "bytes_written_per_launch": n, "launches": 3}))
 
 
 def algorithmic_work(w, counts):
@@ -111,6 +128,10 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
               f"(the multi-GPU expert-group sharding is a design, not code)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch

@@ -2,7 +2,7 @@
 // the gather of token rows into expert order (dropless: every (token, slot) pair
 // gets a row; Pangu Ultra MoE digests on reportify.cn, dropless training).
 //
-// Three launches, no atomics on anything that decides an order:
+// Four launches, no atomics on anything that decides an order:
 //   1. dispatch_hist_kernel   one workgroup per block of 256 tokens counts its
 //                             assignments per expert (LDS integer histogram).
 //   2. dispatch_scan_kernel   one workgroup per expert scans that expert's block
@@ -12,9 +12,9 @@
 //                             loop over the distinct experts of its tokens gives
 //                             every (token, slot) its row = block/wave base + number
 //                             of lower lanes that chose the same expert, so rows of
-//                             an expert stay in ascending token order; finally each
-//                             token row is read from HBM once and written to all of
-//                             its slots' rows with 16-byte coalesced stores.
+//                             an expert stay in ascending token order -> inv, perm.
+//   4. dispatch_copy_kernel   one wave per token reads its row from HBM once and
+//                             writes it to all of its slots' rows (16-byte stores).
 #include "moge_internal.hpp"
 
 namespace moge {
@@ -60,11 +60,10 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int64_t nb, const in
 
 // Dynamic LDS: keys[kTB][KS] | rows[kTB][KS] | offs[N+1] | base[N] | hist[4][N]
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
-    int64_t T, int K, int N, int64_t nb, const int32_t* __restrict__ idx, const char* __restrict__ x,
-    int64_t row_bytes, int e_lo, int e_hi, int64_t rows_cap, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ bprefix, int32_t* __restrict__ offsets_out, int32_t* __restrict__ inv,
-    int32_t* __restrict__ perm, char* __restrict__ x_perm) {
-  // inv == nullptr: offsets only (launched with one workgroup); x_perm == nullptr: no row copies
+    int64_t T, int K, int N, int64_t nb, const int32_t* __restrict__ idx, int e_lo, int e_hi, int64_t rows_cap,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ bprefix, int32_t* __restrict__ offsets_out,
+    int32_t* __restrict__ inv, int32_t* __restrict__ perm) {
+  // inv == nullptr: offsets only (launched with one workgroup)
   extern __shared__ int lds[];
   const int KS = K + 1;  // odd row stride: lanes of a wave hit distinct banks
   int* keys = lds;
@@ -168,16 +167,20 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     inv[t * K + s] = r;
     if (r >= 0) perm[r] = (int32_t)t;
   }
-  __syncthreads();
-  if (!x_perm) return;
+}
 
-  const int64_t nch = row_bytes >> 4;  // 16-byte chunks per row
-  for (int j = 0; j < 64; ++j) {
-    const int tl = wave * 64 + j;
-    const int64_t t = t0 + tl;
-    if (t >= T) break;
-    const int* rr = rows + tl * KS;
+// Row gather: one wave per token reads x[t] once and writes it to every row
+// that inv gives the token (16-byte chunks, 8 in flight per lane).
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(int64_t T, int K, const char* __restrict__ x,
+                                                            int64_t row_bytes, int64_t rows_cap,
+                                                            const int32_t* __restrict__ inv,
+                                                            char* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t nch = row_bytes >> 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + t * row_bytes);
+    const int32_t* rr = inv + t * K;
     for (int64_t c0 = 0; c0 < nch; c0 += 64 * 8) {
       u32x4_t v[8];
 #pragma unroll
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
       }
       for (int s = 0; s < K; ++s) {
         const int r = rr[s];
-        if (r < 0) continue;
+        if (r < 0 || (int64_t)r >= rows_cap) continue;
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(x_perm + (int64_t)r * row_bytes);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -241,8 +244,14 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
     if (st != MOGE_OK) return st;
   }
   hipLaunchKernelGGL(dispatch_permute_kernel, dim3(inv ? (unsigned)nb : 1u), dim3(256), lds, stream, (int64_t)s.T, K, s.N, nb,
-                     idx, static_cast<const char*>(x), row_bytes, e_lo, e_hi, rows_cap, counts, bprefix, offsets,
-                     inv, perm, static_cast<char*>(x_perm));
+                     idx, e_lo, e_hi, rows_cap, counts, bprefix, offsets, inv, perm);
   st = check_launch("dispatch_permute_kernel");
+  if (st == MOGE_OK && x) {
+    int64_t grid = ((int64_t)s.T + 3) / 4;
+    if (grid > 16384) grid = 16384;
+    hipLaunchKernelGGL(dispatch_copy_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (int64_t)s.T, K,
+                       static_cast<const char*>(x), row_bytes, rows_cap, inv, static_cast<char*>(x_perm));
+    st = check_launch("dispatch_copy_kernel");
+  }
   return st == MOGE_OK ? ok() : st;
 }

@@ -9,19 +9,25 @@
 // traffic at high concurrency and double-buffers its loads.  That kernel was
 // written for Ascend; on gfx950 the same ideas become:
 //   * bf16 v_mfma_f32_32x32x16_bf16 with float32 accumulators; a 256-thread
-//     workgroup owns a 128-row x 256-weight-row tile (GEMM 1: 128 gate + 128 up
+//     workgroup owns a 256-row x 256-weight-row tile (GEMM 1: 128 gate + 128 up
 //     rows of the same 128 h columns, so the SwiGLU is fused into the epilogue;
-//     GEMM 2: 256 output columns) and each wave a 64 x 128 quarter of it;
-//   * A and B panels staged in LDS in BK = 64 steps, double buffered: the next
-//     step's global loads are in flight while the current step's MFMAs run; rows
-//     padded by 16 B so the 16-byte operand reads are bank-conflict free;
+//     GEMM 2: 256 output columns) and each wave a 128 x 128 quarter of it (16
+//     accumulator blocks, 8 fragment reads per 16 MFMAs);
+//   * A and B panels staged in LDS in BK = 32 steps through a 3-stage LDS ring
+//     fed by 2 register stages, so every global load has about two steps of
+//     MFMA work to arrive; rows padded by 16 B so the 16-byte fragment reads are
+//     bank-conflict free; one barrier per step;
+//   * a tile with few live rows (the last tile of an expert) skips the MFMAs of
+//     its empty 32-row blocks; the row blocks are interleaved over the waves;
 //   * a persistent grid walks a device-built tile list (no host sync on the
 //     expert counts): every workgroup derives the per-expert tile counts from
 //     `offsets` in LDS.  Tiles of one expert are ordered in groups of 8 m-tiles,
 //     n-tiles outer, so tiles that share a weight panel or an activation panel
 //     run at the same time; consecutive tiles go to one XCD (workgroup b runs on
 //     XCD b % 8), so that sharing happens in that XCD's L2;
-//   * epilogue through LDS so each lane stores 16 contiguous bytes.
+//   * the weight fragment is the MFMA's first operand, so each lane ends with 4
+//     consecutive output columns of one token row: the epilogue (SwiGLU for
+//     GEMM 1) packs them into 8-byte stores straight to HBM.
 // float32 shapes use a plain vector-ALU kernel pair (small shapes only).
 #include <math.h>
 
@@ -29,21 +35,207 @@
 
 namespace moge {
 
-constexpr int kBM = 128;      // rows per tile
-constexpr int kBW = 256;      // weight rows per tile
-constexpr int kBK = 64;       // reduction step
-constexpr int kLD = kBK + 8;  // padded LDS row (bf16 elements)
-constexpr int kGroupM = 8;    // m-tiles per scheduling group
-constexpr int kStageElems = (kBM + kBW) * kLD;
-constexpr size_t kGemmLds = 2 * (size_t)kStageElems * 2;
+constexpr int kBM = 256;                    // token rows per tile
+constexpr int kBW = 256;                    // weight rows per tile
+constexpr int kBK = 32;                     // reduction step (elements)
+constexpr int kRowB = kBK * 2;              // 64-byte LDS rows (unpadded; chunks are XOR-swizzled)
+constexpr int kStageB = (kBM + kBW) * kRowB;  // 32 KiB per stage
+constexpr int kStages = 4;
+constexpr size_t kGemmLds = (size_t)kStages * kStageB;  // 128 KiB
+constexpr int kGroupM = 4;                  // m-tiles per scheduling group
+
+// 16-byte chunk c of LDS row r lives in slot c ^ swz(r): two rows share a 128-byte
+// bank line, so this spreads the 32 rows of a fragment read over all banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory
+// operations of this wave are outstanding; LDS and export counters untouched.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// the same, and every LDS read of this wave has returned its data
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+// One tile: reduction loop and epilogue.  Wave (wm, wn) owns the token row blocks
+// wm, wm+2, wm+4, wm+6 (32 rows each, interleaved so a partly filled tile keeps
+// the four waves balanced) and 4 weight blocks of 32 rows; NL of its row blocks
+// hold live rows (the others skip their MFMAs).  The MFMA takes the weight
+// fragment as its first operand, so each lane ends with 4 consecutive output
+// columns of one token row, which the epilogue packs into 8-byte stores.
+//
+// Pipeline: global -> LDS directly (global_load_lds_dwordx4, no staging registers)
+// into a 4-stage ring.  Each wave moves 16 token rows and 16 weight rows x 64 B
+// per instruction, 8 instructions per step; step s is issued at step s-3, and the
+// step loop waits (vmcnt) for its own loads of step s+1 plus one barrier per step,
+// so every load has two steps of MFMA work to land.
+template <bool SWIGLU, int NL>
+__device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint16_t* __restrict__ abase,
+                                             const uint16_t* __restrict__ wbase0, const uint16_t* __restrict__ wbase1,
+                                             int KD, int wm, int wn, int mrows, int n0, int NOUT,
+                                             uint16_t* __restrict__ cbase) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nkf = KD / kBK;  // full steps; a ragged tail is one extra step below
+  // DMA sources: instruction j < 4 moves token rows wave*64 + 16j .. +16, j >= 4 weight rows.
+  const uint16_t* dsrc[8];
+  int ddst[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wave * 64 + (j & 3) * 16 + (lane >> 2);  // row inside its operand (0..255)
+    const int c = (lane & 3) ^ swz(r);                       // global chunk fetched by this lane
+    if (j < 4) {
+      const int rr = r < mrows ? r : mrows - 1;
+      dsrc[j] = abase + (int64_t)rr * KD + c * 8;
+    } else {
+      int wr = SWIGLU ? n0 + (r & 127) : n0 + r;
+      if (wr > NOUT - 1) wr = NOUT - 1;
+      dsrc[j] = (SWIGLU && r >= 128 ? wbase1 : wbase0) + (int64_t)wr * KD + c * 8;
+    }
+    ddst[j] = ((j < 4 ? 0 : kBM) + wave * 64 + (j & 3) * 16) * kRowB;  // wave-uniform LDS byte offset
+  }
+  // Step ks into stage ks % 4 (steps past the last full step reload step 0).  The
+  // DMA is issued from inline assembly so the compiler does not turn its LDS side
+  // effect into a full vmcnt wait before every LDS read; the waits are explicit
+  // (vmcnt_imm) and each is followed by a barrier before the stage is read.  The
+  // instruction has no register result, only an address operand read at issue.
+  auto issue = [&](int ks) {
+    const int k = ks < nkf ? ks * kBK : 0;
+    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds + (ks % kStages) * kStageB);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(st + (uint32_t)ddst[j]);
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(dsrc[j] + k), "s"(m0v)
+                   : "memory", "m0");
+    }
+  };
+  const int kc = (lane >> 5);  // logical chunk of this lane inside a 16-element sub-step
+  int arow[4], brow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) arow[t] = (wm + 2 * t) * 32 + (lane & 31);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+    brow[cb] = kBM + (SWIGLU ? ((cb < 2 ? 0 : 128) + wn * 64 + (cb & 1) * 32) : (wn * 128 + cb * 32)) + (lane & 31);
+  auto frag = [&](int ks, int kk, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+    const char* st = lds + (ks % kStages) * kStageB;
+    const int c = kk * 2 + kc;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      b[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + brow[cb] * kRowB +
+                                                                              ((c ^ swz(brow[cb])) << 4)));
+#pragma unroll
+    for (int t = 0; t < NL; ++t)
+      a[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + arow[t] * kRowB +
+                                                                             ((c ^ swz(arow[t])) << 4)));
+  };
+  f32x16_t acc[NL > 0 ? NL : 1][4];
+#pragma unroll
+  for (int t = 0; t < (NL > 0 ? NL : 1); ++t)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][cb][r] = 0.f;
+  auto mfma = [&](const bf16x8_t (&a)[4], const bf16x8_t (&b)[4]) {
+#pragma unroll
+    for (int t = 0; t < NL; ++t)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        acc[t][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[cb], a[t], acc[t][cb], 0, 0, 0);
+  };
+
+  bf16x8_t a0[4], b0[4], a1[4], b1[4];
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // nothing of the previous tile in flight
+  issue(0);
+  issue(1);
+  issue(2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));  // steps 0 and 1 landed (this wave)
+  __syncthreads();
+  if (NL) frag(0, 0, a0, b0);
+  for (int ks = 0; ks < nkf; ++ks) {
+    issue(ks + 3);
+    if (NL) {
+      frag(ks, 1, a1, b1);
+      mfma(a0, b0);
+      frag(ks + 1, 0, a0, b0);
+      mfma(a1, b1);
+      // interleave: each fragment read issues in the shadow of an MFMA
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4 + NL; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NL - (4 + NL), 0);
+      }
+    }
+    // step ks+2 landed (this wave) and this step's LDS reads are done, so the DMA
+    // issued after the barrier may overwrite stage ks % 4
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(8));
+    __syncthreads();
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing reloads before LDS is reused
+  __syncthreads();
+  if (KD % kBK) {
+    // ragged tail: one unpipelined step, chunks at or past KD are zero
+    const int k = nkf * kBK;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = wave * 64 + (j & 3) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz(r);
+      const u32x4_t v = (k + c * 8 < KD) ? *reinterpret_cast<const u32x4_t*>(dsrc[j] + k) : zero;
+      *reinterpret_cast<u32x4_t*>(lds + ddst[j] + (lane << 4)) = v;
+    }
+    __syncthreads();
+    if (NL) {
+      frag(0, 0, a0, b0);
+      frag(0, 1, a1, b1);
+      mfma(a0, b0);
+      mfma(a1, b1);
+    }
+  }
+
+  // epilogue (rows of dead blocks are never stored)
+#pragma unroll
+  for (int t = 0; t < NL; ++t) {
+    const int row = (wm + 2 * t) * 32 + (lane & 31);
+    if (row < mrows) {
+      uint16_t* crow = cbase + (int64_t)row * NOUT;
+#pragma unroll
+      for (int cb = 0; cb < (SWIGLU ? 2 : 4); ++cb) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = n0 + (SWIGLU ? wn * 64 + cb * 32 : wn * 128 + cb * 32) + g4 * 8 + (lane >> 5) * 4;
+          if (col < NOUT) {
+            uint16_t hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float v;
+              if (SWIGLU) {
+                const float gv = acc[t][cb][g4 * 4 + i], uv = acc[t][cb + 2][g4 * 4 + i];
+                v = gv / (1.f + expf(-gv)) * uv;
+              } else {
+                v = acc[t][cb][g4 * 4 + i];
+              }
+              hv[i] = f32_to_bf16(v);
+            }
+            uint2 pk;
+            pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+            pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+            *reinterpret_cast<uint2*>(crow + col) = pk;
+          }
+        }
+      }
+    }
+  }
+}
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void ggemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                          int e_lo, int E, int64_t rows_cap, const uint16_t* __restrict__ B0,
                                                          const uint16_t* __restrict__ B1, int NOUT, int KD,
                                                          uint16_t* __restrict__ C) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  __shared__ int tp[kMaxExperts];  // inclusive prefix of tiles per expert
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int tp[kMaxExperts];    // inclusive prefix of tiles per expert
   __shared__ int erow[kMaxExperts];  // rows per expert, clipped to [0, rows_cap)
   __shared__ int scratch[4];
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;  // output columns per tile
@@ -74,7 +266,6 @@ __global__ __launch_bounds__(256) void ggemm_bf16_kernel(const uint16_t* __restr
   const int P = gridDim.x;  // multiple of 8
   const int per_xcd = P >> 3;
   const int slot = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-
   for (int tile = slot; tile < total; tile += P) {
     // expert of this tile: first i with tp[i] > tile
     int lo = 0, hi = E - 1;
@@ -97,139 +288,22 @@ __global__ __launch_bounds__(256) void ggemm_bf16_kernel(const uint16_t* __restr
     const int mrows = (erows - mt * kBM) < kBM ? (erows - mt * kBM) : kBM;
     const int n0 = nt * BNO;
 
-    // this thread's global sources: A rows tid/8 + 32i (i<4), B rows tid/8 + 32i (i<8)
-    const int cc = (tid & 7) * 8;
-    const uint16_t* asrc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int r = (tid >> 3) + 32 * i;
-      if (r > mrows - 1) r = mrows - 1;
-      asrc[i] = A + (int64_t)(m0 + r) * KD + cc;
-    }
-    const uint16_t* bsrc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      if (SWIGLU) {
-        int f = n0 + (r & 127);
-        if (f > NOUT - 1) f = NOUT - 1;
-        const uint16_t* W = r < 128 ? B0 : B1;
-        bsrc[i] = W + ((int64_t)ei * wrows + f) * KD + cc;
-      } else {
-        int j = n0 + r;
-        if (j > NOUT - 1) j = NOUT - 1;
-        bsrc[i] = B0 + ((int64_t)ei * wrows + j) * KD + cc;
-      }
-    }
-    auto gload = [&](int ks, u32x4_t* ar, u32x4_t* br) {
-      const int k = ks * kBK;
-      const bool in = k + cc < KD;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (in) v = *reinterpret_cast<const u32x4_t*>(asrc[i] + k);
-        ar[i] = v;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (in) v = *reinterpret_cast<const u32x4_t*>(bsrc[i] + k);
-        br[i] = v;
-      }
-    };
-    auto lstore = [&](int buf, const u32x4_t* ar, const u32x4_t* br) {
-      uint16_t* st = lds + buf * kStageElems;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4_t*>(st + ((tid >> 3) + 32 * i) * kLD + cc) = ar[i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4_t*>(st + (kBM + (tid >> 3) + 32 * i) * kLD + cc) = br[i];
-    };
+    const uint16_t* abase = A + (int64_t)m0 * KD;
+    const uint16_t* wb0 = B0 + (int64_t)ei * wrows * KD;
+    const uint16_t* wb1 = SWIGLU ? B1 + (int64_t)ei * wrows * KD : wb0;
 
-    f32x16_t acc[2][4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
-
-    // B rows of this wave's four 32-column blocks
-    int brow[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      if (SWIGLU)
-        brow[cb] = (cb < 2 ? wn * 64 + cb * 32 : 128 + wn * 64 + (cb - 2) * 32) + (lane & 31);
-      else
-        brow[cb] = wn * 128 + cb * 32 + (lane & 31);
+    // live row blocks of this wave (wave-uniform): block wm + 2t is live if it starts below mrows
+    const int nrb = (mrows + 31) / 32;
+    const int nl = nrb > wm ? (nrb - wm + 1) / 2 : 0;
+    uint16_t* cbase = C + (int64_t)m0 * NOUT;
+    switch (nl) {
+      case 4: tile_compute<SWIGLU, 4>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
+      case 3: tile_compute<SWIGLU, 3>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
+      case 2: tile_compute<SWIGLU, 2>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
+      case 1: tile_compute<SWIGLU, 1>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
+      default: tile_compute<SWIGLU, 0>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
     }
-    const int arow0 = wm * 64 + (lane & 31);
-    const int kofs = (lane >> 5) * 8;
-
-    const int nk = (KD + kBK - 1) / kBK;
-    u32x4_t ar[4], br[8];
-    gload(0, ar, br);
-    lstore(0, ar, br);
-    __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-      const int buf = ks & 1;
-      const bool more = ks + 1 < nk;
-      if (more) gload(ks + 1, ar, br);
-      const uint16_t* sa = lds + buf * kStageElems;
-      const uint16_t* sb = sa + kBM * kLD;
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        bf16x8_t a[2], b[4];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          a[rb] = __builtin_bit_cast(bf16x8_t,
-                                     *reinterpret_cast<const u32x4_t*>(sa + (arow0 + rb * 32) * kLD + kk * 16 + kofs));
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          b[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sb + brow[cb] * kLD + kk * 16 + kofs));
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
-      }
-      if (more) lstore(buf ^ 1, ar, br);
-      __syncthreads();
-    }
-
-    // epilogue: tile -> LDS (bf16, [kBM][BNO + 8]) -> 16-byte coalesced stores
-    constexpr int LDO = BNO + 8;
-    uint16_t* ot = lds;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + rb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (SWIGLU) {
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            const float gv = acc[rb][cb][r], uv = acc[rb][cb + 2][r];
-            const float hv = gv / (1.f + expf(-gv)) * uv;
-            ot[row * LDO + wn * 64 + cb * 32 + (lane & 31)] = f32_to_bf16(hv);
-          }
-        } else {
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            ot[row * LDO + wn * 128 + cb * 32 + (lane & 31)] = f32_to_bf16(acc[rb][cb][r]);
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int CPR = BNO / 8;  // 16-byte chunks per tile row
-    for (int i = tid; i < kBM * CPR; i += 256) {
-      const int row = i / CPR, ch = i - row * CPR;
-      const int col = n0 + ch * 8;
-      if (row < mrows && col < NOUT)
-        *reinterpret_cast<u32x4_t*>(C + (int64_t)(m0 + row) * NOUT + col) =
-            *reinterpret_cast<const u32x4_t*>(ot + row * LDO + ch * 8);
-    }
-    __syncthreads();
+    __syncthreads();  // LDS stages are reused by the next tile
   }
 }
 
@@ -302,7 +376,7 @@ static moge_status_t launch_ggemm(const uint16_t* A, const int32_t* offsets, int
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
   const int64_t NT = (NOUT + BNO - 1) / BNO;
   const int64_t upper = ((rows_cap + kBM - 1) / kBM + E) * NT;  // >= live tiles
-  int64_t grid = device_cus();                                   // one 108 KiB-LDS workgroup per CU
+  int64_t grid = device_cus();                                   // one 120 KiB-LDS workgroup per CU
   if (upper < grid) grid = upper;
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL(ggemm_bf16_kernel<SWIGLU>, dim3((unsigned)grid), dim3(256), kGemmLds, stream, A, offsets, e_lo,

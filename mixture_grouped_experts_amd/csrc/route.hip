@@ -30,8 +30,11 @@ namespace moge {
 
 // Softmax over the token's N scores (LDS row `l`) and the per-group choice.
 // One full wave per token; lane owns experts lane, lane+64, lane+128, lane+192.
-// rank(e) = #{e' in group(e) : l[e'] > l[e] or (l[e'] == l[e] and e' < e)};
-// experts with rank < k are written to slot g*k + rank.
+// Narrow groups (G <= 64): rank(e) = #{e' in group(e) : l[e'] > l[e] or
+// (l[e'] == l[e] and e' < e)}; experts with rank < k go to slot g*k + rank.
+// Wide groups (G > 64, e.g. the global top-K over 256 experts): k rounds of a
+// wave-wide argmax with the same order (higher score, then lower id) per group;
+// round r fills slot g*k + r, which is the same slot the rank rule gives.
 __device__ __forceinline__ void select_token(const float* __restrict__ l, int N, int n_groups, int k, int64_t t,
                                              int32_t* __restrict__ idx, float* __restrict__ gate) {
   const int lane = threadIdx.x & 63;
@@ -54,20 +57,54 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int N,
     z += ex[j];
   }
   z = wave_sum(z);
+  if (G <= 64) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    if (e < N) {
-      const int g = e / G;
-      const int base = g * G;
-      int rank = 0;
-      for (int e2 = base; e2 < base + G; ++e2) {
-        const float w = l[e2];
-        rank += (w > v[j]) || (w == v[j] && e2 < e);
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (e < N) {
+        const int g = e / G;
+        const int base = g * G;
+        int rank = 0;
+        for (int e2 = base; e2 < base + G; ++e2) {
+          const float w = l[e2];
+          rank += (w > v[j]) || (w == v[j] && e2 < e);
+        }
+        if (rank < k) {
+          idx[t * K + g * k + rank] = e;
+          gate[t * K + g * k + rank] = ex[j] / z;
+        }
       }
-      if (rank < k) {
-        idx[t * K + g * k + rank] = e;
-        gate[t * K + g * k + rank] = ex[j] / z;
+    }
+    return;
+  }
+  unsigned taken = 0u;  // bit j: expert lane + 64j already chosen
+  for (int g = 0; g < n_groups; ++g) {
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        if (e < N && e / G == g && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      // the owner of expert bi records it
+      if ((bi & 63) == lane) {
+        const int j = bi >> 6;
+        taken |= 1u << j;
+        idx[t * K + g * k + r] = bi;
+        gate[t * K + g * k + r] = ex[j] / z;
       }
     }
   }
@@ -206,6 +243,82 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(int64_t T, int d, int N
 }
 
 // ----------------------------------------------------------------------------
+// bf16 scores for few tokens: 32 tokens per workgroup; the 4 waves split the
+// experts (WC column groups of 64) and the hidden dimension (4/WC parts), so a
+// small batch still spreads over many waves.  Operands are read straight from
+// global memory in MFMA layout; the partial sums meet in LDS and are added in a
+// fixed order (deterministic).
+template <int WC>
+__global__ __launch_bounds__(256) void route_mfma_splitk_kernel(int64_t T, int d, int N, int n_groups, int k,
+                                                                const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ w,
+                                                                const float* __restrict__ bias,
+                                                                float* __restrict__ logits_out,
+                                                                int32_t* __restrict__ idx, float* __restrict__ gate) {
+  constexpr int KS = 4 / WC;
+  constexpr int NP = 64 * WC;
+  constexpr int TM = 32;
+  __shared__ __attribute__((aligned(16))) float part[KS * TM * NP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wc = wave % WC, q = wave / WC;
+  const int64_t t0 = (int64_t)blockIdx.x * TM;
+  int64_t arow = t0 + (lane & 31);
+  if (arow > T - 1) arow = T - 1;
+  const uint16_t* ap = x + arow * d + (lane >> 5) * 8;
+  const uint16_t* bp[2];
+  bool bval[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int col = wc * 64 + cb * 32 + (lane & 31);
+    bval[cb] = col < N;
+    bp[cb] = w + (int64_t)(col < N ? col : 0) * d + (lane >> 5) * 8;
+  }
+  f32x16_t acc[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+  const int nk = (d + 63) / 64;
+  for (int ks = q; ks < nk; ks += KS) {
+    u32x4_t a[4], b[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = ks * 64 + j * 16 + (lane >> 5) * 8;
+      const u32x4_t zero = {0u, 0u, 0u, 0u};
+      a[j] = kk < d ? *reinterpret_cast<const u32x4_t*>(ap + ks * 64 + j * 16) : zero;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        b[cb][j] = (kk < d && bval[cb]) ? *reinterpret_cast<const u32x4_t*>(bp[cb] + ks * 64 + j * 16) : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
+                                                          __builtin_bit_cast(bf16x8_t, b[cb][j]), acc[cb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int col = wc * 64 + cb * 32 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      part[(q * TM + row) * NP + col] = acc[cb][r];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TM * NP; i += 256) {
+    const int col = i % NP;
+    float v = part[i];
+#pragma unroll
+    for (int p = 1; p < KS; ++p) v += part[p * TM * NP + i];
+    part[i] = col < N ? v + (bias ? bias[col] : 0.f) : -INFINITY;
+  }
+  __syncthreads();
+  tile_epilogue(part, NP, TM, t0, T, N, n_groups, k, logits_out, idx, gate);
+}
+
+// ----------------------------------------------------------------------------
 // float32 scores on the vector ALUs (small shapes).  16 tokens per workgroup.
 constexpr int kF32Tokens = 16;
 __global__ __launch_bounds__(256) void route_f32_kernel(int64_t T, int d, int N, int n_groups, int k,
@@ -286,12 +399,23 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
                        idx, gate);
     st = check_launch("route_f32_kernel");
   } else {
-    if (s.N <= 64)
+    // few tokens (fewer 128-token tiles than CUs) and N <= 128: the split-K kernel
+    const bool few = ((int64_t)s.T + 127) / 128 < 256;
+    if (few && s.N <= 64) {
+      hipLaunchKernelGGL(route_mfma_splitk_kernel<1>, dim3((unsigned)(((int64_t)s.T + 31) / 32)), dim3(256), 0,
+                         stream, (int64_t)s.T, s.d, s.N, n_groups, k, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w_router), bias, logits, idx, gate);
+    } else if (few && s.N <= 128) {
+      hipLaunchKernelGGL(route_mfma_splitk_kernel<2>, dim3((unsigned)(((int64_t)s.T + 31) / 32)), dim3(256), 0,
+                         stream, (int64_t)s.T, s.d, s.N, n_groups, k, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w_router), bias, logits, idx, gate);
+    } else if (s.N <= 64) {
       launch_route_mfma<1, 128>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
-    else if (s.N <= 128)
+    } else if (s.N <= 128) {
       launch_route_mfma<2, 128>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
-    else
+    } else {
       launch_route_mfma<4, 64>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+    }
     st = check_launch("route_mfma_kernel");
   }
   return st == MOGE_OK ? ok() : st;
