@@ -8,20 +8,20 @@
 // (Pangu Pro MoE, lsdiaocha.cn summary, section 3): it is bound by weight
 // traffic at high concurrency and double-buffers its loads.  That kernel was
 // written for Ascend; on gfx950 the same ideas become:
-//   * bf16 v_mfma_f32_32x32x16_bf16 with float32 accumulators; a 256-thread
-//     workgroup owns a 256-row x 256-weight-row tile (GEMM 1: 128 gate + 128 up
-//     rows of the same 128 h columns, so the SwiGLU is fused into the epilogue;
-//     GEMM 2: 256 output columns) and each wave a 128 x 128 quarter of it (16
-//     accumulator blocks, 8 fragment reads per 16 MFMAs);
-//   * A and B panels staged in LDS in BK = 32 steps through a 3-stage LDS ring
-//     fed by 2 register stages, so every global load has about two steps of
-//     MFMA work to arrive; rows padded by 16 B so the 16-byte fragment reads are
-//     bank-conflict free; one barrier per step;
+//   * bf16 v_mfma_f32_32x32x16_bf16 with float32 accumulators; a 512-thread
+//     workgroup (two waves per SIMD) owns a 320-row x 256-weight-row tile (GEMM 1:
+//     128 gate + 128 up rows of the same 128 h columns, so the SwiGLU is fused into
+//     the epilogue; GEMM 2: 256 output columns), each wave a 160 x 64 part of it;
+//   * both panels go straight from global memory to a 4-stage LDS ring
+//     (global_load_lds_dwordx4, BK = 32), so every load has about two steps of
+//     MFMA work to arrive and no registers stage it; 64-byte LDS rows with an
+//     XOR swizzle keep the 16-byte fragment reads bank-conflict free at the
+//     LDS's full rate, which takes at least two waves per SIMD to reach;
 //   * a tile with few live rows (the last tile of an expert) skips the MFMAs of
 //     its empty 32-row blocks; the row blocks are interleaved over the waves;
 //   * a persistent grid walks a device-built tile list (no host sync on the
 //     expert counts): every workgroup derives the per-expert tile counts from
-//     `offsets` in LDS.  Tiles of one expert are ordered in groups of 8 m-tiles,
+//     `offsets` in LDS.  Tiles of one expert are ordered in groups of 4 m-tiles,
 //     n-tiles outer, so tiles that share a weight panel or an activation panel
 //     run at the same time; consecutive tiles go to one XCD (workgroup b runs on
 //     XCD b % 8), so that sharing happens in that XCD's L2;
@@ -35,72 +35,85 @@
 
 namespace moge {
 
-constexpr int kBM = 256;                    // token rows per tile
+constexpr int kBM = 320;                    // token rows per tile (10 blocks of 32)
 constexpr int kBW = 256;                    // weight rows per tile
 constexpr int kBK = 32;                     // reduction step (elements)
 constexpr int kRowB = kBK * 2;              // 64-byte LDS rows (unpadded; chunks are XOR-swizzled)
-constexpr int kStageB = (kBM + kBW) * kRowB;  // 32 KiB per stage
+constexpr int kStageB = (kBM + kBW) * kRowB;  // 36 KiB per stage
 constexpr int kStages = 4;
-constexpr size_t kGemmLds = (size_t)kStages * kStageB;  // 128 KiB
+constexpr size_t kGemmLds = (size_t)kStages * kStageB;  // 144 KiB
+constexpr int kThreads = 512;               // 8 waves: two per SIMD
 constexpr int kGroupM = 4;                  // m-tiles per scheduling group
 
-// 16-byte chunk c of LDS row r lives in slot c ^ swz(r): two rows share a 128-byte
-// bank line, so this spreads the 32 rows of a fragment read over all banks.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+// 16-byte chunk c of LDS row r lives in slot c ^ swz(r).  Four 64-byte rows share a
+// 256-byte bank line; with this swizzle the 16 rows that one fragment read touches
+// per clock cover all 64 banks (measured conflict-free on gfx950).
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
-// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory
-// operations of this wave are outstanding; LDS and export counters untouched.
+// s_waitcnt immediates (gfx9 encoding): at most n vector memory operations of this
+// wave outstanding; the second form also waits for all of the wave's LDS reads.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-// the same, and every LDS read of this wave has returned its data
 constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 
-// One tile: reduction loop and epilogue.  Wave (wm, wn) owns the token row blocks
-// wm, wm+2, wm+4, wm+6 (32 rows each, interleaved so a partly filled tile keeps
-// the four waves balanced) and 4 weight blocks of 32 rows; NL of its row blocks
-// hold live rows (the others skip their MFMAs).  The MFMA takes the weight
-// fragment as its first operand, so each lane ends with 4 consecutive output
-// columns of one token row, which the epilogue packs into 8-byte stores.
+// One tile: reduction loop and epilogue, 8 waves.  Wave (wm, wn), wm in {0,1},
+// wn in {0..3}, owns the token row blocks wm, wm+2, ..., wm+8 (32 rows each,
+// interleaved so a partly filled tile keeps the waves balanced) and 2 weight
+// blocks of 32 rows (GEMM 1: the gate and the up rows of the same 32 h columns;
+// GEMM 2: 64 output columns).  NL of its row blocks hold live rows; the others
+// skip their MFMAs.  A tile spans 320 token rows so that an expert whose row
+// count is a little above 256 (the common case when the rows spread evenly over
+// hundreds of experts) still reads each weight panel once.  The MFMA takes the
+// weight fragment as its first operand, so each lane ends with 4 consecutive
+// output columns of one token row, which the epilogue packs into 8-byte stores.
 //
 // Pipeline: global -> LDS directly (global_load_lds_dwordx4, no staging registers)
-// into a 4-stage ring.  Each wave moves 16 token rows and 16 weight rows x 64 B
-// per instruction, 8 instructions per step; step s is issued at step s-3, and the
-// step loop waits (vmcnt) for its own loads of step s+1 plus one barrier per step,
-// so every load has two steps of MFMA work to land.
+// into a 4-stage ring.  Per step waves 0-3 move token rows wave*64 .. +64 and
+// waves 4-7 weight rows (wave-4)*64 .. +64 plus token rows 256 + (wave-4)*16 .. +16,
+// 64 B per row.  Step s is issued at step s-3 and each step waits (vmcnt) for its
+// own loads of step s+2, then one barrier, so every load has two steps of MFMA work
+// to land.  Two waves per SIMD keep the MFMA pipe fed across the barriers and give
+// the LDS enough concurrent readers to reach its full rate.
 template <bool SWIGLU, int NL>
 __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint16_t* __restrict__ abase,
                                              const uint16_t* __restrict__ wbase0, const uint16_t* __restrict__ wbase1,
-                                             int KD, int wm, int wn, int mrows, int n0, int NOUT,
-                                             uint16_t* __restrict__ cbase) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                             int KD, int mrows, int n0, int NOUT, uint16_t* __restrict__ cbase) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
+  const int wm = wave & 1, wn = wave >> 1;
   const int nkf = KD / kBK;  // full steps; a ragged tail is one extra step below
-  // DMA sources: instruction j < 4 moves token rows wave*64 + 16j .. +16, j >= 4 weight rows.
-  const uint16_t* dsrc[8];
-  int ddst[8];
+  // DMA sources: instruction j < 4 moves 16 stage rows at ldsrow[j] .. +16; waves 4-7
+  // have a fifth instruction (token rows 256.. of the tile).
+  const bool wtok = wave < 4;
+  const uint16_t* dsrc[5];
+  int lrow[5];  // first stage row of each instruction (wave-uniform)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 64 + (j & 3) * 16 + (lane >> 2);  // row inside its operand (0..255)
-    const int c = (lane & 3) ^ swz(r);                       // global chunk fetched by this lane
-    if (j < 4) {
-      const int rr = r < mrows ? r : mrows - 1;
+  for (int j = 0; j < 5; ++j) {
+    lrow[j] = wtok ? wave * 64 + j * 16 : (j < 4 ? kBM + (wave - 4) * 64 + j * 16 : 256 + (wave - 4) * 16);
+    const int srow = lrow[j] + (lane >> 2);  // stage row (token rows 0..319, weight rows 320..575)
+    const int c = (lane & 3) ^ swz(srow);    // global chunk fetched by this lane
+    if (srow < kBM) {
+      const int rr = srow < mrows ? srow : mrows - 1;
       dsrc[j] = abase + (int64_t)rr * KD + c * 8;
     } else {
+      const int r = srow - kBM;
       int wr = SWIGLU ? n0 + (r & 127) : n0 + r;
       if (wr > NOUT - 1) wr = NOUT - 1;
       dsrc[j] = (SWIGLU && r >= 128 ? wbase1 : wbase0) + (int64_t)wr * KD + c * 8;
     }
-    ddst[j] = ((j < 4 ? 0 : kBM) + wave * 64 + (j & 3) * 16) * kRowB;  // wave-uniform LDS byte offset
   }
   // Step ks into stage ks % 4 (steps past the last full step reload step 0).  The
   // DMA is issued from inline assembly so the compiler does not turn its LDS side
   // effect into a full vmcnt wait before every LDS read; the waits are explicit
   // (vmcnt_imm) and each is followed by a barrier before the stage is read.  The
   // instruction has no register result, only an address operand read at issue.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   auto issue = [&](int ks) {
     const int k = ks < nkf ? ks * kBK : 0;
-    const uint32_t st = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds + (ks % kStages) * kStageB);
+    const uint32_t st = lds0 + (uint32_t)((ks % kStages) * kStageB);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t m0v = __builtin_amdgcn_readfirstlane(st + (uint32_t)ddst[j]);
+    for (int j = 0; j < 5; ++j) {
+      if (j == 4 && wtok) break;
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(st + (uint32_t)(lrow[j] * kRowB));
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                    :
                    : "v"(dsrc[j] + k), "s"(m0v)
@@ -108,45 +121,49 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
     }
   };
   const int kc = (lane >> 5);  // logical chunk of this lane inside a 16-element sub-step
-  int arow[4], brow[4];
+  int arow[5], brow[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) arow[t] = (wm + 2 * t) * 32 + (lane & 31);
+  for (int t = 0; t < 5; ++t) arow[t] = (wm + 2 * t) * 32 + (lane & 31);
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-    brow[cb] = kBM + (SWIGLU ? ((cb < 2 ? 0 : 128) + wn * 64 + (cb & 1) * 32) : (wn * 128 + cb * 32)) + (lane & 31);
-  auto frag = [&](int ks, int kk, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
-    const char* st = lds + (ks % kStages) * kStageB;
+  for (int cb = 0; cb < 2; ++cb)
+    brow[cb] = kBM + (SWIGLU ? cb * 128 + wn * 32 : wn * 64 + cb * 32) + (lane & 31);
+  auto frag = [&](int ks, int kk, bf16x8_t (&a)[5], bf16x8_t (&b)[2]) {
+    const char* sa = lds + (ks % kStages) * kStageB;
+    const char* sb = sa;
     const int c = kk * 2 + kc;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      b[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + brow[cb] * kRowB +
+    for (int cb = 0; cb < 2; ++cb)
+      b[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sb + brow[cb] * kRowB +
                                                                               ((c ^ swz(brow[cb])) << 4)));
 #pragma unroll
     for (int t = 0; t < NL; ++t)
-      a[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + arow[t] * kRowB +
+      a[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sa + arow[t] * kRowB +
                                                                              ((c ^ swz(arow[t])) << 4)));
   };
-  f32x16_t acc[NL > 0 ? NL : 1][4];
+  f32x16_t acc[NL > 0 ? NL : 1][2];
+  static_assert(NL <= 5, "five row blocks per wave at most");
 #pragma unroll
   for (int t = 0; t < (NL > 0 ? NL : 1); ++t)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][cb][r] = 0.f;
-  auto mfma = [&](const bf16x8_t (&a)[4], const bf16x8_t (&b)[4]) {
+  auto mfma = [&](const bf16x8_t (&a)[5], const bf16x8_t (&b)[2]) {
 #pragma unroll
     for (int t = 0; t < NL; ++t)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 2; ++cb)
         acc[t][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[cb], a[t], acc[t][cb], 0, 0, 0);
   };
 
-  bf16x8_t a0[4], b0[4], a1[4], b1[4];
+  bf16x8_t a0[5], b0[2], a1[5], b1[2];
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // nothing of the previous tile in flight
   issue(0);
   issue(1);
   issue(2);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));  // steps 0 and 1 landed (this wave)
+  // steps 0 and 1 landed (this wave; token waves issue 4 loads per step, the others 5)
+  if (wtok) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
   __syncthreads();
   if (NL) frag(0, 0, a0, b0);
   for (int ks = 0; ks < nkf; ++ks) {
@@ -160,16 +177,16 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int i = 0; i < 4 + NL; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        for (int i = 0; i < 2 * NL; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+          if (i < 2 + NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NL - (4 + NL), 0);
       }
     }
     // step ks+2 landed (this wave) and this step's LDS reads are done, so the DMA
     // issued after the barrier may overwrite stage ks % 4
-    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(8));
+    if (wtok) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(4));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(5));
     __syncthreads();
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing reloads before LDS is reused
@@ -179,11 +196,12 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
     const int k = nkf * kBK;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = wave * 64 + (j & 3) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ swz(r);
+    for (int j = 0; j < 5; ++j) {
+      if (j == 4 && wtok) break;
+      const int srow = lrow[j] + (lane >> 2);
+      const int c = (lane & 3) ^ swz(srow);
       const u32x4_t v = (k + c * 8 < KD) ? *reinterpret_cast<const u32x4_t*>(dsrc[j] + k) : zero;
-      *reinterpret_cast<u32x4_t*>(lds + ddst[j] + (lane << 4)) = v;
+      *reinterpret_cast<u32x4_t*>(lds + lrow[j] * kRowB + (lane << 4)) = v;
     }
     __syncthreads();
     if (NL) {
@@ -201,17 +219,17 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
     if (row < mrows) {
       uint16_t* crow = cbase + (int64_t)row * NOUT;
 #pragma unroll
-      for (int cb = 0; cb < (SWIGLU ? 2 : 4); ++cb) {
+      for (int cb = 0; cb < (SWIGLU ? 1 : 2); ++cb) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = n0 + (SWIGLU ? wn * 64 + cb * 32 : wn * 128 + cb * 32) + g4 * 8 + (lane >> 5) * 4;
+          const int col = n0 + (SWIGLU ? wn * 32 : wn * 64 + cb * 32) + g4 * 8 + (lane >> 5) * 4;
           if (col < NOUT) {
             uint16_t hv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               float v;
               if (SWIGLU) {
-                const float gv = acc[t][cb][g4 * 4 + i], uv = acc[t][cb + 2][g4 * 4 + i];
+                const float gv = acc[t][0][g4 * 4 + i], uv = acc[t][1][g4 * 4 + i];
                 v = gv / (1.f + expf(-gv)) * uv;
               } else {
                 v = acc[t][cb][g4 * 4 + i];
@@ -230,42 +248,51 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
 }
 
 template <bool SWIGLU>
-__global__ __launch_bounds__(256) void ggemm_bf16_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                         int e_lo, int E, int64_t rows_cap, const uint16_t* __restrict__ B0,
-                                                         const uint16_t* __restrict__ B1, int NOUT, int KD,
-                                                         uint16_t* __restrict__ C) {
+__global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                              const int32_t* __restrict__ offsets, int e_lo, int E,
+                                                              int64_t rows_cap, const uint16_t* __restrict__ B0,
+                                                              const uint16_t* __restrict__ B1, int NOUT, int KD,
+                                                              uint16_t* __restrict__ C) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int tp[kMaxExperts];    // inclusive prefix of tiles per expert
   __shared__ int erow[kMaxExperts];  // rows per expert, clipped to [0, rows_cap)
-  __shared__ int scratch[4];
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;  // output columns per tile
   const int NT = (NOUT + BNO - 1) / BNO;
   const int64_t wrows = NOUT;  // weight rows per expert in B0/B1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 
-  // per-expert tile counts -> inclusive prefix (E <= 256)
-  {
-    int tiles = 0;
-    if (tid < E) {
-      const int64_t seg0 = (int64_t)offsets[e_lo + tid] - offsets[e_lo];
-      int64_t rows = (int64_t)offsets[e_lo + tid + 1] - offsets[e_lo + tid];
-      if (seg0 < 0 || rows < 0) rows = 0;
-      if (seg0 + rows > rows_cap) rows = rows_cap > seg0 ? rows_cap - seg0 : 0;
-      erow[tid] = (int)rows;
-      tiles = (int)((rows + kBM - 1) / kBM) * NT;
+  // per-expert tile counts -> inclusive prefix (E <= 256), by wave 0
+  if (wave == 0) {
+    int run = 0;
+    for (int b = 0; b < E; b += 64) {
+      const int i = b + lane;
+      int tiles = 0;
+      if (i < E) {
+        const int64_t seg0 = (int64_t)offsets[e_lo + i] - offsets[e_lo];
+        int64_t rows = (int64_t)offsets[e_lo + i + 1] - offsets[e_lo + i];
+        if (seg0 < 0 || rows < 0) rows = 0;
+        if (seg0 + rows > rows_cap) rows = rows_cap > seg0 ? rows_cap - seg0 : 0;
+        erow[i] = (int)rows;
+        tiles = (int)((rows + kBM - 1) / kBM) * NT;
+      }
+      int incl = tiles;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += u;
+      }
+      if (i < E) tp[i] = run + incl;
+      run += __shfl(incl, 63, 64);
     }
-    int tot;
-    const int ex = block_exclusive_scan(tiles, scratch, &tot);
-    if (tid < E) tp[tid] = ex + tiles;
-    __syncthreads();
   }
+  __syncthreads();
   const int total = E > 0 ? tp[E - 1] : 0;
   const int base0 = offsets[e_lo];
 
   const int P = gridDim.x;  // multiple of 8
   const int per_xcd = P >> 3;
   const int slot = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+
   for (int tile = slot; tile < total; tile += P) {
     // expert of this tile: first i with tp[i] > tile
     int lo = 0, hi = E - 1;
@@ -287,21 +314,22 @@ __global__ __launch_bounds__(256) void ggemm_bf16_kernel(const uint16_t* __restr
     const int m0 = seg0 + mt * kBM;
     const int mrows = (erows - mt * kBM) < kBM ? (erows - mt * kBM) : kBM;
     const int n0 = nt * BNO;
-
     const uint16_t* abase = A + (int64_t)m0 * KD;
     const uint16_t* wb0 = B0 + (int64_t)ei * wrows * KD;
     const uint16_t* wb1 = SWIGLU ? B1 + (int64_t)ei * wrows * KD : wb0;
+    uint16_t* cbase = C + (int64_t)m0 * NOUT;
 
     // live row blocks of this wave (wave-uniform): block wm + 2t is live if it starts below mrows
+    const int wm = wave & 1;
     const int nrb = (mrows + 31) / 32;
     const int nl = nrb > wm ? (nrb - wm + 1) / 2 : 0;
-    uint16_t* cbase = C + (int64_t)m0 * NOUT;
     switch (nl) {
-      case 4: tile_compute<SWIGLU, 4>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
-      case 3: tile_compute<SWIGLU, 3>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
-      case 2: tile_compute<SWIGLU, 2>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
-      case 1: tile_compute<SWIGLU, 1>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
-      default: tile_compute<SWIGLU, 0>(lds, abase, wb0, wb1, KD, wm, wn, mrows, n0, NOUT, cbase); break;
+      case 5: tile_compute<SWIGLU, 5>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
+      case 4: tile_compute<SWIGLU, 4>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
+      case 3: tile_compute<SWIGLU, 3>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
+      case 2: tile_compute<SWIGLU, 2>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
+      case 1: tile_compute<SWIGLU, 1>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
+      default: tile_compute<SWIGLU, 0>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
     }
     __syncthreads();  // LDS stages are reused by the next tile
   }
@@ -376,10 +404,10 @@ static moge_status_t launch_ggemm(const uint16_t* A, const int32_t* offsets, int
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
   const int64_t NT = (NOUT + BNO - 1) / BNO;
   const int64_t upper = ((rows_cap + kBM - 1) / kBM + E) * NT;  // >= live tiles
-  int64_t grid = device_cus();                                   // one 120 KiB-LDS workgroup per CU
+  int64_t grid = device_cus();                                   // one 144 KiB-LDS workgroup per CU
   if (upper < grid) grid = upper;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL(ggemm_bf16_kernel<SWIGLU>, dim3((unsigned)grid), dim3(256), kGemmLds, stream, A, offsets, e_lo,
+  hipLaunchKernelGGL(ggemm_bf16_kernel<SWIGLU>, dim3((unsigned)grid), dim3(kThreads), kGemmLds, stream, A, offsets, e_lo,
                      E, rows_cap, B0, B1, NOUT, KD, C);
   return check_launch(SWIGLU ? "ggemm_bf16_kernel<gate_up>" : "ggemm_bf16_kernel<down>");
 }
