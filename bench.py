@@ -19,6 +19,7 @@ its algorithmic bytes (weights + activations it must move) and FLOPs per launch.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -181,6 +182,11 @@ def main():
     torch.cuda.set_device(0)
     dv = H.device_inputs(w)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi)
+    if w.F:
+        # expert weights are packed once, at load time (outside the timed steps)
+        (pg, pu, pd), ps = layer.pack_expert_weights(dv.w_gate, dv.w_up, dv.w_down, dv.shared)
+        dv = dataclasses.replace(dv, w_gate=pg, w_up=pu, w_down=pd, shared=ps)
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step(marks=None):

@@ -19,11 +19,14 @@
  *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     never allocates or frees device memory and keeps no global state.
- *   - Dense tensors are row-major and contiguous.  Weights use the
+ *     never allocates or frees device memory and keeps no per-call state.
+ *   - Tensors are contiguous.  x, logits, idx, gate, inv, the expert outputs
+ *     and y are row-major; the operands of the expert GEMMs use the tiled
+ *     layout described at moge_tiled_elems.  Weights come in the
  *     (out_features, in_features) layout of a linear layer:
  *       w_router [N][d];  w_gate, w_up [E][F][d];  w_down [E][d][F]
- *     where E is the number of experts the array holds (see moge_grouped_ffn).
+ *     where E is the number of experts the array holds; the expert weights are
+ *     packed once into the tiled layout (moge_pack_weights) before use.
  *   - dtype MOGE_BF16: x, weights, x_perm, h and expert outputs are bf16
  *     (uint16 bit patterns); logits, gates and y are float32; bf16 matrix
  *     products use MFMA with float32 accumulation.
@@ -88,14 +91,52 @@ typedef struct {
 /* Host-only shape check (no device call; usable without a GPU). */
 moge_status_t moge_validate(const moge_shape_t* shape);
 
-/* Largest number of rows that (t, slot) pairs of experts in [e_lo, e_hi) can
- * produce under `mode`: GROUPED -> T * sum_g min(K', |[e_lo,e_hi) & group g|);
- * GLOBAL -> T * min(K, e_hi - e_lo).  Returns -1 on invalid arguments.
- * Buffers x_perm, h and expert outputs need this many rows. */
+/*
+ * Tiled layout.  The operands of the expert GEMMs (x_perm, h, the shared
+ * expert's copy of x and the packed expert weights) are stored in tiles of
+ * 16 rows x 32 columns.  With Cp = cols rounded up to a multiple of 32,
+ * element (r, c) of such a matrix is at element index
+ *     ((r / 16) * (Cp / 32) + c / 32) * 512 + (r % 16) * 32 + (c % 32),
+ * i.e. each 16 x 32 tile is one contiguous block of 512 elements (1 KiB in
+ * bf16) and the tiles of a 16-row band follow each other.  Columns cols .. Cp-1
+ * hold zeros.  A GEMM step reads whole tiles: one contiguous burst per 16 rows
+ * instead of 16 separate 64-byte pieces of long rows.
+ *
+ * Row numbering of the permuted rows (x_perm, h and the expert outputs).
+ * Expert e in [e_lo, e_hi) owns local rows P(e) .. P(e) + counts[e] - 1, where
+ *     P(e_lo) = 0,   P(e + 1) = P(e) + 16 * ceil(counts[e] / 16),
+ * so every expert's segment starts on a 16-row boundary and no tile holds rows
+ * of two experts.  The up to 15 padding rows after a segment are never written
+ * into a live output; perm marks them -1.
+ */
+
+/* Largest number of (padded) rows that (t, slot) pairs of experts in [e_lo, e_hi)
+ * can occupy under `mode`: the assignment bound (GROUPED -> T * sum_g min(K',
+ * |[e_lo,e_hi) & group g|); GLOBAL -> T * min(K, e_hi - e_lo)) plus 15 padding
+ * rows per expert of the range.  Returns -1 on invalid arguments.  perm, x_perm,
+ * h and the expert outputs need this many rows. */
 int64_t moge_rows_bound(const moge_shape_t* shape, int32_t mode, int32_t e_lo, int32_t e_hi);
+
+/* Elements of one tiled matrix of `rows` activation rows: ceil16(rows) * ceil32(cols). */
+int64_t moge_tiled_elems(int64_t rows, int64_t cols);
+
+/* Elements of one packed expert weight matrix: ceil32(rows) * ceil32(cols). */
+int64_t moge_packed_weight_elems(int64_t rows, int64_t cols);
 
 /* Bytes of device workspace a stage needs (0 if none; (size_t)-1 if invalid). */
 size_t moge_workspace_size(const moge_shape_t* shape, int32_t stage);
+
+/*
+ * moge_pack_weights -- E row-major matrices src [E][rows][cols] (dtype) into the
+ * tiled layout, rows padded with zero rows to a multiple of 32 and columns with
+ * zeros to a multiple of 32: dst holds E * moge_packed_weight_elems(rows, cols)
+ * elements, expert after expert.  Weights are packed once, when they are
+ * loaded; the expert GEMMs read packed weights only.  For an expert's SwiGLU
+ * block: w_gate and w_up have rows = F, cols = d; w_down has rows = d, cols = F.
+ * src and dst must not overlap.  Requires cols % 8 == 0 and rows >= 1.
+ */
+moge_status_t moge_pack_weights(int32_t dtype, int64_t E, int64_t rows, int64_t cols, const void* src, void* dst,
+                                hipStream_t stream);
 
 /*
  * moge_route -- router scores, global softmax, top-K' per group ([P1] section 1).
@@ -117,17 +158,21 @@ moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, const void* x,
  * moge_dispatch -- per-expert counts and the token permutation (dropless: every
  * (token, slot) pair gets a row; [P4]), plus the gather of x into expert order.
  *   idx      [T][K] int32 from moge_route with the same `mode`.
- *   x        [T][d] (dtype).
+ *   x        [T][d] (dtype), row-major.
  *   [e_lo, e_hi) experts whose rows are materialised (a device's share, e.g.
  *            one group); 0 <= e_lo < e_hi <= N.
  *   rows_cap rows available in perm / x_perm; must be >= moge_rows_bound().
  *   counts   [N] int32 out: rows per expert (all N experts).
  *   offsets  [N+1] int32 out: exclusive prefix sum of counts (all N experts).
- *   inv      [T][K] int32 out: local row of (t, slot) = offsets[e] - offsets[e_lo]
- *            + #{t' < t that chose e}; -1 when the expert is outside [e_lo, e_hi).
- *   perm     [rows_cap] int32 out: token of each local row (rows >= the live
- *            count offsets[e_hi]-offsets[e_lo] are left untouched).
- *   x_perm   [rows_cap][d] (dtype) out: x_perm[r] = x[perm[r]].
+ *   inv      [T][K] int32 out: local row of (t, slot) = P(e) + #{t' < t that
+ *            chose e} (P as defined at the tiled layout above); -1 when the
+ *            expert is outside [e_lo, e_hi).
+ *   perm     [rows_cap] int32 out: token of each local row, -1 on the padding
+ *            rows of a segment (rows past P(e_hi) are left untouched).
+ *   x_perm   tiled, rows_cap rows x d columns (dtype) out: row r = x[perm[r]]
+ *            for live rows; padding rows are left unspecified.
+ *   x_tiled  tiled, T rows x d columns (dtype) out, or NULL: x in token order
+ *            (the input of the always-on shared expert).  Needs x.
  *   ws       device workspace of moge_workspace_size(shape, MOGE_STAGE_DISPATCH) bytes.
  * Rows of one expert are in ascending token order, so the result is unique and
  * deterministic.  Expert ids outside [0, N) in idx are ignored (memory-safe).
@@ -137,22 +182,24 @@ moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, const void* x,
  */
 moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
                             int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts, int32_t* offsets,
-                            int32_t* inv, int32_t* perm, void* x_perm, void* ws, size_t ws_bytes,
+                            int32_t* inv, int32_t* perm, void* x_perm, void* x_tiled, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
 /*
  * moge_grouped_ffn -- the SwiGLU expert applied to every expert's row segment
  * (a grouped GEMM pair).
- *   x_perm   [rows_cap][d]; local row r belongs to expert e when
- *            offsets[e]-offsets[e_lo] <= r < offsets[e+1]-offsets[e_lo].
+ *   x_perm   tiled, rows_cap rows x d columns: local rows P(e) .. P(e)+counts[e]-1
+ *            belong to expert e (counts[e] = offsets[e+1] - offsets[e]).
  *   offsets  [N+1] int32 device (from moge_dispatch).
- *   w_gate, w_up [e_hi-e_lo][F][d]; w_down [e_hi-e_lo][d][F]: the arrays hold
- *            experts e_lo .. e_hi-1 only (a device's share of the weights).
- *   h        [rows_cap][F] scratch (dtype): silu(x.Wg^T) * (x.Wu^T), rounded to
- *            dtype before the down projection.
- *   out      [rows_cap][d] (dtype): FFN_e(x_perm[r]) for every live row.
+ *   w_gate, w_up: packed (moge_pack_weights) [e_hi-e_lo] x (F rows x d cols);
+ *   w_down:  packed [e_hi-e_lo] x (d rows x F cols): the arrays hold experts
+ *            e_lo .. e_hi-1 only (a device's share of the weights).
+ *   h        tiled, rows_cap rows x F columns, scratch (dtype): silu(x.Wg^T) *
+ *            (x.Wu^T), rounded to dtype before the down projection.
+ *   out      [rows_cap][d] (dtype), row-major: FFN_e(x_perm[r]) for every live row.
  * The always-on shared expert is the same call with a one-expert shape
- * (N = M = k_per_group = 1, F = shared width), offsets = {0, T} and x_perm = x.
+ * (N = M = k_per_group = 1, F = shared width), offsets = {0, T} and x_perm = the
+ * x_tiled copy written by moge_dispatch.
  */
 moge_status_t moge_grouped_ffn(const moge_shape_t* shape, const void* x_perm, const int32_t* offsets,
                                int32_t e_lo, int32_t e_hi, int64_t rows_cap, const void* w_gate,

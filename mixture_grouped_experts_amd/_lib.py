@@ -30,9 +30,10 @@ ROUTE_GROUPED = 0
 ROUTE_GLOBAL = 1
 STAGE_DISPATCH = 1
 
-EXPORTS = ("moge_validate", "moge_rows_bound", "moge_workspace_size", "moge_route", "moge_dispatch",
-           "moge_grouped_ffn", "moge_expert_gate_up", "moge_expert_down", "moge_combine", "moge_imbalance",
-           "moge_version", "moge_last_error")
+EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_weight_elems",
+           "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_grouped_ffn",
+           "moge_expert_gate_up", "moge_expert_down", "moge_combine", "moge_imbalance", "moge_version",
+           "moge_last_error")
 
 
 class Shape(ctypes.Structure):
@@ -63,11 +64,18 @@ _lib.moge_validate.argtypes = [_SP]
 _lib.moge_validate.restype = ctypes.c_int
 _lib.moge_rows_bound.argtypes = [_SP, _I32, _I32, _I32]
 _lib.moge_rows_bound.restype = _I64
+_lib.moge_tiled_elems.argtypes = [_I64, _I64]
+_lib.moge_tiled_elems.restype = _I64
+_lib.moge_packed_weight_elems.argtypes = [_I64, _I64]
+_lib.moge_packed_weight_elems.restype = _I64
+_lib.moge_pack_weights.argtypes = [_I32, _I64, _I64, _I64, _P, _P, _P]
+_lib.moge_pack_weights.restype = ctypes.c_int
 _lib.moge_workspace_size.argtypes = [_SP, _I32]
 _lib.moge_workspace_size.restype = ctypes.c_size_t
 _lib.moge_route.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _P]
 _lib.moge_route.restype = ctypes.c_int
-_lib.moge_dispatch.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.moge_dispatch.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                               _P]
 _lib.moge_dispatch.restype = ctypes.c_int
 _lib.moge_grouped_ffn.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P]
 _lib.moge_grouped_ffn.restype = ctypes.c_int
@@ -126,6 +134,27 @@ def rows_bound(shape: Shape, mode: int, e_lo: int, e_hi: int) -> int:
     return int(_lib.moge_rows_bound(ctypes.byref(shape), mode, e_lo, e_hi))
 
 
+def tiled_elems(rows: int, cols: int) -> int:
+    """Elements of a tiled activation matrix: rows rounded up to 16 times cols rounded up to 32."""
+    return int(_lib.moge_tiled_elems(rows, cols))
+
+
+def packed_weight_elems(rows: int, cols: int) -> int:
+    """Elements of one packed expert weight matrix: rows and cols rounded up to 32."""
+    return int(_lib.moge_packed_weight_elems(rows, cols))
+
+
+def pack_weights(dtype: int, w, out, stream=None) -> None:
+    """w [E][rows][cols] row-major -> out, E * packed_weight_elems(rows, cols) elements (tiled)."""
+    if w is None or w.dim() != 3:
+        raise ValueError("w must be a 3-d tensor [E][rows][cols]")
+    E, rows, cols = w.shape
+    et = torch.bfloat16 if dtype == BF16 else torch.float32
+    st = _lib.moge_pack_weights(dtype, E, rows, cols, _ptr(w, "w", et, E * rows * cols),
+                                _ptr(out, "out", et, E * packed_weight_elems(rows, cols)), _stream(stream))
+    _check("moge_pack_weights", st)
+
+
 def workspace_size(shape: Shape, stage: int = STAGE_DISPATCH) -> int:
     return int(_lib.moge_workspace_size(ctypes.byref(shape), stage))
 
@@ -151,7 +180,7 @@ def route(shape: Shape, mode: int, x, w_router, bias, logits, idx, gate, stream=
 
 
 def dispatch(shape: Shape, mode: int, idx, x, e_lo: int, e_hi: int, rows_cap: int, counts, offsets, inv, perm,
-             x_perm, ws, stream=None) -> None:
+             x_perm, ws, x_tiled=None, stream=None) -> None:
     T, N, K, d = shape.T, shape.N, shape.K, shape.d
     et = _elem_dtype(shape)
     st = _lib.moge_dispatch(ctypes.byref(shape), mode, _ptr(idx, "idx", torch.int32, T * K),
@@ -159,7 +188,8 @@ def dispatch(shape: Shape, mode: int, idx, x, e_lo: int, e_hi: int, rows_cap: in
                             _ptr(counts, "counts", torch.int32, N), _ptr(offsets, "offsets", torch.int32, N + 1),
                             _ptr(inv, "inv", torch.int32, T * K, optional=True),
                             _ptr(perm, "perm", torch.int32, rows_cap, optional=True),
-                            _ptr(x_perm, "x_perm", et, rows_cap * d, optional=True), _ptr(ws, "ws", None, None),
+                            _ptr(x_perm, "x_perm", et, tiled_elems(rows_cap, d), optional=True),
+                            _ptr(x_tiled, "x_tiled", et, tiled_elems(T, d), optional=True), _ptr(ws, "ws", None, None),
                             ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check("moge_dispatch", st)
 
@@ -169,11 +199,13 @@ def grouped_ffn(shape: Shape, x_perm, offsets, e_lo: int, e_hi: int, rows_cap: i
     d, F = shape.d, shape.F
     E = e_hi - e_lo
     et = _elem_dtype(shape)
-    st = _lib.moge_grouped_ffn(ctypes.byref(shape), _ptr(x_perm, "x_perm", et, rows_cap * d),
+    st = _lib.moge_grouped_ffn(ctypes.byref(shape), _ptr(x_perm, "x_perm", et, tiled_elems(rows_cap, d)),
                                _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
-                               _ptr(w_gate, "w_gate", et, E * F * d), _ptr(w_up, "w_up", et, E * F * d),
-                               _ptr(w_down, "w_down", et, E * d * F), _ptr(h, "h", et, rows_cap * F),
-                               _ptr(out, "out", et, rows_cap * d), _stream(stream))
+                               _ptr(w_gate, "w_gate", et, E * packed_weight_elems(F, d)),
+                               _ptr(w_up, "w_up", et, E * packed_weight_elems(F, d)),
+                               _ptr(w_down, "w_down", et, E * packed_weight_elems(d, F)),
+                               _ptr(h, "h", et, tiled_elems(rows_cap, F)), _ptr(out, "out", et, rows_cap * d),
+                               _stream(stream))
     _check("moge_grouped_ffn", st)
 
 
@@ -182,10 +214,11 @@ def expert_gate_up(shape: Shape, x_perm, offsets, e_lo: int, e_hi: int, rows_cap
     d, F = shape.d, shape.F
     E = e_hi - e_lo
     et = _elem_dtype(shape)
-    st = _lib.moge_expert_gate_up(ctypes.byref(shape), _ptr(x_perm, "x_perm", et, rows_cap * d),
+    st = _lib.moge_expert_gate_up(ctypes.byref(shape), _ptr(x_perm, "x_perm", et, tiled_elems(rows_cap, d)),
                                   _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
-                                  _ptr(w_gate, "w_gate", et, E * F * d), _ptr(w_up, "w_up", et, E * F * d),
-                                  _ptr(h, "h", et, rows_cap * F), _stream(stream))
+                                  _ptr(w_gate, "w_gate", et, E * packed_weight_elems(F, d)),
+                                  _ptr(w_up, "w_up", et, E * packed_weight_elems(F, d)),
+                                  _ptr(h, "h", et, tiled_elems(rows_cap, F)), _stream(stream))
     _check("moge_expert_gate_up", st)
 
 
@@ -193,10 +226,10 @@ def expert_down(shape: Shape, h, offsets, e_lo: int, e_hi: int, rows_cap: int, w
     d, F = shape.d, shape.F
     E = e_hi - e_lo
     et = _elem_dtype(shape)
-    st = _lib.moge_expert_down(ctypes.byref(shape), _ptr(h, "h", et, rows_cap * F),
+    st = _lib.moge_expert_down(ctypes.byref(shape), _ptr(h, "h", et, tiled_elems(rows_cap, F)),
                                _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
-                               _ptr(w_down, "w_down", et, E * d * F), _ptr(out, "out", et, rows_cap * d),
-                               _stream(stream))
+                               _ptr(w_down, "w_down", et, E * packed_weight_elems(d, F)),
+                               _ptr(out, "out", et, rows_cap * d), _stream(stream))
     _check("moge_expert_down", st)
 
 

@@ -14,7 +14,11 @@
 //                             of lower lanes that chose the same expert, so rows of
 //                             an expert stay in ascending token order -> inv, perm.
 //   4. dispatch_copy_kernel   one wave per token reads its row from HBM once and
-//                             writes it to all of its slots' rows (16-byte stores).
+//                             writes it to all of its slots' rows (16-byte stores)
+//                             in the tiled layout the expert GEMMs read, plus the
+//                             token-order tiled copy the shared expert reads.
+// Every expert's rows start on a 16-row boundary (P(e) in moge.h), so a 16-row
+// tile of the GEMM operands never mixes experts.
 #include "moge_internal.hpp"
 
 namespace moge {
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int64_t nb, const in
   if (threadIdx.x == 0) counts[e] = running;
 }
 
-// Dynamic LDS: keys[kTB][KS] | rows[kTB][KS] | offs[N+1] | base[N] | hist[4][N]
+// Dynamic LDS: keys[kTB][KS] | rows[kTB][KS] | offs[N+1] | base[N] | hist[4][N] | pbase[N+1]
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     int64_t T, int K, int N, int64_t nb, const int32_t* __restrict__ idx, int e_lo, int e_hi, int64_t rows_cap,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ bprefix, int32_t* __restrict__ offsets_out,
@@ -71,6 +75,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
   int* offs = rows + kTB * KS;
   int* base = offs + (N + 1);
   int* hist = base + N;  // [4][N]
+  int* pbase = hist + 4 * N;  // P(e): first local row of expert e (16-row aligned segments)
   __shared__ int scratch[4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -93,6 +98,20 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     if (e < N) base[e] = ex + bprefix[(int64_t)e * nb + b];
   }
   if (!inv) return;
+  {
+    // P(e) = sum over e_lo <= e' < e of counts[e'] rounded up to 16
+    const int e = threadIdx.x;
+    const int v = (e >= e_lo && e < e_hi) ? (counts[e] + kSegAlign - 1) / kSegAlign * kSegAlign : 0;
+    int tot;
+    const int ex = block_exclusive_scan(v, scratch, &tot);
+    if (e < N) pbase[e] = ex;
+    if (e == 0) pbase[N] = tot;
+    // padding rows of a segment: perm = -1 (expert e handled by block e % nb)
+    if (e >= e_lo && e < e_hi && (int64_t)(e % nb) == b) {
+      for (int r = ex + counts[e]; r < ex + v; ++r)
+        if ((int64_t)r < rows_cap) perm[r] = -1;
+    }
+  }
   // stage this block's expert ids; per-wave histograms
   for (int i = threadIdx.x; i < 4 * N; i += 256) hist[i] = 0;
   for (int i = threadIdx.x; i < kTB * K; i += 256) {
@@ -151,8 +170,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
   }
   __syncthreads();
 
-  // inv / perm, then the row copies (wave w copies its 64 tokens)
-  const int off_lo = offs[e_lo];
+  // inv / perm: dense row (offsets numbering) -> local row of the padded segment
   for (int i = threadIdx.x; i < kTB * K; i += 256) {
     const int tl = i / K, s = i - tl * K;
     const int64_t t = t0 + tl;
@@ -160,7 +178,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int e = keys[tl * KS + s];
     int r = -1;
     if (e >= e_lo && e < e_hi) {
-      r = rows[tl * KS + s] - off_lo;
+      r = rows[tl * KS + s] - offs[e] + pbase[e];
       if ((int64_t)r >= rows_cap || r < 0) r = -1;
     }
     rows[tl * KS + s] = r;
@@ -169,34 +187,43 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
   }
 }
 
-// Row gather: one wave per token reads x[t] once and writes it to every row
-// that inv gives the token (16-byte chunks, 8 in flight per lane).
-__global__ __launch_bounds__(256) void dispatch_copy_kernel(int64_t T, int K, const char* __restrict__ x,
-                                                            int64_t row_bytes, int64_t rows_cap,
+// Row gather: one wave per token reads x[t] once (16-byte chunks, 8 in flight per
+// lane) and writes it to every row that inv gives the token, in the tiled layout
+// (a 16-byte chunk never straddles a tile; padding columns are written as zeros),
+// and to row t of the token-order tiled copy when one is requested.
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(int64_t T, int K, const char* __restrict__ x, int esz,
+                                                            int64_t d, int64_t rows_cap,
                                                             const int32_t* __restrict__ inv,
-                                                            char* __restrict__ x_perm) {
+                                                            char* __restrict__ x_perm, char* __restrict__ x_tiled) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
-  const int64_t nch = row_bytes >> 4;
+  const int64_t nch = (d * esz) >> 4;       // 16-byte chunks of a source row
+  const int64_t dp = round_up(d, kTileCols);
+  const int64_t ncp = (dp * esz) >> 4;      // chunks of a padded row
+  const int epc = 16 / esz;                 // elements per chunk
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
   for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + t * row_bytes);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + t * d * esz);
     const int32_t* rr = inv + t * K;
-    for (int64_t c0 = 0; c0 < nch; c0 += 64 * 8) {
+    for (int64_t c0 = 0; c0 < ncp; c0 += 64 * 8) {
       u32x4_t v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int64_t c = c0 + u * 64 + lane;
-        if (c < nch) v[u] = src[c];
+        v[u] = c < nch ? src[c] : zero;
       }
-      for (int s = 0; s < K; ++s) {
-        const int r = rr[s];
-        if (r < 0 || (int64_t)r >= rows_cap) continue;
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(x_perm + (int64_t)r * row_bytes);
+      auto put = [&](char* base, int64_t r) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int64_t c = c0 + u * 64 + lane;
-          if (c < nch) dst[c] = v[u];
+          if (c < ncp) *reinterpret_cast<u32x4_t*>(base + tiled_index(r, c * epc, dp) * esz) = v[u];
         }
+      };
+      if (x_tiled) put(x_tiled, t);
+      for (int s = 0; s < K; ++s) {
+        const int r = rr[s];
+        if (r < 0 || (int64_t)r >= rows_cap) continue;
+        put(x_perm, r);
       }
     }
   }
@@ -208,8 +235,8 @@ using namespace moge;
 
 extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
                                        int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts,
-                                       int32_t* offsets, int32_t* inv, int32_t* perm, void* x_perm, void* ws,
-                                       size_t ws_bytes, hipStream_t stream) {
+                                       int32_t* offsets, int32_t* inv, int32_t* perm, void* x_perm, void* x_tiled,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
   moge_status_t st = validate_shape(shape);
   if (st != MOGE_OK) return st;
   const moge_shape_t& s = *shape;
@@ -218,6 +245,7 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   if ((x == nullptr) != (x_perm == nullptr)) return fail(MOGE_ERR_NULL, "x and x_perm must be given together");
   if ((inv == nullptr) != (perm == nullptr)) return fail(MOGE_ERR_NULL, "inv and perm must be given together");
   if (x && !inv) return fail(MOGE_ERR_NULL, "row copies need inv and perm");
+  if (x_tiled && !x) return fail(MOGE_ERR_NULL, "x_tiled needs x");
   if (e_lo < 0 || e_hi > s.N || e_lo >= e_hi) return fail(MOGE_ERR_ARG, "need 0 <= e_lo < e_hi <= N");
   const int K = s.M * s.k_per_group;
   if (K > 64) return fail(MOGE_ERR_SHAPE, "dispatch supports K = M*k_per_group <= 64");
@@ -230,7 +258,7 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   const int64_t nb = dispatch_blocks(s.T);
   int32_t* bcount = static_cast<int32_t*>(ws);
   int32_t* bprefix = bcount + (int64_t)s.N * nb;
-  const int64_t row_bytes = (int64_t)s.d * (s.dtype == MOGE_BF16 ? 2 : 4);
+  const int esz = s.dtype == MOGE_BF16 ? 2 : 4;
 
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nb), dim3(256), 0, stream, (int64_t)s.T, K, s.N, nb, idx,
                      bcount);
@@ -238,7 +266,8 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3((unsigned)s.N), dim3(256), 0, stream, nb, bcount, bprefix, counts);
   if ((st = check_launch("dispatch_scan_kernel")) != MOGE_OK) return st;
 
-  const size_t lds = sizeof(int) * ((size_t)2 * kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + 4 * (size_t)s.N);
+  const size_t lds =
+      sizeof(int) * ((size_t)2 * kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + 4 * (size_t)s.N + (size_t)(s.N + 1));
   if (lds > 64 * 1024) {
     st = raise_dynamic_lds(reinterpret_cast<const void*>(dispatch_permute_kernel), lds, "dispatch_permute_kernel");
     if (st != MOGE_OK) return st;
@@ -250,7 +279,8 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
     int64_t grid = ((int64_t)s.T + 3) / 4;
     if (grid > 16384) grid = 16384;
     hipLaunchKernelGGL(dispatch_copy_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (int64_t)s.T, K,
-                       static_cast<const char*>(x), row_bytes, rows_cap, inv, static_cast<char*>(x_perm));
+                       static_cast<const char*>(x), esz, (int64_t)s.d, rows_cap, inv, static_cast<char*>(x_perm),
+                       static_cast<char*>(x_tiled));
     st = check_launch("dispatch_copy_kernel");
   }
   return st == MOGE_OK ? ok() : st;

@@ -12,6 +12,13 @@
 //     workgroup (two waves per SIMD) owns a 320-row x 256-weight-row tile (GEMM 1:
 //     128 gate + 128 up rows of the same 128 h columns, so the SwiGLU is fused into
 //     the epilogue; GEMM 2: 256 output columns), each wave a 160 x 64 part of it;
+//   * both operands are in the tiled layout (16 x 32 tiles of 1 KiB, see moge.h):
+//     the token rows as written by dispatch and the weights as packed once at
+//     load time, so every load instruction moves one contiguous 1 KiB tile
+//     (one burst per 16 rows, one address-translation page per instruction)
+//     instead of 16 half cache lines of 16 long rows; this alone took about a
+//     third off the load time.  K is padded with zeros to a multiple of 32, so
+//     there is no ragged reduction step;
 //   * both panels go straight from global memory to a 4-stage LDS ring
 //     (global_load_lds_dwordx4, BK = 32), so every load has about two steps of
 //     MFMA work to arrive and no registers stage it; 64-byte LDS rows with an
@@ -27,8 +34,10 @@
 //     XCD b % 8), so that sharing happens in that XCD's L2;
 //   * the weight fragment is the MFMA's first operand, so each lane ends with 4
 //     consecutive output columns of one token row: the epilogue (SwiGLU for
-//     GEMM 1) packs them into 8-byte stores straight to HBM.
-// float32 shapes use a plain vector-ALU kernel pair (small shapes only).
+//     GEMM 1, into the tiled h; GEMM 2 into the row-major expert output) packs
+//     them into 8-byte stores straight to HBM.
+// float32 shapes use a plain vector-ALU kernel pair on the same layouts (small
+// shapes only).
 #include <math.h>
 
 #include "moge_internal.hpp"
@@ -74,31 +83,35 @@ constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) <<
 // to land.  Two waves per SIMD keep the MFMA pipe fed across the barriers and give
 // the LDS enough concurrent readers to reach its full rate.
 template <bool SWIGLU, int NL>
-__device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint16_t* __restrict__ abase,
+__device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint16_t* __restrict__ A, int64_t mband0,
                                              const uint16_t* __restrict__ wbase0, const uint16_t* __restrict__ wbase1,
-                                             int KD, int mrows, int n0, int NOUT, uint16_t* __restrict__ cbase) {
+                                             int wbands, int nkf, int mrows, int64_t row0, int n0, int NOUT, int NPAD,
+                                             uint16_t* __restrict__ C) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
   const int wm = wave & 1, wn = wave >> 1;
-  const int nkf = KD / kBK;  // full steps; a ragged tail is one extra step below
-  // DMA sources: instruction j < 4 moves 16 stage rows at ldsrow[j] .. +16; waves 4-7
-  // have a fifth instruction (token rows 256.. of the tile).
+  // DMA sources: instruction j < 4 moves the 16 stage rows at lrow[j] .. +16 (one
+  // tile of 16 rows x 32 columns); waves 4-7 have a fifth instruction (token rows
+  // 256.. of the tile).  Lane l brings 16 bytes of row lrow[j] + l/4.
   const bool wtok = wave < 4;
+  const int live_bands = (mrows + kTileRows - 1) / kTileRows;
   const uint16_t* dsrc[5];
   int lrow[5];  // first stage row of each instruction (wave-uniform)
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     lrow[j] = wtok ? wave * 64 + j * 16 : (j < 4 ? kBM + (wave - 4) * 64 + j * 16 : 256 + (wave - 4) * 16);
     const int srow = lrow[j] + (lane >> 2);  // stage row (token rows 0..319, weight rows 320..575)
-    const int c = (lane & 3) ^ swz(srow);    // global chunk fetched by this lane
-    if (srow < kBM) {
-      const int rr = srow < mrows ? srow : mrows - 1;
-      dsrc[j] = abase + (int64_t)rr * KD + c * 8;
+    const int c = (lane & 3) ^ swz(srow);    // 16-byte chunk of the 32-column tile row fetched by this lane
+    const int inner = (lane >> 2) * kTileCols + c * 8;
+    if (lrow[j] < kBM) {
+      int band = lrow[j] / kTileRows;  // bands past the live rows re-read the last live band (never stored)
+      if (band >= live_bands) band = live_bands - 1;
+      dsrc[j] = A + (mband0 + band) * nkf * kTileElems + inner;
     } else {
-      const int r = srow - kBM;
-      int wr = SWIGLU ? n0 + (r & 127) : n0 + r;
-      if (wr > NOUT - 1) wr = NOUT - 1;
-      dsrc[j] = (SWIGLU && r >= 128 ? wbase1 : wbase0) + (int64_t)wr * KD + c * 8;
+      const int r = lrow[j] - kBM;
+      int band = (SWIGLU ? n0 + (r & 127) : n0 + r) / kTileRows;
+      if (band >= wbands) band = wbands - 1;
+      dsrc[j] = (SWIGLU && r >= 128 ? wbase1 : wbase0) + (int64_t)band * nkf * kTileElems + inner;
     }
   }
   // Step ks into stage ks % 4 (steps past the last full step reload step 0).  The
@@ -108,7 +121,7 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
   // instruction has no register result, only an address operand read at issue.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   auto issue = [&](int ks) {
-    const int k = ks < nkf ? ks * kBK : 0;
+    const int k = ks < nkf ? ks * kTileElems : 0;
     const uint32_t st = lds0 + (uint32_t)((ks % kStages) * kStageB);
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
@@ -191,39 +204,20 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing reloads before LDS is reused
   __syncthreads();
-  if (KD % kBK) {
-    // ragged tail: one unpipelined step, chunks at or past KD are zero
-    const int k = nkf * kBK;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      if (j == 4 && wtok) break;
-      const int srow = lrow[j] + (lane >> 2);
-      const int c = (lane & 3) ^ swz(srow);
-      const u32x4_t v = (k + c * 8 < KD) ? *reinterpret_cast<const u32x4_t*>(dsrc[j] + k) : zero;
-      *reinterpret_cast<u32x4_t*>(lds + lrow[j] * kRowB + (lane << 4)) = v;
-    }
-    __syncthreads();
-    if (NL) {
-      frag(0, 0, a0, b0);
-      frag(0, 1, a1, b1);
-      mfma(a0, b0);
-      mfma(a1, b1);
-    }
-  }
-
-  // epilogue (rows of dead blocks are never stored)
+  // epilogue (rows of dead blocks are never stored).  GEMM 1 writes the tiled h
+  // (NPAD = F rounded up to 32 columns; its padding columns come out as zeros from
+  // the zero rows of the packed weights); GEMM 2 writes row-major [row][NOUT].
 #pragma unroll
   for (int t = 0; t < NL; ++t) {
-    const int row = (wm + 2 * t) * 32 + (lane & 31);
-    if (row < mrows) {
-      uint16_t* crow = cbase + (int64_t)row * NOUT;
+    const int trow = (wm + 2 * t) * 32 + (lane & 31);
+    if (trow < mrows) {
+      const int64_t row = row0 + trow;
 #pragma unroll
       for (int cb = 0; cb < (SWIGLU ? 1 : 2); ++cb) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int col = n0 + (SWIGLU ? wn * 32 : wn * 64 + cb * 32) + g4 * 8 + (lane >> 5) * 4;
-          if (col < NOUT) {
+          if (col < (SWIGLU ? NPAD : NOUT)) {
             uint16_t hv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -239,7 +233,8 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
             uint2 pk;
             pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
             pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-            *reinterpret_cast<uint2*>(crow + col) = pk;
+            uint16_t* dst = SWIGLU ? C + tiled_index(row, col, NPAD) : C + row * NOUT + col;
+            *reinterpret_cast<uint2*>(dst) = pk;
           }
         }
       }
@@ -247,47 +242,71 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
   }
 }
 
+// Per-expert rows (clipped to rows_cap) and first local rows P(e) (segments rounded
+// up to 16 rows), for experts e_lo .. e_lo+E-1, by one wave; optionally also the
+// inclusive prefix of tiles per expert (tiles of `bm` rows times nt column tiles).
+__device__ __forceinline__ void expert_segments(const int32_t* __restrict__ offsets, int e_lo, int E, int64_t rows_cap,
+                                                int bm, int nt, int* erow, int* pbase, int* tp) {
+  const int lane = threadIdx.x & 63;
+  int run_rows = 0, run_tiles = 0;
+  for (int b = 0; b < E; b += 64) {
+    const int i = b + lane;
+    int rows = 0;
+    if (i < E) {
+      rows = offsets[e_lo + i + 1] - offsets[e_lo + i];
+      if (rows < 0) rows = 0;
+    }
+    int prow = (rows + kSegAlign - 1) / kSegAlign * kSegAlign;
+    int incl = prow;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += u;
+    }
+    const int64_t p0 = (int64_t)run_rows + incl - prow;  // P(e)
+    if (p0 + rows > rows_cap) rows = rows_cap > p0 ? (int)(rows_cap - p0) : 0;
+    int tiles = ((rows + bm - 1) / bm) * nt;
+    int tincl = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(tincl, off, 64);
+      if (lane >= off) tincl += u;
+    }
+    if (i < E) {
+      erow[i] = rows;
+      pbase[i] = (int)p0;
+      if (tp) tp[i] = run_tiles + tincl;
+    }
+    run_rows += __shfl(incl, 63, 64);
+    run_tiles += __shfl(tincl, 63, 64);
+  }
+}
+
+// GEMM 1 (SWIGLU):  A = x_perm tiled [rows][KP], B0/B1 = packed gate/up [E][NOUT][KP],
+//                   C = h tiled [rows][NPAD] with NPAD = NOUT rounded up to 32.
+// GEMM 2:           A = h tiled [rows][KP], B0 = packed down [E][NOUT][KP], C = out [rows][NOUT].
+// KP = the reduction length rounded up to 32 (zero padded in A and B).
 template <bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                               const int32_t* __restrict__ offsets, int e_lo, int E,
                                                               int64_t rows_cap, const uint16_t* __restrict__ B0,
-                                                              const uint16_t* __restrict__ B1, int NOUT, int KD,
+                                                              const uint16_t* __restrict__ B1, int NOUT, int KP,
                                                               uint16_t* __restrict__ C) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int tp[kMaxExperts];    // inclusive prefix of tiles per expert
-  __shared__ int erow[kMaxExperts];  // rows per expert, clipped to [0, rows_cap)
+  __shared__ int tp[kMaxExperts];     // inclusive prefix of tiles per expert
+  __shared__ int erow[kMaxExperts];   // rows per expert, clipped to rows_cap
+  __shared__ int pbase[kMaxExperts];  // first local row of each expert (16-row aligned)
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;  // output columns per tile
   const int NT = (NOUT + BNO - 1) / BNO;
-  const int64_t wrows = NOUT;  // weight rows per expert in B0/B1
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wrows = (int)round_up(NOUT, kWeightRowAlign);  // packed weight rows per expert
+  const int wbands = wrows / kTileRows;
+  const int NPAD = (int)round_up(NOUT, kTileCols);
+  const int nkf = KP / kTileCols;
+  const int tid = threadIdx.x, wave = tid >> 6;
 
-  // per-expert tile counts -> inclusive prefix (E <= 256), by wave 0
-  if (wave == 0) {
-    int run = 0;
-    for (int b = 0; b < E; b += 64) {
-      const int i = b + lane;
-      int tiles = 0;
-      if (i < E) {
-        const int64_t seg0 = (int64_t)offsets[e_lo + i] - offsets[e_lo];
-        int64_t rows = (int64_t)offsets[e_lo + i + 1] - offsets[e_lo + i];
-        if (seg0 < 0 || rows < 0) rows = 0;
-        if (seg0 + rows > rows_cap) rows = rows_cap > seg0 ? rows_cap - seg0 : 0;
-        erow[i] = (int)rows;
-        tiles = (int)((rows + kBM - 1) / kBM) * NT;
-      }
-      int incl = tiles;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int u = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += u;
-      }
-      if (i < E) tp[i] = run + incl;
-      run += __shfl(incl, 63, 64);
-    }
-  }
+  if (wave == 0) expert_segments(offsets, e_lo, E, rows_cap, kBM, NT, erow, pbase, tp);
   __syncthreads();
   const int total = E > 0 ? tp[E - 1] : 0;
-  const int base0 = offsets[e_lo];
 
   const int P = gridDim.x;  // multiple of 8
   const int per_xcd = P >> 3;
@@ -302,7 +321,6 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const uint16_t* __
     }
     const int ei = lo;
     const int q = tile - (ei > 0 ? tp[ei - 1] : 0);
-    const int seg0 = offsets[e_lo + ei] - base0;
     const int erows = erow[ei];
     const int MT = (erows + kBM - 1) / kBM;
     // grouped order: groups of kGroupM m-tiles; inside a group n outer, m inner
@@ -311,75 +329,87 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const uint16_t* __
     const int gm0 = g * kGroupM;
     const int gm = (MT - gm0) < kGroupM ? (MT - gm0) : kGroupM;
     const int mt = gm0 + qi % gm, nt = qi / gm;
-    const int m0 = seg0 + mt * kBM;
+    const int64_t row0 = (int64_t)pbase[ei] + (int64_t)mt * kBM;  // multiple of 16
     const int mrows = (erows - mt * kBM) < kBM ? (erows - mt * kBM) : kBM;
     const int n0 = nt * BNO;
-    const uint16_t* abase = A + (int64_t)m0 * KD;
-    const uint16_t* wb0 = B0 + (int64_t)ei * wrows * KD;
-    const uint16_t* wb1 = SWIGLU ? B1 + (int64_t)ei * wrows * KD : wb0;
-    uint16_t* cbase = C + (int64_t)m0 * NOUT;
+    const uint16_t* wb0 = B0 + (int64_t)ei * wrows * KP;
+    const uint16_t* wb1 = SWIGLU ? B1 + (int64_t)ei * wrows * KP : wb0;
+    const int64_t mband0 = row0 / kTileRows;
 
     // live row blocks of this wave (wave-uniform): block wm + 2t is live if it starts below mrows
     const int wm = wave & 1;
     const int nrb = (mrows + 31) / 32;
     const int nl = nrb > wm ? (nrb - wm + 1) / 2 : 0;
+#define MOGE_TILE(NLV) tile_compute<SWIGLU, NLV>(lds, A, mband0, wb0, wb1, wbands, nkf, mrows, row0, n0, NOUT, NPAD, C)
     switch (nl) {
-      case 5: tile_compute<SWIGLU, 5>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
-      case 4: tile_compute<SWIGLU, 4>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
-      case 3: tile_compute<SWIGLU, 3>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
-      case 2: tile_compute<SWIGLU, 2>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
-      case 1: tile_compute<SWIGLU, 1>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
-      default: tile_compute<SWIGLU, 0>(lds, abase, wb0, wb1, KD, mrows, n0, NOUT, cbase); break;
+      case 5: MOGE_TILE(5); break;
+      case 4: MOGE_TILE(4); break;
+      case 3: MOGE_TILE(3); break;
+      case 2: MOGE_TILE(2); break;
+      case 1: MOGE_TILE(1); break;
+      default: MOGE_TILE(0); break;
     }
+#undef MOGE_TILE
     __syncthreads();  // LDS stages are reused by the next tile
   }
 }
 
 // ----------------------------------------------------------------------------
-// float32 vector-ALU pair (small shapes): one thread per output element.
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int e_lo, int e_hi, int grow) {
-  int lo = e_lo, hi = e_hi - 1;  // last e with offsets[e] <= grow
+// float32 vector-ALU pair (small shapes): one thread per output element, same
+// layouts as the bf16 kernels (tiled x_perm and h, packed weights, row-major out).
+// Each workgroup first derives the experts' segments.
+__device__ __forceinline__ int segment_of_row(const int* __restrict__ pbase, int E, int64_t r) {
+  int lo = 0, hi = E - 1;  // last i with pbase[i] <= r
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (offsets[mid] <= grow) lo = mid; else hi = mid - 1;
+    if (pbase[mid] <= r) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
 
 __global__ __launch_bounds__(256) void ffn_f32_gateup_kernel(const float* __restrict__ X, const int32_t* __restrict__ offsets,
-                                                             int e_lo, int e_hi, int64_t rows_cap, const float* __restrict__ Wg,
+                                                             int e_lo, int E, int64_t rows_cap, const float* __restrict__ Wg,
                                                              const float* __restrict__ Wu, int d, int F, float* __restrict__ H) {
-  const int64_t live = offsets[e_hi] - offsets[e_lo];
-  const int64_t n = (live < rows_cap ? live : rows_cap) * F;
+  __shared__ int erow[kMaxExperts], pbase[kMaxExperts];
+  if (threadIdx.x < 64) expert_segments(offsets, e_lo, E, rows_cap, 1, 1, erow, pbase, nullptr);
+  __syncthreads();
+  const int64_t dp = round_up(d, kTileCols), fp = round_up(F, kTileCols), wr = round_up(F, kWeightRowAlign);
+  const int64_t rows = (int64_t)pbase[E - 1] + erow[E - 1];
+  const int64_t n = rows * fp;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / F;
-    const int f = (int)(i - r * F);
-    const int e = expert_of_row(offsets, e_lo, e_hi, (int)(r + offsets[e_lo]));
-    const float* xr = X + r * d;
-    const float* wg = Wg + ((int64_t)(e - e_lo) * F + f) * d;
-    const float* wu = Wu + ((int64_t)(e - e_lo) * F + f) * d;
+    const int64_t r = i / fp;
+    const int f = (int)(i - r * fp);
+    const int e = segment_of_row(pbase, E, r);
+    if (r - pbase[e] >= erow[e]) continue;  // padding row
+    const float* wg = Wg + (int64_t)e * wr * dp;
+    const float* wu = Wu + (int64_t)e * wr * dp;
     float a = 0.f, b = 0.f;
     for (int c = 0; c < d; ++c) {
-      a = fmaf(xr[c], wg[c], a);
-      b = fmaf(xr[c], wu[c], b);
+      const float xv = X[tiled_index(r, c, dp)];
+      a = fmaf(xv, wg[tiled_index(f, c, dp)], a);
+      b = fmaf(xv, wu[tiled_index(f, c, dp)], b);
     }
-    H[r * F + f] = a / (1.f + expf(-a)) * b;
+    H[tiled_index(r, f, fp)] = a / (1.f + expf(-a)) * b;
   }
 }
 
 __global__ __launch_bounds__(256) void ffn_f32_down_kernel(const float* __restrict__ H, const int32_t* __restrict__ offsets,
-                                                           int e_lo, int e_hi, int64_t rows_cap, const float* __restrict__ Wd,
+                                                           int e_lo, int E, int64_t rows_cap, const float* __restrict__ Wd,
                                                            int d, int F, float* __restrict__ O) {
-  const int64_t live = offsets[e_hi] - offsets[e_lo];
-  const int64_t n = (live < rows_cap ? live : rows_cap) * d;
+  __shared__ int erow[kMaxExperts], pbase[kMaxExperts];
+  if (threadIdx.x < 64) expert_segments(offsets, e_lo, E, rows_cap, 1, 1, erow, pbase, nullptr);
+  __syncthreads();
+  const int64_t fp = round_up(F, kTileCols), wr = round_up(d, kWeightRowAlign);
+  const int64_t rows = (int64_t)pbase[E - 1] + erow[E - 1];
+  const int64_t n = rows * d;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = i / d;
     const int j = (int)(i - r * d);
-    const int e = expert_of_row(offsets, e_lo, e_hi, (int)(r + offsets[e_lo]));
-    const float* hr = H + r * F;
-    const float* wd = Wd + ((int64_t)(e - e_lo) * d + j) * F;
+    const int e = segment_of_row(pbase, E, r);
+    if (r - pbase[e] >= erow[e]) continue;  // padding row
+    const float* wd = Wd + (int64_t)e * wr * fp;
     float acc = 0.f;
-    for (int f = 0; f < F; ++f) acc = fmaf(hr[f], wd[f], acc);
+    for (int f = 0; f < F; ++f) acc = fmaf(H[tiled_index(r, f, fp)], wd[tiled_index(j, f, fp)], acc);
     O[r * d + j] = acc;
   }
 }
@@ -388,8 +418,9 @@ static int device_cus() {
   static int cus = 0;
   if (!cus) {
     int dev = 0;
-    hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
   }
   return cus;
 }
@@ -408,7 +439,7 @@ static moge_status_t launch_ggemm(const uint16_t* A, const int32_t* offsets, int
   if (upper < grid) grid = upper;
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL(ggemm_bf16_kernel<SWIGLU>, dim3((unsigned)grid), dim3(kThreads), kGemmLds, stream, A, offsets, e_lo,
-                     E, rows_cap, B0, B1, NOUT, KD, C);
+                     E, rows_cap, B0, B1, NOUT, (int)round_up(KD, kTileCols), C);
   return check_launch(SWIGLU ? "ggemm_bf16_kernel<gate_up>" : "ggemm_bf16_kernel<down>");
 }
 
@@ -422,6 +453,7 @@ static moge_status_t ffn_common_checks(const moge_shape_t* shape, int32_t e_lo, 
   if (shape->F <= 0) return fail(MOGE_ERR_SHAPE, "the expert FFN needs F > 0");
   if (e_lo < 0 || e_hi > shape->N || e_lo >= e_hi) return fail(MOGE_ERR_ARG, "need 0 <= e_lo < e_hi <= N");
   if (rows_cap < 1) return fail(MOGE_ERR_CAPACITY, "rows_cap must be >= 1");
+  if (rows_cap >= (int64_t(1) << 31) - kBM) return fail(MOGE_ERR_CAPACITY, "rows_cap must be < 2^31 - 320");
   return MOGE_OK;
 }
 
@@ -443,8 +475,8 @@ extern "C" moge_status_t moge_expert_gate_up(const moge_shape_t* shape, const vo
                             static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), s.F, s.d,
                             static_cast<uint16_t*>(h), stream);
   } else {
-    hipLaunchKernelGGL(ffn_f32_gateup_kernel, dim3((unsigned)grid_1d(rows_cap * s.F)), dim3(256), 0, stream,
-                       static_cast<const float*>(x_perm), offsets, e_lo, e_hi, rows_cap,
+    hipLaunchKernelGGL(ffn_f32_gateup_kernel, dim3((unsigned)grid_1d(rows_cap * round_up(s.F, kTileCols))), dim3(256),
+                       0, stream, static_cast<const float*>(x_perm), offsets, e_lo, e_hi - e_lo, rows_cap,
                        static_cast<const float*>(w_gate), static_cast<const float*>(w_up), s.d, s.F,
                        static_cast<float*>(h));
     st = check_launch("ffn_f32_gateup_kernel");
@@ -465,8 +497,8 @@ extern "C" moge_status_t moge_expert_down(const moge_shape_t* shape, const void*
                              stream);
   } else {
     hipLaunchKernelGGL(ffn_f32_down_kernel, dim3((unsigned)grid_1d(rows_cap * s.d)), dim3(256), 0, stream,
-                       static_cast<const float*>(h), offsets, e_lo, e_hi, rows_cap, static_cast<const float*>(w_down),
-                       s.d, s.F, static_cast<float*>(out));
+                       static_cast<const float*>(h), offsets, e_lo, e_hi - e_lo, rows_cap,
+                       static_cast<const float*>(w_down), s.d, s.F, static_cast<float*>(out));
     st = check_launch("ffn_f32_down_kernel");
   }
   return st == MOGE_OK ? ok() : st;

@@ -62,9 +62,10 @@ moge_status_t raise_dynamic_lds(const void* kernel, size_t bytes, const char* wh
 int64_t rows_bound(const moge_shape_t& s, int32_t mode, int32_t e_lo, int32_t e_hi) {
   const int64_t G = s.N / s.M;
   const int64_t K = (int64_t)s.M * s.k_per_group;
+  const int64_t pad = (int64_t)(kSegAlign - 1) * (e_hi - e_lo);  // each segment starts on a 16-row boundary
   if (mode == MOGE_ROUTE_GLOBAL) {
     const int64_t span = e_hi - e_lo;
-    return (int64_t)s.T * (span < K ? span : K);
+    return (int64_t)s.T * (span < K ? span : K) + pad;
   }
   int64_t per_token = 0;
   for (int64_t g = 0; g < s.M; ++g) {
@@ -72,7 +73,7 @@ int64_t rows_bound(const moge_shape_t& s, int32_t mode, int32_t e_lo, int32_t e_
     const int64_t hi = e_hi < (g + 1) * G ? e_hi : (g + 1) * G;
     if (hi > lo) per_token += (hi - lo) < s.k_per_group ? (hi - lo) : s.k_per_group;
   }
-  return (int64_t)s.T * per_token;
+  return (int64_t)s.T * per_token + pad;
 }
 
 }  // namespace moge
@@ -89,6 +90,16 @@ extern "C" int64_t moge_rows_bound(const moge_shape_t* shape, int32_t mode, int3
   if (mode != MOGE_ROUTE_GROUPED && mode != MOGE_ROUTE_GLOBAL) return -1;
   if (e_lo < 0 || e_hi > shape->N || e_lo >= e_hi) return -1;
   return rows_bound(*shape, mode, e_lo, e_hi);
+}
+
+extern "C" int64_t moge_tiled_elems(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return -1;
+  return round_up(rows, kTileRows) * round_up(cols, kTileCols);
+}
+
+extern "C" int64_t moge_packed_weight_elems(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return -1;
+  return round_up(rows, kWeightRowAlign) * round_up(cols, kTileCols);
 }
 
 extern "C" size_t moge_workspace_size(const moge_shape_t* shape, int32_t stage) {

@@ -23,6 +23,19 @@ moge_status_t raise_dynamic_lds(const void* kernel, size_t bytes, const char* wh
 
 constexpr int kMaxExperts = 256;
 
+// Tiled operand layout: tiles of 16 rows x 32 columns (512 elements), tiles of a
+// 16-row band consecutive; element (r, c) of a matrix with cp (a multiple of 32)
+// padded columns is at tiled_index(r, c, cp).
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 32;
+constexpr int kTileElems = kTileRows * kTileCols;
+constexpr int kSegAlign = 16;        // expert row segments start on a 16-row boundary
+constexpr int kWeightRowAlign = 32;  // packed weights: rows padded with zeros to a multiple of 32
+__host__ __device__ __forceinline__ int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+__host__ __device__ __forceinline__ int64_t tiled_index(int64_t r, int64_t c, int64_t cp) {
+  return ((r >> 4) * (cp >> 5) + (c >> 5)) * kTileElems + (r & 15) * kTileCols + (c & 31);
+}
+
 // Dispatch geometry (shared by moge_workspace_size and the dispatch kernels).
 constexpr int kDispatchTokens = 256;  // tokens per dispatch workgroup
 inline int64_t dispatch_blocks(int64_t T) { return (T + kDispatchTokens - 1) / kDispatchTokens; }

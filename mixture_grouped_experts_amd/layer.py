@@ -5,6 +5,7 @@ reportify.cn for the shared expert):
 
   1. moge_route GROUPED   scores (stored), softmax over all N, top-K' in every group
   2. moge_dispatch        counts, offsets, stable permutation, rows of [e_lo, e_hi)
+                          (tiled), and the tiled copy of x for the shared expert
   3. moge_grouped_ffn     SwiGLU experts on their row segments
   4. moge_grouped_ffn     the always-on shared expert (one-expert shape), if any
   5. moge_combine         gate-weighted sum (+ shared output) -> y (float32)
@@ -13,7 +14,8 @@ reportify.cn for the shared expert):
      moge_dispatch        its counts only, and moge_imbalance of that load.
 
 Buffers are allocated once here (torch supplies device memory); ``forward`` only issues
-library calls, so it allocates nothing and does not synchronise.
+library calls, so it allocates nothing and does not synchronise.  Expert weights are
+passed packed (``pack_expert_weights``, once, when they are loaded).
 """
 from __future__ import annotations
 
@@ -63,18 +65,32 @@ class MoGELayer:
             R = self.rows_cap
             self.inv = torch.empty(T, K, **i32)
             self.perm = torch.empty(R, **i32)
-            self.x_perm = torch.empty(R, d, dtype=self.tdtype, device=dev)
-            self.h = torch.empty(R, F, dtype=self.tdtype, device=dev)
+            self.x_perm = torch.empty(L.tiled_elems(R, d), dtype=self.tdtype, device=dev)
+            self.h = torch.empty(L.tiled_elems(R, F), dtype=self.tdtype, device=dev)
             self.o = torch.empty(R, d, dtype=self.tdtype, device=dev)
             self.y = torch.empty(T, d, **f32)
         if F_shared:
             self.sshape = L.Shape(T, d, 1, 1, 1, F_shared, self.dtype_code)
             self.soffsets = torch.tensor([0, T], **i32)
-            self.sh = torch.empty(T, F_shared, dtype=self.tdtype, device=dev)
+            self.x_tiled = torch.empty(L.tiled_elems(T, d), dtype=self.tdtype, device=dev)
+            self.sh = torch.empty(L.tiled_elems(T, F_shared), dtype=self.tdtype, device=dev)
             self.so = torch.empty(T, d, dtype=self.tdtype, device=dev)
+
+    def pack_expert_weights(self, w_gate, w_up, w_down, shared=None, stream=None):
+        """Row-major expert weights ([E][F][d], [E][F][d], [E][d][F]; shared: three 2-d matrices)
+        -> packed tensors for ``forward``.  Done once, when the weights are loaded."""
+        def pack(w):
+            w3 = w if w.dim() == 3 else w.unsqueeze(0)
+            out = torch.empty(w3.shape[0] * L.packed_weight_elems(w3.shape[1], w3.shape[2]), dtype=w.dtype,
+                              device=w.device)
+            L.pack_weights(self.dtype_code, w3, out, stream)
+            return out
+        packed = (pack(w_gate), pack(w_up), pack(w_down))
+        return packed, (tuple(pack(m) for m in shared) if shared is not None else None)
 
     def forward(self, x, w_router, bias, w_gate=None, w_up=None, w_down=None, shared=None, stream=None, mark=None):
         """Enqueues the layer on `stream` (default: current).  Returns y (None for routing only).
+        w_gate, w_up, w_down and the shared expert's three matrices are packed weights.
 
         `mark(name)`, if given, is called right after each library call is enqueued (a timing hook:
         the caller may record a stream event there)."""
@@ -84,11 +100,12 @@ class MoGELayer:
         mk("route")
         if self.routing_only:
             L.dispatch(s, L.ROUTE_GROUPED, self.idx, None, 0, self.N, 0, self.counts, self.offsets, None, None, None,
-                       self.ws, stream)
+                       self.ws, stream=stream)
             mk("dispatch")
         else:
             L.dispatch(s, L.ROUTE_GROUPED, self.idx, x, self.e_lo, self.e_hi, self.rows_cap, self.counts,
-                       self.offsets, self.inv, self.perm, self.x_perm, self.ws, stream)
+                       self.offsets, self.inv, self.perm, self.x_perm, self.ws,
+                       self.x_tiled if self.F_shared else None, stream)
             mk("dispatch")
             L.expert_gate_up(s, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate, w_up, self.h,
                              stream)
@@ -96,8 +113,8 @@ class MoGELayer:
             L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o, stream)
             mk("down")
             if self.F_shared:
-                L.grouped_ffn(self.sshape, x, self.soffsets, 0, 1, self.T, shared[0], shared[1], shared[2], self.sh,
-                              self.so, stream)
+                L.grouped_ffn(self.sshape, self.x_tiled, self.soffsets, 0, 1, self.T, shared[0], shared[1],
+                              shared[2], self.sh, self.so, stream)
                 mk("shared")
             L.combine(s, self.o, self.inv, self.gate, self.rows_cap, self.so if self.F_shared else None, self.y,
                       stream)
@@ -107,7 +124,7 @@ class MoGELayer:
         if self.comparator:
             L.route(s, L.ROUTE_GLOBAL, None, None, None, self.logits, self.gidx, self.ggate, stream)
             L.dispatch(s, L.ROUTE_GLOBAL, self.gidx, None, 0, self.N, 0, self.gcounts, self.goffsets, None, None,
-                       None, self.ws, stream)
+                       None, self.ws, stream=stream)
             L.imbalance(s, self.gcounts, self.g_group_load, self.g_is_raw, self.g_is_norm, stream)
             mk("global_comparator")
         return None if self.routing_only else self.y

@@ -26,6 +26,57 @@ def tol_ok(gpu: np.ndarray, ref: np.ndarray):
     return err <= bound, err, bound
 
 
+# ---- the tiled operand layout and padded row numbering of include/moge.h, restated here
+# from that header's definition (test side; the library is not consulted)
+
+def _up(v: int, a: int) -> int:
+    return -(-v // a) * a
+
+
+def tile_rows(a: torch.Tensor, row_align: int = 16) -> torch.Tensor:
+    """[R][C] row-major -> flat tiled layout: 16 x 32 tiles, rows padded to row_align, cols to 32 (zeros)."""
+    R, C = a.shape
+    Rp, Cp = _up(R, row_align), _up(C, 32)
+    p = torch.zeros(Rp, Cp, dtype=a.dtype, device=a.device)
+    p[:R, :C] = a
+    return p.reshape(Rp // 16, 16, Cp // 32, 32).permute(0, 2, 1, 3).contiguous().reshape(-1)
+
+
+def untile_rows(flat: torch.Tensor, R: int, C: int, keep_pad_cols: bool = False) -> torch.Tensor:
+    """Inverse of tile_rows for the first R rows (all Cp columns if keep_pad_cols)."""
+    Rp, Cp = _up(R, 16), _up(C, 32)
+    a = flat[:Rp * Cp].reshape(Rp // 16, Cp // 32, 16, 32).permute(0, 2, 1, 3).reshape(Rp, Cp)
+    return a[:R] if keep_pad_cols else a[:R, :C]
+
+
+def pack_ref(w: torch.Tensor) -> torch.Tensor:
+    """Packed expert weights [E][rows][cols] -> E tiled matrices, rows and cols padded to 32."""
+    return torch.cat([tile_rows(w[e], 32) for e in range(w.shape[0])])
+
+
+def segment_bases(counts: np.ndarray, e_lo: int, e_hi: int) -> np.ndarray:
+    """P(e) for e in [e_lo, e_hi] (index e - e_lo): segments rounded up to 16 rows."""
+    c = np.asarray(counts, dtype=np.int64)[e_lo:e_hi]
+    return np.concatenate([[0], np.cumsum(-(-c // 16) * 16)])
+
+
+def padded_rows(idx: np.ndarray, rinv: np.ndarray, rperm: np.ndarray, counts: np.ndarray, offsets: np.ndarray,
+                e_lo: int, e_hi: int):
+    """The oracle's dense local rows -> the padded numbering: (inv, perm) with perm -1 on padding rows."""
+    P = segment_bases(counts, e_lo, e_hi)
+    inv = rinv.astype(np.int64).copy()
+    live = rinv >= 0
+    e = idx[live].astype(np.int64)
+    inv[live] = rinv[live] - (offsets[e] - offsets[e_lo]) + P[e - e_lo]
+    perm = np.full(int(P[-1]), -1, dtype=np.int64)
+    for k in range(e_hi - e_lo):
+        ee = e_lo + k
+        n = int(counts[ee])
+        d0 = int(offsets[ee] - offsets[e_lo])
+        perm[P[k]:P[k] + n] = rperm[d0:d0 + n]
+    return inv.astype(np.int32), perm.astype(np.int32)
+
+
 @dataclasses.dataclass
 class DeviceInputs:
     x: torch.Tensor

@@ -48,16 +48,38 @@ def test_validate(shape, code):
 
 def test_rows_bound_and_workspace():
     s = S(T=100, N=64, M=8, Kp=2)
-    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 64) == 100 * 16
-    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 8) == 100 * 2        # one group
-    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 7, 9) == 100 * 2        # one expert in each of two groups
-    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 1) == 100
-    assert moge.rows_bound(s, moge.ROUTE_GLOBAL, 0, 8) == 100 * 8
-    assert moge.rows_bound(s, moge.ROUTE_GLOBAL, 0, 64) == 100 * 16
+    # assignment bound + 15 padding rows per expert of the range (segments start on 16-row boundaries)
+    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 64) == 100 * 16 + 15 * 64
+    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 8) == 100 * 2 + 15 * 8       # one group
+    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 7, 9) == 100 * 2 + 15 * 2       # one expert in each of two groups
+    assert moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 1) == 100 + 15
+    assert moge.rows_bound(s, moge.ROUTE_GLOBAL, 0, 8) == 100 * 8 + 15 * 8
+    assert moge.rows_bound(s, moge.ROUTE_GLOBAL, 0, 64) == 100 * 16 + 15 * 64
     assert moge.rows_bound(s, 5, 0, 8) == -1 and moge.rows_bound(s, 0, 8, 8) == -1
     assert moge.workspace_size(S(T=65536, N=64)) == 2 * 64 * 256 * 4
     assert moge.workspace_size(S(T=1, N=8)) == 2 * 8 * 1 * 4
     assert moge.workspace_size(S(T=0)) == 2 ** 64 - 1
+
+
+def test_tiled_sizes():
+    # tiles of 16 rows x 32 columns; packed weights pad rows to 32
+    assert moge.tiled_elems(1, 8) == 16 * 32
+    assert moge.tiled_elems(16, 32) == 512 and moge.tiled_elems(17, 33) == 32 * 64
+    assert moge.tiled_elems(65536 + 15 * 256, 7680) == (65536 + 15 * 256) * 7680
+    assert moge.packed_weight_elems(200, 256) == 224 * 256 and moge.packed_weight_elems(2048, 7680) == 2048 * 7680
+    assert moge.tiled_elems(-1, 8) == -1 and moge.packed_weight_elems(4, -1) == -1
+
+
+def test_pack_weights_argument_errors():
+    lib = ctypes.CDLL(moge.LIB_PATH)
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: every case fails host validation first
+    lib.moge_pack_weights.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
+    assert lib.moge_pack_weights(9, 1, 8, 8, fake, fake, None) == 5
+    assert lib.moge_pack_weights(0, 0, 8, 8, fake, fake, None) == 2
+    assert lib.moge_pack_weights(0, 1, 8, 12, fake, fake, None) == 2
+    assert lib.moge_pack_weights(0, 1, 0, 8, fake, fake, None) == 2
+    assert lib.moge_pack_weights(0, 1, 8, 8, None, fake, None) == 3
 
 
 def _call(fn, *args):
@@ -78,22 +100,26 @@ def test_null_and_argument_errors_before_any_launch():
     assert lib.moge_route(sp, 0, None, None, fake, fake, fake, fake, None) == 1          # bias with logits-in
     assert lib.moge_route(sp, 0, fake, None, None, None, fake, fake, None) == 3          # x without w_router
     lib.moge_dispatch.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-                                  P, P, P, P, P, P, ctypes.c_size_t, P]
+                                  P, P, P, P, P, P, P, ctypes.c_size_t, P]
     ws = moge.workspace_size(s)
-    cap = moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 8)   # 64 tokens x 4 groups x 1
-    assert cap == 256
-    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap - 1, fake, fake, fake, fake, fake, fake, ws, None) == 7
-    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, fake, ws - 1, None) == 4
-    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, None, ws, None) == 4
-    assert lib.moge_dispatch(sp, 0, fake, fake, 3, 3, cap, fake, fake, fake, fake, fake, fake, ws, None) == 1
-    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 9, cap, fake, fake, fake, fake, fake, fake, ws, None) == 1
-    assert lib.moge_dispatch(sp, 3, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, fake, ws, None) == 1
-    assert lib.moge_dispatch(sp, 0, fake, None, 0, 8, cap, fake, fake, fake, fake, fake, fake, ws, None) == 3
-    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, None, fake, fake, fake, ws, None) == 3
-    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, None, None, fake, fake, ws, None) == 3
+    cap = moge.rows_bound(s, moge.ROUTE_GROUPED, 0, 8)   # 64 tokens x 4 groups x 1 + 15 x 8 padding
+    assert cap == 256 + 120
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap - 1, fake, fake, fake, fake, fake, None, fake, ws,
+                             None) == 7
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, None, fake, ws - 1,
+                             None) == 4
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, None, None, ws, None) == 4
+    assert lib.moge_dispatch(sp, 0, fake, fake, 3, 3, cap, fake, fake, fake, fake, fake, None, fake, ws, None) == 1
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 9, cap, fake, fake, fake, fake, fake, None, fake, ws, None) == 1
+    assert lib.moge_dispatch(sp, 3, fake, fake, 0, 8, cap, fake, fake, fake, fake, fake, None, fake, ws, None) == 1
+    assert lib.moge_dispatch(sp, 0, fake, None, 0, 8, cap, fake, fake, fake, fake, fake, None, fake, ws, None) == 3
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, None, fake, fake, None, fake, ws, None) == 3
+    assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, None, None, fake, None, fake, ws, None) == 3
+    # x_tiled without x
+    assert lib.moge_dispatch(sp, 0, fake, None, 0, 8, cap, fake, fake, fake, fake, None, fake, fake, ws, None) == 3
     big = S(N=128, M=2, Kp=64)                                                            # K = 128 > 64
-    assert lib.moge_dispatch(ctypes.byref(big), 0, fake, fake, 0, 128, 64 * 128, fake, fake, fake, fake, fake,
-                             fake, 1 << 20, None) == 2
+    assert lib.moge_dispatch(ctypes.byref(big), 0, fake, fake, 0, 128, 64 * 128 + 15 * 128, fake, fake, fake,
+                             fake, fake, None, fake, 1 << 20, None) == 2
     lib.moge_grouped_ffn.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64] + [P] * 6
     assert lib.moge_grouped_ffn(ctypes.byref(S(F=0)), fake, fake, 0, 8, 64, fake, fake, fake, fake, fake, None) == 2
     assert lib.moge_grouped_ffn(sp, fake, fake, 0, 8, 64, fake, None, fake, fake, fake, None) == 3

@@ -6,6 +6,7 @@ import torch
 import mixture_grouped_experts_amd as moge
 import oracle
 import synth
+from tests import moge_harness as H
 
 pytestmark = pytest.mark.gpu
 
@@ -27,11 +28,34 @@ def _run(T, d, N, M, Kp, idx, e_lo, e_hi, bf16=True, mode=moge.ROUTE_GROUPED, ex
     offsets = torch.full((N + 1,), -1, **dev)
     inv = torch.full((T, K), -9, **dev)
     perm = torch.full((cap,), -9, **dev)
-    xp = torch.zeros(cap, d, dtype=x.dtype, device="cuda")
+    xp = torch.full((moge.tiled_elems(cap, d),), 7.0, dtype=x.dtype, device="cuda")   # padding columns must become 0
+    xt = torch.full((moge.tiled_elems(T, d),), 7.0, dtype=x.dtype, device="cuda")
     ws = torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda")
-    moge.dispatch(s, mode, torch.from_numpy(idx).cuda(), x, e_lo, e_hi, cap, counts, offsets, inv, perm, xp, ws)
+    moge.dispatch(s, mode, torch.from_numpy(idx).cuda(), x, e_lo, e_hi, cap, counts, offsets, inv, perm, xp, ws,
+                  x_tiled=xt)
     torch.cuda.synchronize()
+    # the token-order tiled copy is x itself, padding columns zero
+    assert torch.equal(H.untile_rows(xt, T, d), x)
+    assert (H.untile_rows(xt, T, d, keep_pad_cols=True)[:, d:] == 0).all()
     return x, counts.cpu().numpy(), offsets.cpu().numpy(), inv.cpu().numpy(), perm.cpu().numpy(), xp
+
+
+def _check_rows(idx, x, counts, offsets, inv, perm, xp, e_lo, e_hi):
+    """counts/offsets bit-exact; inv/perm equal to the oracle's rows in the padded numbering; live rows
+    of x_perm are the tokens' rows (padding columns zero); rows past the last segment untouched."""
+    N = counts.size
+    rc, ro, rinv, rperm = oracle.dispatch(idx, N, e_lo, e_hi)
+    assert (counts == rc).all() and (offsets == ro).all()
+    pinv, pperm = H.padded_rows(idx, rinv, rperm, rc, ro, e_lo, e_hi)
+    assert (inv == pinv).all()
+    end = pperm.size
+    assert (perm[:end] == pperm).all() and (perm[end:] == -9).all()
+    d = x.shape[1]
+    live = np.nonzero(pperm >= 0)[0]
+    rows = H.untile_rows(xp, end, d, keep_pad_cols=True) if end else None
+    if live.size:
+        assert torch.equal(rows[torch.from_numpy(live).cuda(), :d], x[torch.from_numpy(pperm[live]).long().cuda()])
+        assert (rows[torch.from_numpy(live).cuda(), d:] == 0).all()
 
 
 CASES = [
@@ -51,12 +75,7 @@ CASES = [
 def test_dispatch_bitexact(gpu, T, d, N, M, Kp, e_lo, e_hi):
     idx = _idx(T, N, M, Kp, seed=T + N)
     x, counts, offsets, inv, perm, xp = _run(T, d, N, M, Kp, idx, e_lo, e_hi)
-    rc, ro, rinv, rperm = oracle.dispatch(idx, N, e_lo, e_hi)
-    assert (counts == rc).all() and (offsets == ro).all()
-    assert (inv == rinv).all()
-    live = rperm.size
-    assert (perm[:live] == rperm).all() and (perm[live:] == -9).all()
-    assert torch.equal(xp[:live], x[torch.from_numpy(rperm).long().cuda()])
+    _check_rows(idx, x, counts, offsets, inv, perm, xp, e_lo, e_hi)
 
 
 def test_dispatch_skewed_and_empty_experts(gpu):
@@ -65,20 +84,15 @@ def test_dispatch_skewed_and_empty_experts(gpu):
     idx[:] = np.arange(M) * (N // M)           # every token picks the first expert of every group
     idx[::5] += 1                              # a few pick the second; experts 2..7 of each group stay empty
     x, counts, offsets, inv, perm, xp = _run(T, d, N, M, Kp, idx, 0, N)
-    rc, ro, rinv, rperm = oracle.dispatch(idx, N)
-    assert (counts == rc).all() and (offsets == ro).all() and (inv == rinv).all() and (perm == rperm).all()
+    _check_rows(idx, x, counts, offsets, inv, perm, xp, 0, N)
     assert (counts[2:8] == 0).all()
-    assert torch.equal(xp, x[torch.from_numpy(rperm).long().cuda()])
 
 
 def test_dispatch_float32_and_global_mode(gpu):
     T, d, N, M, Kp = 333, 64, 16, 4, 1
     idx = _idx(T, N, M, Kp, seed=1, mode="global")
-    x, counts, offsets, inv, perm, xp = _run(T, d, N, M, Kp, idx, 4, 12, bf16=False, mode=moge.ROUTE_GLOBAL)
-    rc, ro, rinv, rperm = oracle.dispatch(idx, N, 4, 12)
-    assert (counts == rc).all() and (offsets == ro).all() and (inv == rinv).all()
-    assert (perm[:rperm.size] == rperm).all()
-    assert torch.equal(xp[:rperm.size], x[torch.from_numpy(rperm).long().cuda()])
+    x, counts, offsets, inv, perm, xp = _run(T, 72, N, M, Kp, idx, 4, 12, bf16=False, mode=moge.ROUTE_GLOBAL)
+    _check_rows(idx, x, counts, offsets, inv, perm, xp, 4, 12)
 
 
 def test_dispatch_rejects_small_capacity(gpu):
@@ -89,5 +103,5 @@ def test_dispatch_rejects_small_capacity(gpu):
         moge.dispatch(s, moge.ROUTE_GROUPED, torch.zeros(100, 4, **dev), torch.zeros(100, 64, dtype=torch.bfloat16,
                       device="cuda"), 0, 8, cap - 1, torch.zeros(8, **dev), torch.zeros(9, **dev),
                       torch.zeros(100, 4, **dev), torch.zeros(cap, **dev),
-                      torch.zeros(cap, 64, dtype=torch.bfloat16, device="cuda"),
+                      torch.zeros(moge.tiled_elems(cap, 64), dtype=torch.bfloat16, device="cuda"),
                       torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda"))

@@ -14,7 +14,15 @@ from tests import moge_harness as H
 pytestmark = pytest.mark.gpu
 
 
+def _pack(dtype_code, w):
+    out = torch.empty(w.shape[0] * moge.packed_weight_elems(w.shape[1], w.shape[2]), dtype=w.dtype, device="cuda")
+    moge.pack_weights(dtype_code, w, out)
+    return out
+
+
 def _dispatch_then_ffn(w, e_lo=None, e_hi=None):
+    """Route with the oracle, dispatch and run the grouped FFN through the C ABI.  Returns the
+    un-tiled x_perm and h (test-side restatement of the tiled layout) and the segment bases."""
     e_lo = w.e_lo if e_lo is None else e_lo
     e_hi = w.e_hi if e_hi is None else e_hi
     w = dataclasses.replace(w, e_lo=e_lo, e_hi=e_hi)
@@ -22,21 +30,38 @@ def _dispatch_then_ffn(w, e_lo=None, e_hi=None):
     hi = H.HostInputs(w)
     lg = H.oracle_logits_all(hi)
     idx, _, _ = oracle.route(lg, w.M, w.Kp, "grouped")
-    s = moge.Shape(w.T, w.d, w.N, w.M, w.Kp, w.F, moge.BF16 if w.dtype == "bf16" else moge.F32)
+    dc = moge.BF16 if w.dtype == "bf16" else moge.F32
+    s = moge.Shape(w.T, w.d, w.N, w.M, w.Kp, w.F, dc)
     cap = moge.rows_bound(s, moge.ROUTE_GROUPED, e_lo, e_hi)
     dt = dv.x.dtype
     i32 = dict(dtype=torch.int32, device="cuda")
     counts, offsets = torch.empty(w.N, **i32), torch.empty(w.N + 1, **i32)
     inv, perm = torch.empty(w.T, w.K, **i32), torch.empty(cap, **i32)
-    xp = torch.empty(cap, w.d, dtype=dt, device="cuda")
+    xp = torch.empty(moge.tiled_elems(cap, w.d), dtype=dt, device="cuda")
     ws = torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda")
     moge.dispatch(s, moge.ROUTE_GROUPED, torch.from_numpy(idx).cuda(), dv.x, e_lo, e_hi, cap, counts, offsets, inv,
                   perm, xp, ws)
-    hbuf = torch.full((cap, w.F), float("nan"), dtype=dt, device="cuda")
-    out = torch.full((cap, w.d), float("nan"), dtype=dt, device="cuda")
-    moge.grouped_ffn(s, xp, offsets, e_lo, e_hi, cap, dv.w_gate, dv.w_up, dv.w_down, hbuf, out)
+    pg, pu, pd = _pack(dc, dv.w_gate), _pack(dc, dv.w_up), _pack(dc, dv.w_down)
     torch.cuda.synchronize()
-    return w, dv, hi, idx, offsets.cpu().numpy(), perm.cpu().numpy(), xp, hbuf, out
+    # packing against the test-side restatement of the layout
+    assert torch.equal(pg, H.pack_ref(dv.w_gate)) and torch.equal(pd, H.pack_ref(dv.w_down))
+    hbuf = torch.full((moge.tiled_elems(cap, w.F),), float("nan"), dtype=dt, device="cuda")
+    out = torch.full((cap, w.d), float("nan"), dtype=dt, device="cuda")
+    moge.grouped_ffn(s, xp, offsets, e_lo, e_hi, cap, pg, pu, pd, hbuf, out)
+    torch.cuda.synchronize()
+    counts = counts.cpu().numpy()
+    P = H.segment_bases(counts, e_lo, e_hi)
+    X = H.untile_rows(xp, cap, w.d)
+    Hm = H.untile_rows(hbuf, cap, w.F, keep_pad_cols=True)
+    return w, dv, hi, idx, counts, P, perm.cpu().numpy(), X, Hm, out
+
+
+def _live_rows(w, counts, P):
+    return np.concatenate([np.arange(P[k], P[k] + counts[w.e_lo + k]) for k in range(w.e_hi - w.e_lo)])
+
+
+def _expert_of(w, P, rows):
+    return np.searchsorted(P, rows, side="right") - 1 + w.e_lo
 
 
 MID = W.variant(W.decode(), name="mid_T300_d256_N16_M4_K2_F200", T=300, d=256, N=16, M=4, Kp=2, F=200,
@@ -47,31 +72,33 @@ MID = W.variant(W.decode(), name="mid_T300_d256_N16_M4_K2_F200", T=300, d=256, N
                                W.decode()], ids=lambda w: w.name)
 def test_grouped_ffn_vs_torch_matmul(gpu, w):
     print(f"[ffn vs torch] {w.name}", flush=True)
-    w, dv, _, _, off, perm, xp, hbuf, out = _dispatch_then_ffn(w)
-    live = int(off[w.e_hi] - off[w.e_lo])
+    w, dv, _, _, counts, P, perm, X, Hm, out = _dispatch_then_ffn(w)
     for ei in range(w.e_hi - w.e_lo):
         e = w.e_lo + ei
-        r0, r1 = int(off[e] - off[w.e_lo]), int(off[e + 1] - off[w.e_lo])
+        r0, r1 = int(P[ei]), int(P[ei] + counts[e])
         if r1 == r0:
             continue
-        xe = xp[r0:r1].float()
+        xe = X[r0:r1].float()
         a = xe @ dv.w_gate[ei].float().t().contiguous()
         b = xe @ dv.w_up[ei].float().t().contiguous()
         href = (a * torch.sigmoid(a) * b)
         # h: float32 epilogue of float32 sums, rounded to bf16 -> within a couple of bf16 ulps
-        assert torch.allclose(hbuf[r0:r1].float(), href, rtol=1.6e-2, atol=1e-3 * href.abs().max().item() + 1e-6)
-        oref = hbuf[r0:r1].float() @ dv.w_down[ei].float().t().contiguous()
+        hm = Hm[r0:r1, :w.F].float()
+        assert torch.allclose(hm, href, rtol=1.6e-2, atol=1e-3 * href.abs().max().item() + 1e-6)
+        assert (Hm[r0:r1, w.F:] == 0).all()  # padding columns of h are exact zeros
+        oref = hm @ dv.w_down[ei].float().t().contiguous()
         assert torch.allclose(out[r0:r1].float(), oref, rtol=1.6e-2, atol=1e-3 * oref.abs().max().item() + 1e-6)
-    assert not torch.isnan(out[:live].float()).any()
+    live = torch.from_numpy(_live_rows(w, counts, P)).long().cuda()
+    assert not torch.isnan(out[live].float()).any()
 
 
 @pytest.mark.parametrize("w", [MID, W.decode(), W.tiny()], ids=lambda w: w.name)
 def test_grouped_ffn_vs_oracle_rows(gpu, w):
     print(f"[ffn vs oracle] {w.name}", flush=True)
-    w, dv, hi, idx, off, perm, xp, hbuf, out = _dispatch_then_ffn(w)
-    live = int(off[w.e_hi] - off[w.e_lo])
-    rows = np.unique(np.linspace(0, live - 1, min(live, 48)).astype(int))
-    expert_of = np.searchsorted(off[w.e_lo:w.e_hi + 1] - off[w.e_lo], rows, side="right") - 1 + w.e_lo
+    w, dv, hi, idx, counts, P, perm, X, Hm, out = _dispatch_then_ffn(w)
+    live = _live_rows(w, counts, P)
+    rows = live[np.unique(np.linspace(0, live.size - 1, min(live.size, 48)).astype(int))]
+    expert_of = _expert_of(w, P, rows)
     ref = np.stack([oracle.ffn_row(hi.x_rows([perm[r]])[0], *hi.expert(int(e))) for r, e in zip(rows, expert_of)])
     got = out[torch.from_numpy(rows).long().cuda()].float().cpu().numpy()
     ok, err, bound = H.tol_ok(got, ref)
@@ -80,22 +107,23 @@ def test_grouped_ffn_vs_oracle_rows(gpu, w):
 
 def test_grouped_ffn_expert_range_and_shared_form(gpu):
     # a device's share: experts [4, 8) only, weights of those experts only
-    w, dv, hi, idx, off, perm, xp, hbuf, out = _dispatch_then_ffn(MID, 4, 8)
-    live = int(off[8] - off[4])
-    rows = np.arange(0, live, max(1, live // 20))
-    expert_of = np.searchsorted(off[4:9] - off[4], rows, side="right") - 1 + 4
+    w, dv, hi, idx, counts, P, perm, X, Hm, out = _dispatch_then_ffn(MID, 4, 8)
+    live = _live_rows(w, counts, P)
+    rows = live[::max(1, live.size // 20)]
+    expert_of = _expert_of(w, P, rows)
     ref = np.stack([oracle.ffn_row(hi.x_rows([perm[r]])[0], *hi.expert(int(e))) for r, e in zip(rows, expert_of)])
     ok, err, bound = H.tol_ok(out[torch.from_numpy(rows).long().cuda()].float().cpu().numpy(), ref)
     assert ok, (err, bound)
-    # the shared-expert form: one expert, offsets {0, T}, x_perm = x
+    # the shared-expert form: one expert, offsets {0, T}, x_perm = x in the tiled layout
     sw = W.variant(MID, F_shared=136, std_shared_down=0.02)
     dsh = H.device_inputs(sw).shared
     hsh = H.HostInputs(sw).shared()
     s1 = moge.Shape(sw.T, sw.d, 1, 1, 1, 136, moge.BF16)
     so = torch.tensor([0, sw.T], dtype=torch.int32, device="cuda")
-    hb = torch.empty(sw.T, 136, dtype=torch.bfloat16, device="cuda")
+    hb = torch.empty(moge.tiled_elems(sw.T, 136), dtype=torch.bfloat16, device="cuda")
     ob = torch.empty(sw.T, sw.d, dtype=torch.bfloat16, device="cuda")
-    moge.grouped_ffn(s1, dv.x, so, 0, 1, sw.T, dsh[0], dsh[1], dsh[2], hb, ob)
+    packed = [_pack(moge.BF16, m.unsqueeze(0)) for m in dsh]
+    moge.grouped_ffn(s1, H.tile_rows(dv.x), so, 0, 1, sw.T, packed[0], packed[1], packed[2], hb, ob)
     torch.cuda.synchronize()
     toks = [0, 1, 150, sw.T - 1]
     ref = np.stack([oracle.ffn_row(hi.x_rows([t])[0], *hsh) for t in toks])

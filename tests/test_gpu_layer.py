@@ -19,9 +19,18 @@ from tests import moge_harness as H
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(w):
+def packed_inputs(w, layer):
+    """Device inputs with the expert weights packed once (the row-major copies are dropped)."""
     dv = H.device_inputs(w)
+    if w.F:
+        (pg, pu, pd), ps = layer.pack_expert_weights(dv.w_gate, dv.w_up, dv.w_down, dv.shared)
+        dv = dataclasses.replace(dv, w_gate=pg, w_up=pu, w_down=pd, shared=ps)
+    return dv
+
+
+def run_layer(w):
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi)
+    dv = packed_inputs(w, layer)
     y = layer.forward(dv.x, dv.w_router, dv.bias, dv.w_gate, dv.w_up, dv.w_down, dv.shared)
     torch.cuda.synchronize()
     return dv, layer, y
@@ -98,8 +107,8 @@ def test_layer_group0_sampled(gpu):
 
 def test_layer_deterministic(gpu):
     w = W.variant(W.decode(), name="det", T=600, std_bias=2.0)
-    dv = H.device_inputs(w)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, 0, "bf16")
+    dv = packed_inputs(w, layer)
     outs = []
     for _ in range(2):
         y = layer.forward(dv.x, dv.w_router, dv.bias, dv.w_gate, dv.w_up, dv.w_down)
