@@ -54,15 +54,7 @@ constexpr size_t kGemmLds = (size_t)kStages * kStageB;  // 144 KiB
 constexpr int kThreads = 512;               // 8 waves: two per SIMD
 constexpr int kGroupM = 4;                  // m-tiles per scheduling group
 
-// 16-byte chunk c of LDS row r lives in slot c ^ swz(r).  Four 64-byte rows share a
-// 256-byte bank line; with this swizzle the 16 rows that one fragment read touches
-// per clock cover all 64 banks (measured conflict-free on gfx950).
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-// s_waitcnt immediates (gfx9 encoding): at most n vector memory operations of this
-// wave outstanding; the second form also waits for all of the wave's LDS reads.
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+__device__ __forceinline__ int swz(int r) { return lds_swz(r); }
 
 // One tile: reduction loop and epilogue, 8 waves.  Wave (wm, wn), wm in {0,1},
 // wn in {0..3}, owns the token row blocks wm, wm+2, ..., wm+8 (32 rows each,
@@ -114,23 +106,17 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
       dsrc[j] = (SWIGLU && r >= 128 ? wbase1 : wbase0) + (int64_t)band * nkf * kTileElems + inner;
     }
   }
-  // Step ks into stage ks % 4 (steps past the last full step reload step 0).  The
-  // DMA is issued from inline assembly so the compiler does not turn its LDS side
-  // effect into a full vmcnt wait before every LDS read; the waits are explicit
-  // (vmcnt_imm) and each is followed by a barrier before the stage is read.  The
-  // instruction has no register result, only an address operand read at issue.
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  // Step ks into stage ks % 4 (steps past the last full step reload step 0); the
+  // waits are explicit (vmcnt_imm) and each is followed by a barrier before the
+  // stage is read.
+  const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int ks) {
     const int k = ks < nkf ? ks * kTileElems : 0;
     const uint32_t st = lds0 + (uint32_t)((ks % kStages) * kStageB);
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
       if (j == 4 && wtok) break;
-      const uint32_t m0v = __builtin_amdgcn_readfirstlane(st + (uint32_t)(lrow[j] * kRowB));
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :
-                   : "v"(dsrc[j] + k), "s"(m0v)
-                   : "memory", "m0");
+      dma_16x64(dsrc[j] + k, st + (uint32_t)(lrow[j] * kRowB));
     }
   };
   const int kc = (lane >> 5);  // logical chunk of this lane inside a 16-element sub-step

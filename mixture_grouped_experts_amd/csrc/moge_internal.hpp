@@ -67,6 +67,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ---- direct-to-LDS staging of 64-byte rows (the expert GEMMs and the router)
+// 16-byte chunk c of 64-byte LDS row r lives in slot c ^ lds_swz(r).  Four such rows
+// share a 256-byte bank line; with this swizzle the 16 rows that one 16-byte
+// fragment read touches per clock cover all 64 banks (measured conflict-free on
+// gfx950).
+__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// s_waitcnt immediates (gfx9 encoding): at most n vector memory operations of this
+// wave outstanding; the second form also waits for all of the wave's LDS reads.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+// LDS byte address of a __shared__ pointer (what M0 takes for a direct load).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One wave moves 64 x 16 bytes from global memory straight into LDS: lane l's 16
+// bytes at `src` land at LDS byte m0 + 16 l (m0 wave-uniform).  Issued from inline
+// assembly so the compiler does not turn the LDS side effect into a full vmcnt wait
+// before every LDS read; callers wait with vmcnt_imm and a barrier before reading.
+// The instruction has no register result, only an address operand read at issue.
+__device__ __forceinline__ void dma_16x64(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(m0))
+               : "memory", "m0");
+}
+
 // Number of lanes below the calling lane whose bit is set in `mask`.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

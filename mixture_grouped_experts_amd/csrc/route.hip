@@ -8,16 +8,15 @@
 //
 // gfx950 design
 //   * bf16 scores: x [T][d] is streamed from HBM exactly once.  A workgroup of 4
-//     waves owns TM tokens x NP (N rounded up to 64) experts; each wave owns a
-//     32-token x 64-expert block and accumulates it with v_mfma_f32_32x32x16_bf16
-//     (float32 accumulate).  x goes straight from HBM into MFMA operand registers:
-//     the reduction over d is order-free, so every lane reads a contiguous
-//     BK/2-element run of its token row (lane half h owns k in [h*BK/2, (h+1)*BK/2)
-//     of each BK step) and the router weights are read from LDS with the same k
-//     assignment.  The router weight slab of each BK step is staged once per
-//     workgroup in LDS (rows padded by 16 B, so the 16-byte operand reads are
-//     bank-conflict free) and double buffered; the next step's x and weights are
-//     in flight while the current step's MFMAs run.
+//     waves owns TM tokens x NP (N rounded up to 64, 128 or 256) experts, TM*NP =
+//     8192; each wave owns a 32-token x 64-expert block and accumulates it with
+//     v_mfma_f32_32x32x16_bf16 (float32 accumulate).  Token rows and router rows go
+//     from global memory straight into a 6- or 7-stage LDS ring with direct-to-LDS
+//     loads, several 32-element steps ahead, so each workgroup keeps tens of KiB of
+//     x in flight (what HBM needs to stream at full rate) without staging
+//     registers; the router slab of a step is shared by the workgroup's waves.
+//     Few tokens (fewer 128-token tiles than CUs): a split-K kernel whose operands
+//     go straight from global memory into MFMA registers.
 //   * Epilogue in the same kernel: the TM x N score tile goes to LDS, the optional
 //     score store is coalesced, and one wave per token does the softmax (wave-wide
 //     max and sum) and the per-group rank count that picks the top-K'.
@@ -110,7 +109,66 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int N,
   }
 }
 
+// Lane-parallel choice for up to 64 groups: in one wave pass, lane (tl, g) handles
+// group g of token tl; a token's Mp lanes (n_groups rounded up to a power of two)
+// are adjacent, so the softmax max and sum over its N scores are butterflies over
+// Mp lanes, and a pass covers 64 / Mp tokens at once.  Inside the group, k rounds
+// each take the best score that comes after the previous pick in the order
+// (score descending, expert id ascending): round r finds the expert of rank r.
+// Score rows are `ld` floats apart (ld odd keeps the lanes' reads on distinct banks).
+__device__ __forceinline__ void select_tile(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
+                                            int N, int n_groups, int k, int32_t* __restrict__ idx,
+                                            float* __restrict__ gate) {
+  const int G = N / n_groups, K = n_groups * k;
+  int Mp = 1;
+  while (Mp < n_groups) Mp <<= 1;
+  const int tpp = 64 / Mp;  // tokens per wave pass
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int g = lane & (Mp - 1), tl = lane / Mp;
+  for (int r0 = wave * tpp; r0 < rows; r0 += nw * tpp) {  // wave-uniform
+    const int r = r0 + tl;
+    const bool own = r < rows && t0 + r < T && g < n_groups;
+    const float* v = lt + (int64_t)(own ? r : 0) * ld + (own ? g * G : 0);
+    const int n = own ? G : 0;
+    float m = -INFINITY;
+    for (int i = 0; i < n; ++i) m = fmaxf(m, v[i]);
+    for (int off = 1; off < Mp; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    float z = 0.f;
+    for (int i = 0; i < n; ++i) z += expf(v[i] - m);
+    for (int off = 1; off < Mp; off <<= 1) z += __shfl_xor(z, off, 64);
+    if (own) {
+      const int64_t t = t0 + r;
+      float pv = INFINITY;
+      int pi = -1;
+      for (int rk = 0; rk < k; ++rk) {
+        float bv = -INFINITY;
+        int bi = -1;
+        for (int i = 0; i < n; ++i) {
+          const float x = v[i];
+          const bool after = x < pv || (x == pv && i > pi);  // not yet taken
+          if (after && (bi < 0 || x > bv)) {
+            bv = x;
+            bi = i;
+          }
+        }
+        pv = bv;
+        pi = bi;
+        idx[t * K + g * k + rk] = g * G + bi;
+        gate[t * K + g * k + rk] = expf(bv - m) / z;
+      }
+    }
+  }
+}
+
+// The lane-parallel choice scans (k + 2) * G scores per lane; past a small budget
+// (wide groups such as the global top-K over all experts) one wave per token with
+// wave-wide reductions is faster.
+__host__ __device__ __forceinline__ bool lane_parallel_choice(int N, int n_groups, int k) {
+  return n_groups <= 64 && (k + 2) * (N / n_groups) <= 256;
+}
+
 // Writes the LDS score tile [rows][ld] to logits_out (if any) and runs the choice.
+// (all threads of the block call it)
 __device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
                                               int N, int n_groups, int k, float* __restrict__ logits_out,
                                               int32_t* __restrict__ idx, float* __restrict__ gate) {
@@ -120,6 +178,10 @@ __device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int 
       if (t0 + r < T) logits_out[(t0 + r) * N + c] = lt[r * ld + c];
     }
   }
+  if (lane_parallel_choice(N, n_groups, k)) {
+    select_tile(lt, ld, rows, t0, T, N, n_groups, k, idx, gate);
+    return;
+  }
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
   for (int r = wave; r < rows; r += nwaves) {
@@ -128,118 +190,171 @@ __device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int 
 }
 
 // ----------------------------------------------------------------------------
-// bf16 scores with MFMA.  WC waves across experts (NP = 64*WC), 4/WC across tokens.
-template <int WC, int BK>
-__global__ __launch_bounds__(256) void route_mfma_kernel(int64_t T, int d, int N, int n_groups, int k,
-                                                         const uint16_t* __restrict__ x,
-                                                         const uint16_t* __restrict__ w,
-                                                         const float* __restrict__ bias,
-                                                         float* __restrict__ logits_out, int32_t* __restrict__ idx,
-                                                         float* __restrict__ gate) {
-  constexpr int WR = 4 / WC;
-  constexpr int TM = 32 * WR;
-  constexpr int NP = 64 * WC;
-  constexpr int LDW = BK + 8;          // padded LDS row, bf16 elements
-  constexpr int HALF = BK / 2;         // k run per lane half
-  constexpr int NCH = HALF / 8;        // 16-byte chunks per lane per step (= MFMAs per col block)
-  constexpr int WCH = NP * (BK / 8) / 256;  // weight chunks per thread per step
-  constexpr int WBUF = NP * LDW;       // bf16 elements per weight buffer
-  constexpr int SMEM_W = 2 * WBUF * 2;
-  constexpr int SMEM_L = TM * NP * 4;
-  constexpr int SMEM = SMEM_W > SMEM_L ? SMEM_W : SMEM_L;
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
-  uint16_t* wl = reinterpret_cast<uint16_t*>(smem);
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wr = wave / WC, wc = wave % WC;
+// bf16 scores, many tokens.  A workgroup of 4 waves owns TM tokens x NP experts
+// (NP = N rounded up to 64, 128 or 256 and TM = 8192 / NP, so every wave owns one
+// 32-token x 64-expert block: two 32x32 accumulators).  The token rows and the
+// router rows of each 32-element step go from global memory straight into an
+// S-stage LDS ring (global_load_lds_dwordx4, 16 rows of 64 bytes per instruction,
+// XOR-swizzled rows), S - 1 steps ahead, so x streams from HBM with several steps
+// of loads in flight per workgroup and no staging registers; x is read exactly
+// once.  One barrier per step.  The epilogue keeps the TM x NP score tile in LDS
+// for the softmax and the per-group choice.
+template <int TM, int NP, int S>
+__global__ __launch_bounds__(256) void route_dma_kernel(int64_t T, int d, int N, int n_groups, int k,
+                                                        const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ w,
+                                                        const float* __restrict__ bias,
+                                                        float* __restrict__ logits_out, int32_t* __restrict__ idx,
+                                                        float* __restrict__ gate) {
+  constexpr int ROWS = TM + NP;      // stage rows of 64 bytes: tokens, then experts
+  constexpr int NI = ROWS / 16;      // load instructions per step
+  constexpr int NJ = (NI + 3) / 4;   // per wave, at most
+  constexpr int CH = NJ;             // loads per step of waves 0 .. NI%4 - 1 (all waves when NI%4 == 0)
+  constexpr int CL = NI / 4;         // loads per step of the other waves
+  constexpr int STAGE = ROWS * 64;
+  constexpr int TB = TM / 32;        // token blocks; wave = token block + TB * expert slice
+  static_assert(TM * NP == 8192 && S >= 4 && NI % 4 != 1, "route tile");
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tb = wave % TB, es = wave / TB;
   const int64_t t0 = (int64_t)blockIdx.x * TM;
-  int64_t arow = t0 + wr * 32 + (lane & 31);
-  if (arow > T - 1) arow = T - 1;
-  const uint16_t* aptr = x + arow * d + (lane >> 5) * HALF;
-  const int nk = (d + BK - 1) / BK;
+  const int nkf = d / 32;                        // full steps; a ragged tail follows the loop
+  const bool many = (NI % 4 == 0) || wave < (NI % 4);  // this wave issues CH loads per step, else CL
 
-  // weight chunk c of a step: row c / (BK/8), 16-byte column c % (BK/8)
-  auto load_w = [&](int ks, u32x4_t* reg) {
+  // load j of this wave moves stage rows 16 i .. 16 i + 15 with i = wave + 4 j
+  const uint16_t* src[NJ];
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-      const int kk = ks * BK + col;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (row < N && kk < d) v = *reinterpret_cast<const u32x4_t*>(w + (int64_t)row * d + kk);
-      reg[i] = v;
+  for (int j = 0; j < NJ; ++j) {
+    const int srow = 16 * (wave + 4 * j) + (lane >> 2);
+    const int c = (lane & 3) ^ lds_swz(srow);
+    if (srow < TM) {
+      int64_t t = t0 + srow;
+      if (t > T - 1) t = T - 1;
+      src[j] = x + t * d + c * 8;
+    } else {
+      int e = srow - TM;
+      if (e > N - 1) e = N - 1;
+      src[j] = w + (int64_t)e * d + c * 8;
     }
-  };
-  auto store_w = [&](int buf, const u32x4_t* reg) {
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int ks) {
+    if (ks >= nkf) return;
+    const uint32_t st = lds0 + (uint32_t)((ks % S) * STAGE);
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-      *reinterpret_cast<u32x4_t*>(wl + buf * WBUF + row * LDW + col) = reg[i];
-    }
+    for (int j = 0; j < NJ; ++j)
+      if (wave + 4 * j < NI) dma_16x64(src[j] + ks * 32, st + (uint32_t)(16 * (wave + 4 * j) * 64));
   };
-  auto load_a = [&](int ks, u32x4_t* reg) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int kk = ks * BK + (lane >> 5) * HALF + j * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (kk < d) v = *reinterpret_cast<const u32x4_t*>(aptr + (int64_t)ks * BK + j * 8);
-      reg[j] = v;
+  // at most `steps` steps of this wave's loads still in flight (and, with lgkm, no LDS reads)
+  auto wait_steps = [&](int steps_left_ok, bool lgkm) {
+    // steps_left_ok is S - 3 (steady state) or 0 (prologue / tail); both branches are immediates
+    if (steps_left_ok == 0) {
+      if (lgkm) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else if (many) {
+      if (lgkm) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((S - 3) * CH));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * CH));
+    } else {
+      if (lgkm) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((S - 3) * CL));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * CL));
     }
   };
 
+  const int kc = lane >> 5;
+  const int arow = tb * 32 + (lane & 31);
+  int brow[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) brow[cb] = TM + es * 64 + cb * 32 + (lane & 31);
+  auto frag = [&](int stage, int kk, bf16x8_t& a, bf16x8_t (&b)[2]) {
+    const char* st = lds + stage * STAGE;
+    const int c = kk * 2 + kc;
+    a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + arow * 64 + ((c ^ lds_swz(arow)) << 4)));
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      b[cb] = __builtin_bit_cast(bf16x8_t,
+                                 *reinterpret_cast<const u32x4_t*>(st + brow[cb] * 64 + ((c ^ lds_swz(brow[cb])) << 4)));
+  };
   f32x16_t acc[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+  auto mfma = [&](const bf16x8_t& a, const bf16x8_t (&b)[2]) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[cb], acc[cb], 0, 0, 0);
+  };
 
-  u32x4_t wreg[WCH], areg[NCH], anext[NCH];
-  load_w(0, wreg);
-  load_a(0, areg);
-  store_w(0, wreg);
+  // prologue: steps 0 .. S-2 in flight; steps 0 and 1 landed
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  wait_steps(nkf >= S - 1 ? S - 3 : 0, false);
   __syncthreads();
-
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) {
-      load_w(ks + 1, wreg);
-      load_a(ks + 1, anext);
-    }
-    const uint16_t* wb = wl + buf * WBUF;
+  bf16x8_t a0, b0[2], a1, b1[2];
+  frag(0, 0, a0, b0);
+  for (int ks = 0; ks < nkf; ++ks) {
+    issue(ks + S - 1);  // into stage (ks - 1) % S, last read before the previous barrier
+    frag(ks % S, 1, a1, b1);
+    mfma(a0, b0);
+    frag((ks + 1) % S, 0, a0, b0);  // read-ahead (unused after the last step)
+    mfma(a1, b1);
+    // step ks + 2 landed (every step is waited for once the tail issues no more)
+    wait_steps(ks + S - 1 < nkf ? S - 3 : 0, true);
+    __syncthreads();
+  }
+  if (d % 32) {
+    // ragged tail: one step through registers, columns at or past d are zero
+    const int kt = nkf * 32;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, areg[j]);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int col = wc * 64 + cb * 32 + (lane & 31);
-        const u32x4_t braw = *reinterpret_cast<const u32x4_t*>(wb + col * LDW + (lane >> 5) * HALF + j * 8);
-        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, braw), acc[cb], 0, 0, 0);
+    for (int j = 0; j < NJ; ++j) {
+      if (wave + 4 * j < NI) {
+        const int srow = 16 * (wave + 4 * j) + (lane >> 2);
+        const int c = (lane & 3) ^ lds_swz(srow);
+        const u32x4_t v = (kt + c * 8 < d) ? *reinterpret_cast<const u32x4_t*>(src[j] + kt) : zero;
+        *reinterpret_cast<u32x4_t*>(lds + 16 * (wave + 4 * j) * 64 + lane * 16) = v;
       }
     }
-    if (more) {
-      store_w(buf ^ 1, wreg);
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) areg[j] = anext[j];
-    }
+    __syncthreads();
+    frag(0, 0, a0, b0);
+    frag(0, 1, a1, b1);
+    mfma(a0, b0);
+    mfma(a1, b1);
     __syncthreads();
   }
 
-  // scores -> LDS tile [TM][NP]; padded experts get -inf (never chosen, exp = 0)
-  float* lt = reinterpret_cast<float*>(smem);
+  // scores -> LDS tile [TM][NP + 1] (odd row stride); padded experts get -inf
+  constexpr int LD = NP + 1;
+  float* lt = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const int col = wc * 64 + cb * 32 + (lane & 31);
+    const int col = es * 64 + cb * 32 + (lane & 31);
     const float b = (bias && col < N) ? bias[col] : 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wr * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      lt[row * NP + col] = col < N ? acc[cb][r] + b : -INFINITY;
+      const int row = tb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      lt[row * LD + col] = col < N ? acc[cb][r] + b : -INFINITY;
     }
   }
   __syncthreads();
-  tile_epilogue(lt, NP, TM, t0, T, N, n_groups, k, logits_out, idx, gate);
+  tile_epilogue(lt, LD, TM, t0, T, N, n_groups, k, logits_out, idx, gate);
+}
+
+template <int TM, int NP, int S>
+static moge_status_t launch_route_dma(const moge_shape_t& s, int n_groups, int k, const void* x, const void* w,
+                                      const float* bias, float* logits, int32_t* idx, float* gate,
+                                      hipStream_t stream) {
+  constexpr size_t ring = (size_t)S * (TM + NP) * 64;
+  constexpr size_t tile = (size_t)TM * (NP + 1) * 4;
+  constexpr size_t lds = ring > tile ? ring : tile;
+  const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S>);
+  moge_status_t st = raise_dynamic_lds(kern, lds, "route_dma_kernel");
+  if (st != MOGE_OK) return st;
+  const int64_t grid = ((int64_t)s.T + TM - 1) / TM;
+  hipLaunchKernelGGL((route_dma_kernel<TM, NP, S>), dim3((unsigned)grid), dim3(256), lds, stream, (int64_t)s.T, s.d,
+                     s.N, n_groups, k, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
+                     logits, idx, gate);
+  return check_launch("route_dma_kernel");
 }
 
 // ----------------------------------------------------------------------------
@@ -344,29 +459,34 @@ __global__ __launch_bounds__(256) void route_f32_kernel(int64_t T, int d, int N,
 }
 
 // ----------------------------------------------------------------------------
-// Caller-supplied scores.  32 tokens per workgroup.
-constexpr int kSelTokens = 32;
+// Caller-supplied scores.  Lane-parallel choice: 64 tokens per workgroup, staged in
+// LDS with an odd row stride.  Wide groups: one token per wave, 4 per workgroup
+// (the choice is a chain of wave-wide reductions; many resident waves hide it).
+constexpr int kSelTokens = 64;
+constexpr int kSelTokensWide = 4;
+template <bool LANES>
 __global__ __launch_bounds__(256) void route_select_kernel(int64_t T, int N, int n_groups, int k,
                                                            const float* __restrict__ logits,
                                                            int32_t* __restrict__ idx, float* __restrict__ gate) {
-  __shared__ float lt[kSelTokens * kMaxExperts];
-  const int64_t t0 = (int64_t)blockIdx.x * kSelTokens;
-  for (int i = threadIdx.x; i < kSelTokens * N; i += blockDim.x) {
-    const int r = i / N, c = i - r * N;
-    lt[r * N + c] = (t0 + r < T) ? logits[(t0 + r) * N + c] : 0.f;
+  extern __shared__ float lt[];
+  if (LANES) {  // [kSelTokens][N + 1]
+    const int ld = N + 1;
+    const int64_t t0 = (int64_t)blockIdx.x * kSelTokens;
+    for (int i = threadIdx.x; i < kSelTokens * N; i += blockDim.x) {
+      const int r = i / N, c = i - r * N;
+      lt[r * ld + c] = (t0 + r < T) ? logits[(t0 + r) * N + c] : 0.f;
+    }
+    __syncthreads();
+    select_tile(lt, ld, kSelTokens, t0, T, N, n_groups, k, idx, gate);
+  } else {      // [kSelTokensWide][N]
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kSelTokensWide + wave;
+    if (t >= T) return;  // wave-uniform; no barrier below
+    float* row = lt + wave * N;
+    for (int e = lane; e < N; e += 64) row[e] = logits[t * N + e];
+    __builtin_amdgcn_wave_barrier();  // the row is written and read by this wave only (LDS is in order per wave)
+    select_token(row, N, n_groups, k, t, idx, gate);
   }
-  __syncthreads();
-  tile_epilogue(lt, N, kSelTokens, t0, T, N, n_groups, k, nullptr, idx, gate);
-}
-
-template <int WC, int BK>
-static void launch_route_mfma(const moge_shape_t& s, int n_groups, int k, const void* x, const void* w,
-                              const float* bias, float* logits, int32_t* idx, float* gate, hipStream_t stream) {
-  constexpr int TM = 32 * (4 / WC);
-  const int64_t grid = ((int64_t)s.T + TM - 1) / TM;
-  hipLaunchKernelGGL((route_mfma_kernel<WC, BK>), dim3((unsigned)grid), dim3(256), 0, stream, (int64_t)s.T, s.d,
-                     s.N, n_groups, k, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
-                     logits, idx, gate);
 }
 
 }  // namespace moge
@@ -388,9 +508,21 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
   const int k = mode == MOGE_ROUTE_GROUPED ? s.k_per_group : s.M * s.k_per_group;
 
   if (!x) {
-    const int64_t grid = ((int64_t)s.T + kSelTokens - 1) / kSelTokens;
-    hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (int64_t)s.T, s.N,
-                       n_groups, k, logits, idx, gate);
+    if (lane_parallel_choice(s.N, n_groups, k)) {
+      const int64_t grid = ((int64_t)s.T + kSelTokens - 1) / kSelTokens;
+      const size_t lds = sizeof(float) * kSelTokens * (size_t)(s.N + 1);
+      if (lds > 64 * 1024) {
+        st = raise_dynamic_lds(reinterpret_cast<const void*>(route_select_kernel<true>), lds, "route_select_kernel");
+        if (st != MOGE_OK) return st;
+      }
+      hipLaunchKernelGGL(route_select_kernel<true>, dim3((unsigned)grid), dim3(256), lds, stream, (int64_t)s.T, s.N,
+                         n_groups, k, logits, idx, gate);
+    } else {
+      const int64_t grid = ((int64_t)s.T + kSelTokensWide - 1) / kSelTokensWide;
+      hipLaunchKernelGGL(route_select_kernel<false>, dim3((unsigned)grid), dim3(256),
+                         sizeof(float) * kSelTokensWide * (size_t)s.N, stream, (int64_t)s.T, s.N, n_groups, k, logits,
+                         idx, gate);
+    }
     st = check_launch("route_select_kernel");
   } else if (s.dtype == MOGE_F32) {
     const int64_t grid = ((int64_t)s.T + kF32Tokens - 1) / kF32Tokens;
@@ -405,18 +537,19 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
       hipLaunchKernelGGL(route_mfma_splitk_kernel<1>, dim3((unsigned)(((int64_t)s.T + 31) / 32)), dim3(256), 0,
                          stream, (int64_t)s.T, s.d, s.N, n_groups, k, static_cast<const uint16_t*>(x),
                          static_cast<const uint16_t*>(w_router), bias, logits, idx, gate);
+      st = check_launch("route_mfma_splitk_kernel");
     } else if (few && s.N <= 128) {
       hipLaunchKernelGGL(route_mfma_splitk_kernel<2>, dim3((unsigned)(((int64_t)s.T + 31) / 32)), dim3(256), 0,
                          stream, (int64_t)s.T, s.d, s.N, n_groups, k, static_cast<const uint16_t*>(x),
                          static_cast<const uint16_t*>(w_router), bias, logits, idx, gate);
+      st = check_launch("route_mfma_splitk_kernel");
     } else if (s.N <= 64) {
-      launch_route_mfma<1, 128>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+      st = launch_route_dma<128, 64, 6>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
     } else if (s.N <= 128) {
-      launch_route_mfma<2, 128>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+      st = launch_route_dma<64, 128, 6>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
     } else {
-      launch_route_mfma<4, 64>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+      st = launch_route_dma<32, 256, 7>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
     }
-    st = check_launch("route_mfma_kernel");
   }
   return st == MOGE_OK ? ok() : st;
 }
