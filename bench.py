@@ -62,7 +62,7 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read_per_launch": n, "bytes_written_per_launch": n, "launches": 3}))
 
 
-def algorithmic_work(w, counts):
+def algorithmic_work(w, counts, fused_shared=False):
     """Bytes and FLOPs each call must move / compute (unique HBM traffic; no re-reads counted)."""
     import numpy as np
 
@@ -81,7 +81,14 @@ def algorithmic_work(w, counts):
         work["combine"] = dict(bytes=R * d * b + T * d * 4 + T * K * 8 + (T * d * b if w.F_shared else 0), flops=0)
     if w.F_shared:
         Fs = w.F_shared
-        work["shared"] = dict(bytes=3 * Fs * d * b + 2 * T * d * b + T * Fs * b * 2, flops=2 * T * d * 3 * Fs)
+        gu = dict(bytes=2 * Fs * d * b + T * d * b + T * Fs * b, flops=2 * T * d * 2 * Fs)
+        dn = dict(bytes=Fs * d * b + T * Fs * b + T * d * b, flops=2 * T * Fs * d)
+        if fused_shared:
+            # the shared expert runs inside the routed experts' gate/up and down launches
+            for stage, extra in (("gate_up", gu), ("down", dn)):
+                work[stage] = {k: work[stage][k] + extra[k] for k in ("bytes", "flops")}
+        else:
+            work["shared"] = {k: gu[k] + dn[k] for k in ("bytes", "flops")}
     return work
 
 
@@ -227,7 +234,7 @@ def main():
     value = w.T * args.steps / (total_ms / 1000.0)
 
     counts = layer.counts.cpu().numpy()
-    work = algorithmic_work(w, counts)
+    work = algorithmic_work(w, counts, fused_shared=bool(w.F_shared) and layer.fuse_shared)
     dom = max((k for k in work if k in stage_us), key=lambda k: stage_us[k])
     t = stage_us[dom] * 1e-6
     wb, wf = work[dom]["bytes"], work[dom]["flops"]

@@ -218,6 +218,29 @@ moge_status_t moge_expert_down(const moge_shape_t* shape, const void* h, const i
                                int32_t e_hi, int64_t rows_cap, const void* w_down, void* out, hipStream_t stream);
 
 /*
+ * The routed experts' SwiGLU blocks and the always-on shared expert's block over
+ * all T tokens ([P4]: one shared expert), in the same launches: one persistent
+ * tile list per GEMM holds the tiles of both problems, interleaved evenly, so the
+ * shared expert's dense tiles run beside the routed experts' weight-streaming
+ * tiles and neither leaves a round of tiles half empty.  bf16 only.
+ *   Routed arguments as moge_expert_gate_up / moge_expert_down.
+ *   F_shared  the shared expert's width (F_shared % 8 == 0).
+ *   x_tiled   tiled, T rows x d columns (moge_dispatch's x_tiled).
+ *   ws_gate, ws_up: packed F_shared x d; ws_down: packed d x F_shared.
+ *   hs        tiled, T rows x F_shared columns (scratch: the shared expert's h).
+ *   out_shared [T][d] (dtype), row-major: the shared expert's output.
+ * Each output element is computed exactly as by the separate calls (bit-identical).
+ */
+moge_status_t moge_expert_gate_up_with_shared(const moge_shape_t* shape, int32_t F_shared, const void* x_perm,
+                                              const int32_t* offsets, int32_t e_lo, int32_t e_hi, int64_t rows_cap,
+                                              const void* w_gate, const void* w_up, void* h, const void* x_tiled,
+                                              const void* ws_gate, const void* ws_up, void* hs, hipStream_t stream);
+moge_status_t moge_expert_down_with_shared(const moge_shape_t* shape, int32_t F_shared, const void* h,
+                                           const int32_t* offsets, int32_t e_lo, int32_t e_hi, int64_t rows_cap,
+                                           const void* w_down, void* out, const void* hs, const void* ws_down,
+                                           void* out_shared, hipStream_t stream);
+
+/*
  * moge_combine -- gate-weighted sum of the expert outputs back in token order.
  *   y[t] = sum over slots s (in slot order) with inv[t][s] >= 0 of
  *          gate[t][s] * o[inv[t][s]]   (+ shared_out[t] when not NULL), in float32.

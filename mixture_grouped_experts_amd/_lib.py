@@ -32,8 +32,8 @@ STAGE_DISPATCH = 1
 
 EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_weight_elems",
            "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_grouped_ffn",
-           "moge_expert_gate_up", "moge_expert_down", "moge_combine", "moge_imbalance", "moge_version",
-           "moge_last_error")
+           "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
+           "moge_expert_down_with_shared", "moge_combine", "moge_imbalance", "moge_version", "moge_last_error")
 
 
 class Shape(ctypes.Structure):
@@ -83,6 +83,10 @@ _lib.moge_expert_gate_up.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, 
 _lib.moge_expert_gate_up.restype = ctypes.c_int
 _lib.moge_expert_down.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P]
 _lib.moge_expert_down.restype = ctypes.c_int
+_lib.moge_expert_gate_up_with_shared.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.moge_expert_gate_up_with_shared.restype = ctypes.c_int
+_lib.moge_expert_down_with_shared.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P]
+_lib.moge_expert_down_with_shared.restype = ctypes.c_int
 _lib.moge_combine.argtypes = [_SP, _P, _P, _P, _I64, _P, _P, _P]
 _lib.moge_combine.restype = ctypes.c_int
 _lib.moge_imbalance.argtypes = [_SP, _P, _P, _P, _P, _P]
@@ -231,6 +235,36 @@ def expert_down(shape: Shape, h, offsets, e_lo: int, e_hi: int, rows_cap: int, w
                                _ptr(w_down, "w_down", et, E * packed_weight_elems(d, F)),
                                _ptr(out, "out", et, rows_cap * d), _stream(stream))
     _check("moge_expert_down", st)
+
+
+def expert_gate_up_with_shared(shape: Shape, F_shared: int, x_perm, offsets, e_lo: int, e_hi: int, rows_cap: int,
+                               w_gate, w_up, h, x_tiled, ws_gate, ws_up, hs, stream=None) -> None:
+    T, d, F = shape.T, shape.d, shape.F
+    E = e_hi - e_lo
+    et = _elem_dtype(shape)
+    st = _lib.moge_expert_gate_up_with_shared(
+        ctypes.byref(shape), F_shared, _ptr(x_perm, "x_perm", et, tiled_elems(rows_cap, d)),
+        _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
+        _ptr(w_gate, "w_gate", et, E * packed_weight_elems(F, d)), _ptr(w_up, "w_up", et, E * packed_weight_elems(F, d)),
+        _ptr(h, "h", et, tiled_elems(rows_cap, F)), _ptr(x_tiled, "x_tiled", et, tiled_elems(T, d)),
+        _ptr(ws_gate, "ws_gate", et, packed_weight_elems(F_shared, d)),
+        _ptr(ws_up, "ws_up", et, packed_weight_elems(F_shared, d)), _ptr(hs, "hs", et, tiled_elems(T, F_shared)),
+        _stream(stream))
+    _check("moge_expert_gate_up_with_shared", st)
+
+
+def expert_down_with_shared(shape: Shape, F_shared: int, h, offsets, e_lo: int, e_hi: int, rows_cap: int, w_down, out,
+                            hs, ws_down, out_shared, stream=None) -> None:
+    T, d, F = shape.T, shape.d, shape.F
+    E = e_hi - e_lo
+    et = _elem_dtype(shape)
+    st = _lib.moge_expert_down_with_shared(
+        ctypes.byref(shape), F_shared, _ptr(h, "h", et, tiled_elems(rows_cap, F)),
+        _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
+        _ptr(w_down, "w_down", et, E * packed_weight_elems(d, F)), _ptr(out, "out", et, rows_cap * d),
+        _ptr(hs, "hs", et, tiled_elems(T, F_shared)), _ptr(ws_down, "ws_down", et, packed_weight_elems(d, F_shared)),
+        _ptr(out_shared, "out_shared", et, T * d), _stream(stream))
+    _check("moge_expert_down_with_shared", st)
 
 
 def combine(shape: Shape, o, inv, gate, rows_cap: int, shared_out, y, stream=None) -> None:

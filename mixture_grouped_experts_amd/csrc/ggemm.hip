@@ -268,46 +268,73 @@ __device__ __forceinline__ void expert_segments(const int32_t* __restrict__ offs
   }
 }
 
-// GEMM 1 (SWIGLU):  A = x_perm tiled [rows][KP], B0/B1 = packed gate/up [E][NOUT][KP],
-//                   C = h tiled [rows][NPAD] with NPAD = NOUT rounded up to 32.
-// GEMM 2:           A = h tiled [rows][KP], B0 = packed down [E][NOUT][KP], C = out [rows][NOUT].
+// Operands of one grouped GEMM problem.
+//   GEMM 1 (SWIGLU):  A = x_perm tiled [rows][KP], B0/B1 = packed gate/up [E][NOUT][KP],
+//                     C = h tiled [rows][NPAD] with NPAD = NOUT rounded up to 32.
+//   GEMM 2:           A = h tiled [rows][KP], B0 = packed down [E][NOUT][KP], C = out [rows][NOUT].
 // KP = the reduction length rounded up to 32 (zero padded in A and B).
+struct GemmOperands {
+  const uint16_t* A;
+  const uint16_t* B0;
+  const uint16_t* B1;
+  uint16_t* C;
+  int NOUT;
+  int KP;
+};
+
+// One persistent launch runs the tiles of two problems: the routed experts (problem
+// 0: segments from `offsets`) and, when rows1 > 0, one dense expert over rows1 rows
+// (problem 1: the always-on shared expert).  Their tile lists are interleaved evenly
+// (tile q of the launch is a shared-expert tile when floor((q+1) n1 / n) passes an
+// integer), so the dense, MFMA-bound tiles run beside the weight-streaming routed
+// tiles and no problem leaves a round of tiles half empty.
 template <bool SWIGLU>
-__global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                              const int32_t* __restrict__ offsets, int e_lo, int E,
-                                                              int64_t rows_cap, const uint16_t* __restrict__ B0,
-                                                              const uint16_t* __restrict__ B1, int NOUT, int KP,
-                                                              uint16_t* __restrict__ C) {
+__global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, const int32_t* __restrict__ offsets,
+                                                              int e_lo, int E, int64_t rows_cap, GemmOperands p1,
+                                                              int rows1) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int tp[kMaxExperts];     // inclusive prefix of tiles per expert
   __shared__ int erow[kMaxExperts];   // rows per expert, clipped to rows_cap
   __shared__ int pbase[kMaxExperts];  // first local row of each expert (16-row aligned)
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;  // output columns per tile
-  const int NT = (NOUT + BNO - 1) / BNO;
-  const int wrows = (int)round_up(NOUT, kWeightRowAlign);  // packed weight rows per expert
-  const int wbands = wrows / kTileRows;
-  const int NPAD = (int)round_up(NOUT, kTileCols);
-  const int nkf = KP / kTileCols;
+  const int NT0 = (p0.NOUT + BNO - 1) / BNO;
+  const int NT1 = (p1.NOUT + BNO - 1) / BNO;
   const int tid = threadIdx.x, wave = tid >> 6;
 
-  if (wave == 0) expert_segments(offsets, e_lo, E, rows_cap, kBM, NT, erow, pbase, tp);
+  if (wave == 0) expert_segments(offsets, e_lo, E, rows_cap, kBM, NT0, erow, pbase, tp);
   __syncthreads();
-  const int total = E > 0 ? tp[E - 1] : 0;
+  const int n0 = E > 0 ? tp[E - 1] : 0;
+  const int n1 = rows1 > 0 ? ((rows1 + kBM - 1) / kBM) * NT1 : 0;
+  const int total = n0 + n1;
 
   const int P = gridDim.x;  // multiple of 8
   const int per_xcd = P >> 3;
   const int slot = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
 
   for (int tile = slot; tile < total; tile += P) {
-    // expert of this tile: first i with tp[i] > tile
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (tp[mid] > tile) hi = mid; else lo = mid + 1;
+    // problem and tile index inside it
+    const int c0 = (int)((int64_t)tile * n1 / total), c1 = (int)((int64_t)(tile + 1) * n1 / total);
+    const bool dense = c1 > c0;
+    const GemmOperands& op = dense ? p1 : p0;
+    int ei = 0, q, erows, pb;
+    if (dense) {
+      q = c0;
+      erows = rows1;
+      pb = 0;
+    } else {
+      q = tile - c0;
+      // expert of this tile: first i with tp[i] > q
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (tp[mid] > q) hi = mid; else lo = mid + 1;
+      }
+      ei = lo;
+      q -= ei > 0 ? tp[ei - 1] : 0;
+      erows = erow[ei];
+      pb = pbase[ei];
     }
-    const int ei = lo;
-    const int q = tile - (ei > 0 ? tp[ei - 1] : 0);
-    const int erows = erow[ei];
+    const int NT = dense ? NT1 : NT0;
     const int MT = (erows + kBM - 1) / kBM;
     // grouped order: groups of kGroupM m-tiles; inside a group n outer, m inner
     const int gsz = kGroupM * NT;
@@ -315,18 +342,23 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(const uint16_t* __
     const int gm0 = g * kGroupM;
     const int gm = (MT - gm0) < kGroupM ? (MT - gm0) : kGroupM;
     const int mt = gm0 + qi % gm, nt = qi / gm;
-    const int64_t row0 = (int64_t)pbase[ei] + (int64_t)mt * kBM;  // multiple of 16
+    const int64_t row0 = (int64_t)pb + (int64_t)mt * kBM;  // multiple of 16
     const int mrows = (erows - mt * kBM) < kBM ? (erows - mt * kBM) : kBM;
-    const int n0 = nt * BNO;
-    const uint16_t* wb0 = B0 + (int64_t)ei * wrows * KP;
-    const uint16_t* wb1 = SWIGLU ? B1 + (int64_t)ei * wrows * KP : wb0;
+    const int ncol0 = nt * BNO;
+    const int wrows = (int)round_up(op.NOUT, kWeightRowAlign);  // packed weight rows per expert
+    const uint16_t* wb0 = op.B0 + (int64_t)ei * wrows * op.KP;
+    const uint16_t* wb1 = SWIGLU ? op.B1 + (int64_t)ei * wrows * op.KP : wb0;
     const int64_t mband0 = row0 / kTileRows;
+    const int wbands = wrows / kTileRows;
+    const int npad = (int)round_up(op.NOUT, kTileCols);
+    const int nkf = op.KP / kTileCols;
 
     // live row blocks of this wave (wave-uniform): block wm + 2t is live if it starts below mrows
     const int wm = wave & 1;
     const int nrb = (mrows + 31) / 32;
     const int nl = nrb > wm ? (nrb - wm + 1) / 2 : 0;
-#define MOGE_TILE(NLV) tile_compute<SWIGLU, NLV>(lds, A, mband0, wb0, wb1, wbands, nkf, mrows, row0, n0, NOUT, NPAD, C)
+#define MOGE_TILE(NLV)                                                                                          \
+  tile_compute<SWIGLU, NLV>(lds, op.A, mband0, wb0, wb1, wbands, nkf, mrows, row0, ncol0, op.NOUT, npad, op.C)
     switch (nl) {
       case 5: MOGE_TILE(5); break;
       case 4: MOGE_TILE(4); break;
@@ -411,22 +443,28 @@ static int device_cus() {
   return cus;
 }
 
+// rows1 = 0: routed problem only.
 template <bool SWIGLU>
-static moge_status_t launch_ggemm(const uint16_t* A, const int32_t* offsets, int e_lo, int E, int64_t rows_cap,
-                                  const uint16_t* B0, const uint16_t* B1, int NOUT, int KD, uint16_t* C,
-                                  hipStream_t stream) {
+static moge_status_t launch_ggemm(const GemmOperands& p0, const int32_t* offsets, int e_lo, int E, int64_t rows_cap,
+                                  const GemmOperands& p1, int rows1, hipStream_t stream) {
   moge_status_t st = raise_dynamic_lds(reinterpret_cast<const void*>(ggemm_bf16_kernel<SWIGLU>), kGemmLds,
                                        "ggemm_bf16_kernel");
   if (st != MOGE_OK) return st;
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
-  const int64_t NT = (NOUT + BNO - 1) / BNO;
-  const int64_t upper = ((rows_cap + kBM - 1) / kBM + E) * NT;  // >= live tiles
-  int64_t grid = device_cus();                                   // one 144 KiB-LDS workgroup per CU
+  const int64_t upper = ((rows_cap + kBM - 1) / kBM + E) * ((p0.NOUT + BNO - 1) / BNO) +
+                        ((int64_t)rows1 + kBM - 1) / kBM * ((p1.NOUT + BNO - 1) / BNO);  // >= live tiles
+  int64_t grid = device_cus();  // one 144 KiB-LDS workgroup per CU
   if (upper < grid) grid = upper;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL(ggemm_bf16_kernel<SWIGLU>, dim3((unsigned)grid), dim3(kThreads), kGemmLds, stream, A, offsets, e_lo,
-                     E, rows_cap, B0, B1, NOUT, (int)round_up(KD, kTileCols), C);
+  hipLaunchKernelGGL(ggemm_bf16_kernel<SWIGLU>, dim3((unsigned)grid), dim3(kThreads), kGemmLds, stream, p0, offsets,
+                     e_lo, E, rows_cap, p1, rows1);
   return check_launch(SWIGLU ? "ggemm_bf16_kernel<gate_up>" : "ggemm_bf16_kernel<down>");
+}
+
+static GemmOperands operands(const void* A, const void* B0, const void* B1, void* C, int NOUT, int KD) {
+  return GemmOperands{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
+                      static_cast<const uint16_t*>(B1), static_cast<uint16_t*>(C), NOUT,
+                      (int)round_up(KD, kTileCols)};
 }
 
 }  // namespace moge
@@ -457,9 +495,9 @@ extern "C" moge_status_t moge_expert_gate_up(const moge_shape_t* shape, const vo
     return fail(MOGE_ERR_NULL, "x_perm, offsets, w_gate, w_up and h are required");
   const moge_shape_t& s = *shape;
   if (s.dtype == MOGE_BF16) {
-    st = launch_ggemm<true>(static_cast<const uint16_t*>(x_perm), offsets, e_lo, e_hi - e_lo, rows_cap,
-                            static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up), s.F, s.d,
-                            static_cast<uint16_t*>(h), stream);
+    const GemmOperands none{};
+    st = launch_ggemm<true>(operands(x_perm, w_gate, w_up, h, s.F, s.d), offsets, e_lo, e_hi - e_lo, rows_cap, none,
+                            0, stream);
   } else {
     hipLaunchKernelGGL(ffn_f32_gateup_kernel, dim3((unsigned)grid_1d(rows_cap * round_up(s.F, kTileCols))), dim3(256),
                        0, stream, static_cast<const float*>(x_perm), offsets, e_lo, e_hi - e_lo, rows_cap,
@@ -478,9 +516,9 @@ extern "C" moge_status_t moge_expert_down(const moge_shape_t* shape, const void*
   if (!h || !offsets || !w_down || !out) return fail(MOGE_ERR_NULL, "h, offsets, w_down and out are required");
   const moge_shape_t& s = *shape;
   if (s.dtype == MOGE_BF16) {
-    st = launch_ggemm<false>(static_cast<const uint16_t*>(h), offsets, e_lo, e_hi - e_lo, rows_cap,
-                             static_cast<const uint16_t*>(w_down), nullptr, s.d, s.F, static_cast<uint16_t*>(out),
-                             stream);
+    const GemmOperands none{};
+    st = launch_ggemm<false>(operands(h, w_down, nullptr, out, s.d, s.F), offsets, e_lo, e_hi - e_lo, rows_cap, none,
+                             0, stream);
   } else {
     hipLaunchKernelGGL(ffn_f32_down_kernel, dim3((unsigned)grid_1d(rows_cap * s.d)), dim3(256), 0, stream,
                        static_cast<const float*>(h), offsets, e_lo, e_hi - e_lo, rows_cap,
@@ -497,4 +535,45 @@ extern "C" moge_status_t moge_grouped_ffn(const moge_shape_t* shape, const void*
   moge_status_t st = moge_expert_gate_up(shape, x_perm, offsets, e_lo, e_hi, rows_cap, w_gate, w_up, h, stream);
   if (st != MOGE_OK) return st;
   return moge_expert_down(shape, h, offsets, e_lo, e_hi, rows_cap, w_down, out, stream);
+}
+
+// ---- routed experts and the shared expert in the same two launches
+static moge_status_t shared_checks(const moge_shape_t* shape, int32_t F_shared, int32_t e_lo, int32_t e_hi,
+                                   int64_t rows_cap) {
+  moge_status_t st = ffn_common_checks(shape, e_lo, e_hi, rows_cap);
+  if (st != MOGE_OK) return st;
+  if (F_shared < 8 || F_shared % 8 != 0) return fail(MOGE_ERR_SHAPE, "F_shared must be a positive multiple of 8");
+  if (shape->dtype != MOGE_BF16)
+    return fail(MOGE_ERR_DTYPE, "the fused shared-expert calls are bf16 only; float32 uses moge_grouped_ffn twice");
+  return MOGE_OK;
+}
+
+extern "C" moge_status_t moge_expert_gate_up_with_shared(const moge_shape_t* shape, int32_t F_shared,
+                                                         const void* x_perm, const int32_t* offsets, int32_t e_lo,
+                                                         int32_t e_hi, int64_t rows_cap, const void* w_gate,
+                                                         const void* w_up, void* h, const void* x_tiled,
+                                                         const void* ws_gate, const void* ws_up, void* hs,
+                                                         hipStream_t stream) {
+  moge_status_t st = shared_checks(shape, F_shared, e_lo, e_hi, rows_cap);
+  if (st != MOGE_OK) return st;
+  if (!x_perm || !offsets || !w_gate || !w_up || !h || !x_tiled || !ws_gate || !ws_up || !hs)
+    return fail(MOGE_ERR_NULL, "every operand is required");
+  const moge_shape_t& s = *shape;
+  st = launch_ggemm<true>(operands(x_perm, w_gate, w_up, h, s.F, s.d), offsets, e_lo, e_hi - e_lo, rows_cap,
+                          operands(x_tiled, ws_gate, ws_up, hs, F_shared, s.d), s.T, stream);
+  return st == MOGE_OK ? ok() : st;
+}
+
+extern "C" moge_status_t moge_expert_down_with_shared(const moge_shape_t* shape, int32_t F_shared, const void* h,
+                                                      const int32_t* offsets, int32_t e_lo, int32_t e_hi,
+                                                      int64_t rows_cap, const void* w_down, void* out, const void* hs,
+                                                      const void* ws_down, void* out_shared, hipStream_t stream) {
+  moge_status_t st = shared_checks(shape, F_shared, e_lo, e_hi, rows_cap);
+  if (st != MOGE_OK) return st;
+  if (!h || !offsets || !w_down || !out || !hs || !ws_down || !out_shared)
+    return fail(MOGE_ERR_NULL, "every operand is required");
+  const moge_shape_t& s = *shape;
+  st = launch_ggemm<false>(operands(h, w_down, nullptr, out, s.d, s.F), offsets, e_lo, e_hi - e_lo, rows_cap,
+                           operands(hs, ws_down, nullptr, out_shared, s.d, F_shared), s.T, stream);
+  return st == MOGE_OK ? ok() : st;
 }

@@ -6,11 +6,14 @@ reportify.cn for the shared expert):
   1. moge_route GROUPED   scores (stored), softmax over all N, top-K' in every group
   2. moge_dispatch        counts, offsets, stable permutation, rows of [e_lo, e_hi)
                           (tiled), and the tiled copy of x for the shared expert
-  3. moge_grouped_ffn     SwiGLU experts on their row segments
-  4. moge_grouped_ffn     the always-on shared expert (one-expert shape), if any
-  5. moge_combine         gate-weighted sum (+ shared output) -> y (float32)
-  6. moge_imbalance       per-group load and imbalance score (0 by construction)
-  7. moge_route GLOBAL    the conventional top-K comparator from the stored scores,
+  3. moge_expert_gate_up_with_shared, moge_expert_down_with_shared
+                          SwiGLU experts on their row segments and the always-on shared
+                          expert over all tokens, in the same two launches (bf16); float32
+                          shapes use moge_expert_gate_up / _down and a one-expert
+                          moge_grouped_ffn for the shared expert
+  4. moge_combine         gate-weighted sum (+ shared output) -> y (float32)
+  5. moge_imbalance       per-group load and imbalance score (0 by construction)
+  6. moge_route GLOBAL    the conventional top-K comparator from the stored scores,
      moge_dispatch        its counts only, and moge_imbalance of that load.
 
 Buffers are allocated once here (torch supplies device memory); ``forward`` only issues
@@ -37,6 +40,7 @@ class MoGELayer:
         self.K = M * Kp
         self.e_lo, self.e_hi = e_lo, (N if e_hi is None else e_hi)
         self.F_shared = F_shared
+        self.fuse_shared = dtype == "bf16"  # the fused routed + shared launches are bf16 only
         self.comparator = comparator
         self.routing_only = F == 0
         dev = torch.device(device)
@@ -107,15 +111,25 @@ class MoGELayer:
                        self.offsets, self.inv, self.perm, self.x_perm, self.ws,
                        self.x_tiled if self.F_shared else None, stream)
             mk("dispatch")
-            L.expert_gate_up(s, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate, w_up, self.h,
-                             stream)
-            mk("gate_up")
-            L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o, stream)
-            mk("down")
-            if self.F_shared:
-                L.grouped_ffn(self.sshape, self.x_tiled, self.soffsets, 0, 1, self.T, shared[0], shared[1],
-                              shared[2], self.sh, self.so, stream)
-                mk("shared")
+            if self.F_shared and self.fuse_shared:
+                # routed and shared experts in the same two launches
+                L.expert_gate_up_with_shared(s, self.F_shared, self.x_perm, self.offsets, self.e_lo, self.e_hi,
+                                             self.rows_cap, w_gate, w_up, self.h, self.x_tiled, shared[0], shared[1],
+                                             self.sh, stream)
+                mk("gate_up")
+                L.expert_down_with_shared(s, self.F_shared, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap,
+                                          w_down, self.o, self.sh, shared[2], self.so, stream)
+                mk("down")
+            else:
+                L.expert_gate_up(s, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate, w_up,
+                                 self.h, stream)
+                mk("gate_up")
+                L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o, stream)
+                mk("down")
+                if self.F_shared:
+                    L.grouped_ffn(self.sshape, self.x_tiled, self.soffsets, 0, 1, self.T, shared[0], shared[1],
+                                  shared[2], self.sh, self.so, stream)
+                    mk("shared")
             L.combine(s, self.o, self.inv, self.gate, self.rows_cap, self.so if self.F_shared else None, self.y,
                       stream)
             mk("combine")

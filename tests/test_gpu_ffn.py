@@ -129,3 +129,42 @@ def test_grouped_ffn_expert_range_and_shared_form(gpu):
     ref = np.stack([oracle.ffn_row(hi.x_rows([t])[0], *hsh) for t in toks])
     ok, err, bound = H.tol_ok(ob[toks].float().cpu().numpy(), ref)
     assert ok, (err, bound)
+
+
+def test_routed_and_shared_in_one_launch_bitexact(gpu):
+    # the fused launches compute every element exactly as the separate calls do
+    w = W.variant(MID, F_shared=136, std_shared_down=0.02, T=333)
+    dv = H.device_inputs(w)
+    hi = H.HostInputs(w)
+    idx, _, _ = oracle.route(H.oracle_logits_all(hi), w.M, w.Kp, "grouped")
+    s = moge.Shape(w.T, w.d, w.N, w.M, w.Kp, w.F, moge.BF16)
+    cap = moge.rows_bound(s, moge.ROUTE_GROUPED, 0, w.N)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    counts, offsets = torch.empty(w.N, **i32), torch.empty(w.N + 1, **i32)
+    inv, perm = torch.empty(w.T, w.K, **i32), torch.empty(cap, **i32)
+    xp, xt = torch.empty(moge.tiled_elems(cap, w.d), **bf), torch.empty(moge.tiled_elems(w.T, w.d), **bf)
+    ws = torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda")
+    moge.dispatch(s, moge.ROUTE_GROUPED, torch.from_numpy(idx).cuda(), dv.x, 0, w.N, cap, counts, offsets, inv, perm,
+                  xp, ws, x_tiled=xt)
+    pg, pu, pd = _pack(moge.BF16, dv.w_gate), _pack(moge.BF16, dv.w_up), _pack(moge.BF16, dv.w_down)
+    sg, su, sd = (_pack(moge.BF16, m.unsqueeze(0)) for m in dv.shared)
+    Fs = w.F_shared
+
+    def bufs():
+        return (torch.zeros(moge.tiled_elems(cap, w.F), **bf), torch.zeros(cap, w.d, **bf),
+                torch.zeros(moge.tiled_elems(w.T, Fs), **bf), torch.zeros(w.T, w.d, **bf))
+    h1, o1, hs1, so1 = bufs()
+    moge.expert_gate_up(s, xp, offsets, 0, w.N, cap, pg, pu, h1)
+    moge.expert_down(s, h1, offsets, 0, w.N, cap, pd, o1)
+    moge.grouped_ffn(moge.Shape(w.T, w.d, 1, 1, 1, Fs, moge.BF16), xt,
+                     torch.tensor([0, w.T], **i32), 0, 1, w.T, sg, su, sd, hs1, so1)
+    h2, o2, hs2, so2 = bufs()
+    moge.expert_gate_up_with_shared(s, Fs, xp, offsets, 0, w.N, cap, pg, pu, h2, xt, sg, su, hs2)
+    moge.expert_down_with_shared(s, Fs, h2, offsets, 0, w.N, cap, pd, o2, hs2, sd, so2)
+    torch.cuda.synchronize()
+    P = H.segment_bases(counts.cpu().numpy(), 0, w.N)
+    live = torch.from_numpy(_live_rows(w, counts.cpu().numpy(), P)).long().cuda()
+    assert torch.equal(H.untile_rows(h1, cap, w.F)[live], H.untile_rows(h2, cap, w.F)[live])
+    assert torch.equal(o1[live], o2[live])
+    assert torch.equal(hs1, hs2) and torch.equal(so1, so2)
