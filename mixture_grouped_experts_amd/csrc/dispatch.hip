@@ -3,16 +3,17 @@
 // gets a row; Pangu Ultra MoE digests on reportify.cn, dropless training).
 //
 // Four launches, no atomics on anything that decides an order:
-//   1. dispatch_hist_kernel   one workgroup per block of 256 tokens counts its
+//   1. dispatch_hist_kernel   one workgroup per block of 64 tokens counts its
 //                             assignments per expert (LDS integer histogram).
 //   2. dispatch_scan_kernel   one workgroup per expert scans that expert's block
 //                             counts -> per-block starting rows and counts[e].
-//   3. dispatch_permute_kernel one workgroup per token block: offsets from counts,
-//                             then per wave (64 tokens, one per lane) a ballot
-//                             loop over the distinct experts of its tokens gives
-//                             every (token, slot) its row = block/wave base + number
+//   3. dispatch_permute_kernel one workgroup per token block (one token per lane):
+//                             offsets from counts, then wave w takes the experts
+//                             e = w (mod 4): a ballot loop over its distinct experts
+//                             gives every (token, slot) its row = block base + number
 //                             of lower lanes that chose the same expert, so rows of
 //                             an expert stay in ascending token order -> inv, perm.
+//                             The four waves work on disjoint experts at once.
 //   4. dispatch_copy_kernel   one wave per token reads its row from HBM once and
 //                             writes it to all of its slots' rows (16-byte stores)
 //                             in the tiled layout the expert GEMMs read, plus the
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int64_t nb, const in
   if (threadIdx.x == 0) counts[e] = running;
 }
 
-// Dynamic LDS: keys[kTB][KS] | rows[kTB][KS] | offs[N+1] | base[N] | hist[4][N] | pbase[N+1]
+// Dynamic LDS: keys[kTB][KS] | offs[N+1] | base[N] | pbase[N+1]
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     int64_t T, int K, int N, int64_t nb, const int32_t* __restrict__ idx, int e_lo, int e_hi, int64_t rows_cap,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ bprefix, int32_t* __restrict__ offsets_out,
@@ -71,11 +72,9 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
   extern __shared__ int lds[];
   const int KS = K + 1;  // odd row stride: lanes of a wave hit distinct banks
   int* keys = lds;
-  int* rows = keys + kTB * KS;
-  int* offs = rows + kTB * KS;
+  int* offs = keys + kTB * KS;
   int* base = offs + (N + 1);
-  int* hist = base + N;  // [4][N]
-  int* pbase = hist + 4 * N;  // P(e): first local row of expert e (16-row aligned segments)
+  int* pbase = base + N;  // P(e): first local row of expert e (16-row aligned segments)
   __shared__ int scratch[4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -95,7 +94,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
       if (e < N) offsets_out[e] = ex;
       if (e == 0) offsets_out[N] = tot;
     }
-    if (e < N) base[e] = ex + bprefix[(int64_t)e * nb + b];
+    if (e < N) base[e] = bprefix[(int64_t)e * nb + b];  // rows of e in earlier blocks
   }
   if (!inv) return;
   {
@@ -112,8 +111,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
         if ((int64_t)r < rows_cap) perm[r] = -1;
     }
   }
-  // stage this block's expert ids; per-wave histograms
-  for (int i = threadIdx.x; i < 4 * N; i += 256) hist[i] = 0;
+  // stage this block's expert ids (token tl = lane); slots of other experts get inv = -1
   for (int i = threadIdx.x; i < kTB * K; i += 256) {
     const int tl = i / K, s = i - tl * K;
     const int64_t t = t0 + tl;
@@ -121,37 +119,21 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     if (t < T) {
       e = idx[t * K + s];
       if ((unsigned)e >= (unsigned)N) e = -1;
+      if (e < e_lo || e >= e_hi) inv[t * K + s] = -1;
     }
     keys[tl * KS + s] = e;
-    rows[tl * KS + s] = -1;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kTB * K; i += 256) {
-    const int tl = i / K, s = i - tl * K;
-    const int e = keys[tl * KS + s];
-    if (e >= 0) atomicAdd(&hist[(tl >> 6) * N + e], 1);
-  }
-  __syncthreads();
-  // per-wave starting row of every expert: block base + counts of lower waves
-  // (one thread per expert rewrites that expert's four entries in place)
-  for (int e = threadIdx.x; e < N; e += 256) {
-    int s = base[e];
-    for (int w = 0; w < 4; ++w) {
-      const int c = hist[w * N + e];
-      hist[w * N + e] = s;
-      s += c;
-    }
   }
   __syncthreads();
 
-  // rank: one distinct expert per iteration, all of its occurrences at once
+  // wave w: experts e in [e_lo, e_hi) with e % 4 == w, one distinct expert per iteration
   {
-    const int tl = wave * 64 + lane;
-    const int* my = keys + tl * KS;
+    const int64_t t = t0 + lane;
+    const int* my = keys + lane * KS;
     uint64_t pending = 0;
-    for (int s = 0; s < K; ++s)
-      if (my[s] >= 0) pending |= (1ull << s);
-    const int* wbase = hist + wave * N;
+    for (int s = 0; s < K; ++s) {
+      const int e = my[s];
+      if (e >= e_lo && e < e_hi && (e & 3) == wave) pending |= (1ull << s);
+    }
     while (true) {
       const uint64_t pm = __ballot(pending != 0);
       if (pm == 0) break;
@@ -163,27 +145,14 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
         if (((pending >> s) & 1ull) && my[s] == e) slot = s;
       const uint64_t m = __ballot(slot >= 0);
       if (slot >= 0) {
-        rows[tl * KS + slot] = wbase[e] + lanes_below(m);
+        int r = pbase[e] + base[e] + lanes_below(m);  // local row in the padded numbering
+        if ((int64_t)r >= rows_cap || r < 0) r = -1;
+        inv[t * K + slot] = r;
+        if (r >= 0) perm[r] = (int32_t)t;
         pending &= ~(1ull << slot);
       }
+      // (a token holds an expert at most once, so expert e is done in this one pass)
     }
-  }
-  __syncthreads();
-
-  // inv / perm: dense row (offsets numbering) -> local row of the padded segment
-  for (int i = threadIdx.x; i < kTB * K; i += 256) {
-    const int tl = i / K, s = i - tl * K;
-    const int64_t t = t0 + tl;
-    if (t >= T) continue;
-    const int e = keys[tl * KS + s];
-    int r = -1;
-    if (e >= e_lo && e < e_hi) {
-      r = rows[tl * KS + s] - offs[e] + pbase[e];
-      if ((int64_t)r >= rows_cap || r < 0) r = -1;
-    }
-    rows[tl * KS + s] = r;
-    inv[t * K + s] = r;
-    if (r >= 0) perm[r] = (int32_t)t;
   }
 }
 
@@ -266,8 +235,7 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3((unsigned)s.N), dim3(256), 0, stream, nb, bcount, bprefix, counts);
   if ((st = check_launch("dispatch_scan_kernel")) != MOGE_OK) return st;
 
-  const size_t lds =
-      sizeof(int) * ((size_t)2 * kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + 4 * (size_t)s.N + (size_t)(s.N + 1));
+  const size_t lds = sizeof(int) * ((size_t)kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + (size_t)(s.N + 1));
   if (lds > 64 * 1024) {
     st = raise_dynamic_lds(reinterpret_cast<const void*>(dispatch_permute_kernel), lds, "dispatch_permute_kernel");
     if (st != MOGE_OK) return st;

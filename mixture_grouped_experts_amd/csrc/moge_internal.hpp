@@ -37,7 +37,7 @@ __host__ __device__ __forceinline__ int64_t tiled_index(int64_t r, int64_t c, in
 }
 
 // Dispatch geometry (shared by moge_workspace_size and the dispatch kernels).
-constexpr int kDispatchTokens = 256;  // tokens per dispatch workgroup
+constexpr int kDispatchTokens = 64;   // tokens per dispatch workgroup (one per lane)
 inline int64_t dispatch_blocks(int64_t T) { return (T + kDispatchTokens - 1) / kDispatchTokens; }
 
 // ---------------------------------------------------------------- device side

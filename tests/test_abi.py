@@ -56,7 +56,7 @@ def test_rows_bound_and_workspace():
     assert moge.rows_bound(s, moge.ROUTE_GLOBAL, 0, 8) == 100 * 8 + 15 * 8
     assert moge.rows_bound(s, moge.ROUTE_GLOBAL, 0, 64) == 100 * 16 + 15 * 64
     assert moge.rows_bound(s, 5, 0, 8) == -1 and moge.rows_bound(s, 0, 8, 8) == -1
-    assert moge.workspace_size(S(T=65536, N=64)) == 2 * 64 * 256 * 4
+    assert moge.workspace_size(S(T=65536, N=64)) == 2 * 64 * 1024 * 4   # blocks of 64 tokens
     assert moge.workspace_size(S(T=1, N=8)) == 2 * 8 * 1 * 4
     assert moge.workspace_size(S(T=0)) == 2 ** 64 - 1
 
