@@ -220,9 +220,9 @@ moge_status_t moge_expert_down(const moge_shape_t* shape, const void* h, const i
 /*
  * The routed experts' SwiGLU blocks and the always-on shared expert's block over
  * all T tokens ([P4]: one shared expert), in the same launches: one persistent
- * tile list per GEMM holds the tiles of both problems, interleaved evenly, so the
- * shared expert's dense tiles run beside the routed experts' weight-streaming
- * tiles and neither leaves a round of tiles half empty.  bf16 only.
+ * tile list per GEMM holds the routed tiles followed by the shared expert's, so
+ * the shared tiles fill the last round of routed tiles instead of running as
+ * launches of their own with half-empty rounds.  bf16 only.
  *   Routed arguments as moge_expert_gate_up / moge_expert_down.
  *   F_shared  the shared expert's width (F_shared % 8 == 0).
  *   x_tiled   tiled, T rows x d columns (moge_dispatch's x_tiled).

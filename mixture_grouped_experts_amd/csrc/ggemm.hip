@@ -284,10 +284,12 @@ struct GemmOperands {
 
 // One persistent launch runs the tiles of two problems: the routed experts (problem
 // 0: segments from `offsets`) and, when rows1 > 0, one dense expert over rows1 rows
-// (problem 1: the always-on shared expert).  Their tile lists are interleaved evenly
-// (tile q of the launch is a shared-expert tile when floor((q+1) n1 / n) passes an
-// integer), so the dense, MFMA-bound tiles run beside the weight-streaming routed
-// tiles and no problem leaves a round of tiles half empty.
+// (problem 1: the always-on shared expert), whose tiles follow the routed ones in the
+// same list, so they fill the last, partly empty round of routed tiles instead of
+// running as separate launches with half-empty rounds of their own.  (Spreading them
+// evenly through the list was measured to cost 50% more HBM reads: tiles of unequal
+// length let the workgroups drift apart, so the 16 column tiles of a routed expert no
+// longer run together and its row panel leaves L2 between uses.)
 template <bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, const int32_t* __restrict__ offsets,
                                                               int e_lo, int E, int64_t rows_cap, GemmOperands p1,
@@ -313,16 +315,15 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
 
   for (int tile = slot; tile < total; tile += P) {
     // problem and tile index inside it
-    const int c0 = (int)((int64_t)tile * n1 / total), c1 = (int)((int64_t)(tile + 1) * n1 / total);
-    const bool dense = c1 > c0;
+    const bool dense = tile >= n0;
     const GemmOperands& op = dense ? p1 : p0;
     int ei = 0, q, erows, pb;
     if (dense) {
-      q = c0;
+      q = tile - n0;
       erows = rows1;
       pb = 0;
     } else {
-      q = tile - c0;
+      q = tile;
       // expert of this tile: first i with tp[i] > q
       int lo = 0, hi = E - 1;
       while (lo < hi) {
