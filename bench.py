@@ -155,12 +155,16 @@ def cpu_baseline(w, seconds: float):
             oracle.combine_rows(x, idx, gate, w.e_lo, w.e_hi, hi.expert, hi.shared())
         return time.perf_counter() - t0
 
-    probe = H.sample_tokens(w.T, 2, seed=7)[:2]
+    # size the sample to about `seconds` of oracle time: a small probe, then one correction
+    probe = H.sample_tokens(w.T, 8, seed=7)[:8]
     dt = run(probe)
-    n = int(max(2, min(w.T, seconds / max(dt / len(probe), 1e-9))))
-    n = min(n, 4096)
+    n = int(max(2, min(w.T, 4096, seconds / max(dt / len(probe), 1e-9))))
     tokens = H.sample_tokens(w.T, n, seed=11)[:n]
     dt = run(tokens)
+    if dt < 0.6 * seconds and n < min(w.T, 4096):
+        n = int(min(w.T, 4096, n * seconds / max(dt, 1e-9)))
+        tokens = H.sample_tokens(w.T, n, seed=11)[:n]
+        dt = run(tokens)
     return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(tokens)} of {w.T} tokens (seeded sample), full layer per token in binary64; "
                       f"{dt:.1f} s"}

@@ -14,7 +14,8 @@ reportify.cn for the shared expert):
   4. moge_combine         gate-weighted sum (+ shared output) -> y (float32)
   5. moge_imbalance       per-group load and imbalance score (0 by construction)
   6. moge_route GLOBAL    the conventional top-K comparator from the stored scores,
-     moge_dispatch        its counts only, and moge_imbalance of that load.
+     moge_dispatch        its counts only, and moge_imbalance of that load -- with expert
+                          FFNs, on a second stream right after step 1, overlapping steps 2-5.
 
 Buffers are allocated once here (torch supplies device memory); ``forward`` only issues
 library calls, so it allocates nothing and does not synchronise.  Expert weights are
@@ -57,6 +58,10 @@ class MoGELayer:
         self.is_raw = torch.empty(1, **i32)
         self.is_norm = torch.empty(1, dtype=torch.float64, device=dev)
         if comparator:
+            # the comparator only needs the stored scores: with expert FFNs to hide behind it
+            # runs on a second stream (default priority), with a workspace of its own
+            self.side = torch.cuda.Stream(device=dev) if F else None
+            self.gws = torch.empty(max(L.workspace_size(self.shape), 4), dtype=torch.uint8, device=dev)
             self.gidx = torch.empty(T, K, **i32)
             self.ggate = torch.empty(T, K, **f32)
             self.gcounts = torch.empty(N, **i32)
@@ -100,8 +105,19 @@ class MoGELayer:
         the caller may record a stream event there)."""
         s = self.shape
         mk = mark if mark is not None else (lambda name: None)
-        L.route(s, L.ROUTE_GROUPED, x, w_router, bias, self.logits, self.idx, self.gate, stream)
+        main = stream if stream is not None else torch.cuda.current_stream()
+        L.route(s, L.ROUTE_GROUPED, x, w_router, bias, self.logits, self.idx, self.gate, main)
         mk("route")
+        def comparator(on):
+            # conventional global top-K on the same scores, its loads and imbalance
+            L.route(s, L.ROUTE_GLOBAL, None, None, None, self.logits, self.gidx, self.ggate, on)
+            L.dispatch(s, L.ROUTE_GLOBAL, self.gidx, None, 0, self.N, 0, self.gcounts, self.goffsets, None, None,
+                       None, self.gws, stream=on)
+            L.imbalance(s, self.gcounts, self.g_group_load, self.g_is_raw, self.g_is_norm, on)
+        if self.comparator and self.side is not None:
+            self.side.wait_stream(main)  # after the scores exist; joined back before the step ends
+            comparator(self.side)
+        stream = main
         if self.routing_only:
             L.dispatch(s, L.ROUTE_GROUPED, self.idx, None, 0, self.N, 0, self.counts, self.offsets, None, None, None,
                        self.ws, stream=stream)
@@ -136,9 +152,9 @@ class MoGELayer:
         L.imbalance(s, self.counts, self.group_load, self.is_raw, self.is_norm, stream)
         mk("imbalance")
         if self.comparator:
-            L.route(s, L.ROUTE_GLOBAL, None, None, None, self.logits, self.gidx, self.ggate, stream)
-            L.dispatch(s, L.ROUTE_GLOBAL, self.gidx, None, 0, self.N, 0, self.gcounts, self.goffsets, None, None,
-                       None, self.ws, stream=stream)
-            L.imbalance(s, self.gcounts, self.g_group_load, self.g_is_raw, self.g_is_norm, stream)
+            if self.side is not None:
+                main.wait_stream(self.side)  # (the mark then times the part not hidden by the layer)
+            else:
+                comparator(main)
             mk("global_comparator")
         return None if self.routing_only else self.y
