@@ -260,6 +260,20 @@ moge_status_t moge_combine(const moge_shape_t* shape, const void* o, const int32
 moge_status_t moge_imbalance(const moge_shape_t* shape, const int32_t* counts, int32_t* group_load,
                              int32_t* is_raw, double* is_norm, hipStream_t stream);
 
+/*
+ * moge_imbalance_batches -- the imbalance score of each of B batches routed in one
+ * call: the setting in which [P1] (section 1) compares the routers by Monte-Carlo
+ * simulation.  Batch b holds tokens b*Tb .. (b+1)*Tb - 1 of idx.
+ *   shape   the shape of the routing call: T = B * Tb tokens, N, M, k_per_group
+ *           (idx has K = M*k_per_group slots per token in both route modes).
+ *   idx     [T][K] int32 (device) from moge_route; ids outside [0, N) are ignored.
+ *   tokens_per_batch  Tb, must divide T.
+ *   group_load [B][M] int32 out: assignments per group (group(e) = e / (N/M)).
+ *   is_raw  [B] int32 out: busiest minus idlest group of the batch.
+ */
+moge_status_t moge_imbalance_batches(const moge_shape_t* shape, const int32_t* idx, int64_t tokens_per_batch,
+                                     int32_t* group_load, int32_t* is_raw, hipStream_t stream);
+
 /* Library version string and the calling thread's last error message. */
 const char* moge_version(void);
 const char* moge_last_error(void);

@@ -33,7 +33,8 @@ STAGE_DISPATCH = 1
 EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_weight_elems",
            "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_grouped_ffn",
            "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
-           "moge_expert_down_with_shared", "moge_combine", "moge_imbalance", "moge_version", "moge_last_error")
+           "moge_expert_down_with_shared", "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_version",
+           "moge_last_error")
 
 
 class Shape(ctypes.Structure):
@@ -91,6 +92,8 @@ _lib.moge_combine.argtypes = [_SP, _P, _P, _P, _I64, _P, _P, _P]
 _lib.moge_combine.restype = ctypes.c_int
 _lib.moge_imbalance.argtypes = [_SP, _P, _P, _P, _P, _P]
 _lib.moge_imbalance.restype = ctypes.c_int
+_lib.moge_imbalance_batches.argtypes = [_SP, _P, _I64, _P, _P, _P]
+_lib.moge_imbalance_batches.restype = ctypes.c_int
 _lib.moge_version.argtypes = []
 _lib.moge_version.restype = ctypes.c_char_p
 _lib.moge_last_error.argtypes = []
@@ -283,3 +286,11 @@ def imbalance(shape: Shape, counts, group_load, is_raw, is_norm, stream=None) ->
                              _ptr(is_raw, "is_raw", torch.int32, 1), _ptr(is_norm, "is_norm", torch.float64, 1),
                              _stream(stream))
     _check("moge_imbalance", st)
+
+
+def imbalance_batches(shape: Shape, idx, tokens_per_batch: int, group_load, is_raw, stream=None) -> None:
+    B = shape.T // tokens_per_batch if tokens_per_batch > 0 else 0
+    st = _lib.moge_imbalance_batches(ctypes.byref(shape), _ptr(idx, "idx", torch.int32, shape.T * shape.K),
+                                     tokens_per_batch, _ptr(group_load, "group_load", torch.int32, B * shape.M),
+                                     _ptr(is_raw, "is_raw", torch.int32, B), _stream(stream))
+    _check("moge_imbalance_batches", st)

@@ -128,6 +128,10 @@ def test_null_and_argument_errors_before_any_launch():
     lib.moge_combine.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P]
     assert lib.moge_combine(sp, fake, fake, None, 64, None, fake, None) == 3
     assert lib.moge_combine(sp, fake, fake, fake, 0, None, fake, None) == 7
+    lib.moge_imbalance_batches.argtypes = [P, P, ctypes.c_int64, P, P, P]
+    assert lib.moge_imbalance_batches(sp, fake, 0, fake, fake, None) == 1       # tokens per batch < 1
+    assert lib.moge_imbalance_batches(sp, fake, 48, fake, fake, None) == 1      # does not divide T = 64
+    assert lib.moge_imbalance_batches(sp, None, 16, fake, fake, None) == 3
     lib.moge_imbalance.argtypes = [P] * 6
     assert lib.moge_imbalance(sp, fake, fake, None, fake, None) == 3
     assert lib.moge_imbalance(ctypes.byref(S(M=3)), fake, fake, fake, fake, None) == 2
