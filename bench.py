@@ -13,7 +13,7 @@ Prints ONE JSON line.  Per-call times come from HIP events recorded on the strea
 on, between consecutive library calls inside the timed steps.  The dominant kernel's roofline uses
 its algorithmic bytes (weights + activations it must move) and FLOPs per launch.
 
-    python bench.py [--steps K] [--warmup W] [--workload ultra|group0|decode|routing|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload ultra|group0|decode|routing|tiny|pro]
                     [--no-cpu-baseline] [--cpu-seconds S]
 """
 from __future__ import annotations
@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="ultra", choices=["ultra", "group0", "decode", "routing", "tiny"])
+    p.add_argument("--workload", default="ultra", choices=["ultra", "group0", "decode", "routing", "tiny", "pro"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -188,7 +188,8 @@ def main():
     from synth import workloads as W
     from tests import moge_harness as H
 
-    w = {"ultra": W.ultra, "group0": W.group0, "decode": W.decode, "routing": W.routing, "tiny": W.tiny}[
+    w = {"ultra": W.ultra, "group0": W.group0, "decode": W.decode, "routing": W.routing, "tiny": W.tiny,
+         "pro": W.pro}[
         args.workload]()
     torch.cuda.set_device(0)
     dv = H.device_inputs(w)

@@ -1,10 +1,11 @@
-"""The five seeded synthetic MoGE workloads (shapes and value distributions only).
+"""The seeded synthetic MoGE workloads (shapes and value distributions only).
 
 Shapes follow the pages' workloads: a tiny layer with 8 experts in 4 groups of 2
 (the restaurant picture of 8 waiters in 4 zones, Pangu Pro MoE summary, section 1);
 Pangu Pro's 64 experts in 8 groups with top-1 per group; the Pangu Ultra MoE shape
 (hidden 7680, 256 routed experts, 1 shared expert, expert width 2048, 8 active);
-and one device's share of a 32 x 2048-token batch under 8-way expert grouping.
+one device's share of a 32 x 2048-token batch under 8-way expert grouping; and the
+Pangu Pro layer (hidden 5120, 64 experts, 4 shared experts; expert width chosen).
 
 ``N(0, s)`` names the standard deviation ``s``.  Values come from the counter-based
 generator in ``synth_def.h``; each tensor has its own stream id below.
@@ -98,6 +99,15 @@ def group0() -> Workload:
                     0.02, 0.02, 0.0, 2.0, 0, 8)
 
 
+def pro() -> Workload:
+    """Pangu Pro layer shape (lsdiaocha.cn summary, section 2: hidden 5120, 64 routed experts in
+    8 groups with top-1 per group, 4 shared experts).  The expert width is not on the pages: 1408
+    is chosen (the width of the other 64-expert workloads); the 4 shared SwiGLU experts are one
+    shared expert of width 4 x 1408 = 5632, which computes exactly their sum."""
+    return Workload("pro_T8192_d5120_N64_M8_F1408_shared4", 8192, 5120, 64, 8, 1, 1408, 4 * 1408, "bf16", 1.0,
+                    0.02, 0.02, 0.02, 0.02, 0.02, None, 0, 64)
+
+
 def variant(base: Workload, **kw) -> Workload:
     """A workload derived from `base`; the expert range defaults to all N experts."""
     if "e_hi" not in kw:
@@ -106,4 +116,4 @@ def variant(base: Workload, **kw) -> Workload:
     return dataclasses.replace(base, **kw)
 
 
-ALL = {w.name: w for w in (tiny(), routing(), decode(), ultra(), group0())}
+ALL = {w.name: w for w in (tiny(), routing(), decode(), ultra(), group0(), pro())}

@@ -105,6 +105,22 @@ def test_layer_group0_sampled(gpu):
     assert int(off[w.e_hi] - off[w.e_lo]) == w.T * w.Kp
 
 
+def test_layer_pro_sampled(gpu):
+    # Pangu Pro shape: 64 experts in 8 groups, 4 shared experts as one of width 4 x 1408
+    check_layer(W.pro(), n_sample=12)
+
+
+@pytest.mark.parametrize("T", [1, 15, 17])
+def test_layer_few_tokens(gpu, T):
+    # fewer tokens than one 16-row tile, one past it; every expert segment is padded
+    check_layer(W.variant(W.decode(), name=f"few_T{T}", T=T, F_shared=264, std_shared_down=0.02))
+
+
+def test_layer_one_expert_range(gpu):
+    w = W.variant(W.decode(), name="one_expert", T=400, Kp=1, e_lo=37, e_hi=38, std_bias=1.0)
+    check_layer(w)
+
+
 def test_layer_deterministic(gpu):
     w = W.variant(W.decode(), name="det", T=600, std_bias=2.0)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, 0, "bf16")
