@@ -3,9 +3,11 @@
 // lsdiaocha.cn summary, section 1), plus the always-on shared expert's output
 // (Pangu Ultra MoE digests on reportify.cn: one shared expert).
 //
-// HBM-bound gather: one wave per token; each lane owns 8 consecutive hidden
-// elements per pass, loads the K rows' 16- or 32-byte pieces together and
-// accumulates in float32 in slot order (deterministic), then writes 32 bytes of y.
+// HBM-bound gather.  A wave takes one (token, 512-column block) item, so even a
+// few tokens spread over the whole chip; each lane owns 8 consecutive hidden
+// elements.  The token's slots are read in batches of 8 whose row loads are all
+// in flight together (the slot indices are wave-uniform, read through the scalar
+// cache), then accumulated in float32 in slot order (deterministic).
 #include "moge_internal.hpp"
 
 namespace moge {
@@ -34,36 +36,67 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
   }
 }
 
+constexpr int kCombineCols = 512;  // columns per wave item: 64 lanes x 8
+constexpr int kCombineBatch = 8;   // slots whose rows are loaded together
+
 template <typename OT>
 __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int K, int d, const OT* __restrict__ o,
                                                       const int32_t* __restrict__ inv, const float* __restrict__ gate,
                                                       int64_t rows_cap, const OT* __restrict__ shared_out,
                                                       float* __restrict__ y) {
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nblk = (d + kCombineCols - 1) / kCombineCols;
+  const int64_t items = T * nblk;
   const int64_t nw = (int64_t)gridDim.x * 4;
-  const int chunks = d >> 3;
-  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
-    for (int c = lane; c < chunks; c += 64) {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < K; ++s) {
-        const int r = inv[t * K + s];
-        if (r < 0 || (int64_t)r >= rows_cap) continue;
-        const float g = gate[t * K + s];
-        float v[8];
-        load8<OT>(o + (int64_t)r * d + c * 8, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+  for (int64_t it = (int64_t)blockIdx.x * 4 + wave; it < items; it += nw) {
+    const int64_t t = it / nblk;
+    const int c = (int)(it - t * nblk) * kCombineCols + lane * 8;
+    const bool live = c < d;
+    const int cl = live ? c : 0;  // lanes past d read (and drop) the row's first columns
+    const int32_t* ti = inv + t * K;
+    const float* tg = gate + t * K;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < K; s0 += 64) {
+      // lane j holds slot s0 + j: its row (-1 when absent or outside the computed experts) and gate
+      int rv = -1;
+      float gv = 0.f;
+      if (s0 + lane < K) {
+        rv = ti[s0 + lane];
+        gv = tg[s0 + lane];
       }
-      if (shared_out) {
-        float v[8];
-        load8<OT>(shared_out + t * d + c * 8, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      if (rv < 0 || (int64_t)rv >= rows_cap) {
+        rv = -1;
+        gv = 0.f;
       }
-      f32x4_t a = {acc[0], acc[1], acc[2], acc[3]}, b = {acc[4], acc[5], acc[6], acc[7]};
-      *reinterpret_cast<f32x4_t*>(y + t * d + c * 8) = a;
-      *reinterpret_cast<f32x4_t*>(y + t * d + c * 8 + 4) = b;
+      const int nb = K - s0 < 64 ? K - s0 : 64;
+      for (int j0 = 0; j0 < nb; j0 += kCombineBatch) {
+        float v[kCombineBatch][8];
+        float g[kCombineBatch];
+        bool use[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) {  // all loads of the batch issued before any is used
+          const int r = __builtin_amdgcn_readlane(rv, j0 + j);
+          use[j] = r >= 0;
+          g[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j0 + j));
+          load8<OT>(o + (int64_t)(use[j] ? r : 0) * d + cl, v[j]);  // unused slots read row 0 and drop it
+        }
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], use[j] ? v[j][i] : 0.f, acc[i]);
+      }
     }
+    if (!live) continue;
+    if (shared_out) {
+      float v[8];
+      load8<OT>(shared_out + t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    f32x4_t a = {acc[0], acc[1], acc[2], acc[3]}, b = {acc[4], acc[5], acc[6], acc[7]};
+    *reinterpret_cast<f32x4_t*>(y + t * d + c) = a;
+    *reinterpret_cast<f32x4_t*>(y + t * d + c + 4) = b;
   }
 }
 
@@ -79,8 +112,9 @@ extern "C" moge_status_t moge_combine(const moge_shape_t* shape, const void* o, 
   if (!o || !inv || !gate || !y) return fail(MOGE_ERR_NULL, "o, inv, gate and y are required");
   if (rows_cap < 1) return fail(MOGE_ERR_CAPACITY, "rows_cap must be >= 1");
   const int K = s.M * s.k_per_group;
-  int64_t grid = ((int64_t)s.T + 3) / 4;
-  if (grid > 8192) grid = 8192;
+  const int64_t items = (int64_t)s.T * ((s.d + kCombineCols - 1) / kCombineCols);
+  int64_t grid = (items + 3) / 4;  // 4 waves per workgroup, one item per wave per pass
+  if (grid > 4096) grid = 4096;
   if (s.dtype == MOGE_BF16)
     hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, stream, (int64_t)s.T, K, s.d,
                        static_cast<const uint16_t*>(o), inv, gate, rows_cap,

@@ -199,8 +199,8 @@ __device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int 
 // of loads in flight per workgroup and no staging registers; x is read exactly
 // once.  One barrier per step.  The epilogue keeps the TM x NP score tile in LDS
 // for the softmax and the per-group choice.
-template <int TM, int NP, int S>
-__global__ __launch_bounds__(256) void route_dma_kernel(int64_t T, int d, int N, int n_groups, int k,
+template <int TM, int NP, int S, int WV>
+__global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, int N, int n_groups, int k,
                                                         const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ w,
                                                         const float* __restrict__ bias,
@@ -208,25 +208,25 @@ __global__ __launch_bounds__(256) void route_dma_kernel(int64_t T, int d, int N,
                                                         float* __restrict__ gate) {
   constexpr int ROWS = TM + NP;      // stage rows of 64 bytes: tokens, then experts
   constexpr int NI = ROWS / 16;      // load instructions per step
-  constexpr int NJ = (NI + 3) / 4;   // per wave, at most
-  constexpr int CH = NJ;             // loads per step of waves 0 .. NI%4 - 1 (all waves when NI%4 == 0)
-  constexpr int CL = NI / 4;         // loads per step of the other waves
+  constexpr int NJ = (NI + WV - 1) / WV;  // per wave, at most
+  constexpr int CH = NJ;                  // loads per step of waves 0 .. NI%WV - 1 (all when NI%WV == 0)
+  constexpr int CL = NI / WV;             // loads per step of the other waves
   constexpr int STAGE = ROWS * 64;
   constexpr int TB = TM / 32;        // token blocks; wave = token block + TB * expert slice
-  static_assert(TM * NP == 8192 && S >= 4 && NI % 4 != 1, "route tile");
+  static_assert(TM * NP == 2048 * WV && S >= 4, "route tile: one 32 x 64 block per wave");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tb = wave % TB, es = wave / TB;
   const int64_t t0 = (int64_t)blockIdx.x * TM;
   const int nkf = d / 32;                        // full steps; a ragged tail follows the loop
-  const bool many = (NI % 4 == 0) || wave < (NI % 4);  // this wave issues CH loads per step, else CL
+  const bool many = (NI % WV == 0) || wave < (NI % WV);  // this wave issues CH loads per step, else CL
 
-  // load j of this wave moves stage rows 16 i .. 16 i + 15 with i = wave + 4 j
+  // load j of this wave moves stage rows 16 i .. 16 i + 15 with i = wave + WV j
   const uint16_t* src[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int srow = 16 * (wave + 4 * j) + (lane >> 2);
+    const int srow = 16 * (wave + WV * j) + (lane >> 2);
     const int c = (lane & 3) ^ lds_swz(srow);
     if (srow < TM) {
       int64_t t = t0 + srow;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void route_dma_kernel(int64_t T, int d, int N,
     const uint32_t st = lds0 + (uint32_t)((ks % S) * STAGE);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      if (wave + 4 * j < NI) dma_16x64(src[j] + ks * 32, st + (uint32_t)(16 * (wave + 4 * j) * 64));
+      if (wave + WV * j < NI) dma_16x64(src[j] + ks * 32, st + (uint32_t)(16 * (wave + WV * j) * 64));
   };
   // at most `steps` steps of this wave's loads still in flight (and, with lgkm, no LDS reads)
   auto wait_steps = [&](int steps_left_ok, bool lgkm) {
@@ -308,11 +308,11 @@ __global__ __launch_bounds__(256) void route_dma_kernel(int64_t T, int d, int N,
     const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      if (wave + 4 * j < NI) {
-        const int srow = 16 * (wave + 4 * j) + (lane >> 2);
+      if (wave + WV * j < NI) {
+        const int srow = 16 * (wave + WV * j) + (lane >> 2);
         const int c = (lane & 3) ^ lds_swz(srow);
         const u32x4_t v = (kt + c * 8 < d) ? *reinterpret_cast<const u32x4_t*>(src[j] + kt) : zero;
-        *reinterpret_cast<u32x4_t*>(lds + 16 * (wave + 4 * j) * 64 + lane * 16) = v;
+        *reinterpret_cast<u32x4_t*>(lds + 16 * (wave + WV * j) * 64 + lane * 16) = v;
       }
     }
     __syncthreads();
@@ -340,18 +340,18 @@ __global__ __launch_bounds__(256) void route_dma_kernel(int64_t T, int d, int N,
   tile_epilogue(lt, LD, TM, t0, T, N, n_groups, k, logits_out, idx, gate);
 }
 
-template <int TM, int NP, int S>
+template <int TM, int NP, int S, int WV>
 static moge_status_t launch_route_dma(const moge_shape_t& s, int n_groups, int k, const void* x, const void* w,
                                       const float* bias, float* logits, int32_t* idx, float* gate,
                                       hipStream_t stream) {
   constexpr size_t ring = (size_t)S * (TM + NP) * 64;
   constexpr size_t tile = (size_t)TM * (NP + 1) * 4;
   constexpr size_t lds = ring > tile ? ring : tile;
-  const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S>);
+  const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV>);
   moge_status_t st = raise_dynamic_lds(kern, lds, "route_dma_kernel");
   if (st != MOGE_OK) return st;
   const int64_t grid = ((int64_t)s.T + TM - 1) / TM;
-  hipLaunchKernelGGL((route_dma_kernel<TM, NP, S>), dim3((unsigned)grid), dim3(256), lds, stream, (int64_t)s.T, s.d,
+  hipLaunchKernelGGL((route_dma_kernel<TM, NP, S, WV>), dim3((unsigned)grid), dim3(64 * WV), lds, stream, (int64_t)s.T, s.d,
                      s.N, n_groups, k, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
                      logits, idx, gate);
   return check_launch("route_dma_kernel");
@@ -544,11 +544,11 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
                          static_cast<const uint16_t*>(w_router), bias, logits, idx, gate);
       st = check_launch("route_mfma_splitk_kernel");
     } else if (s.N <= 64) {
-      st = launch_route_dma<128, 64, 6>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+      st = launch_route_dma<128, 64, 6, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
     } else if (s.N <= 128) {
-      st = launch_route_dma<64, 128, 6>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+      st = launch_route_dma<64, 128, 6, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
     } else {
-      st = launch_route_dma<32, 256, 7>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+      st = launch_route_dma<32, 256, 7, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
     }
   }
   return st == MOGE_OK ? ok() : st;
