@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="ultra", choices=["ultra", "group0", "decode", "routing", "tiny", "pro"])
+    p.add_argument("--rows", default="auto", choices=["auto", "gather", "copy"],
+                   help="gate/up token rows: read from x through perm, or copied by dispatch (auto: the layer's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -62,8 +64,9 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read_per_launch": n, "bytes_written_per_launch": n, "launches": 3}))
 
 
-def algorithmic_work(w, counts, fused_shared=False):
-    """Bytes and FLOPs each call must move / compute (unique HBM traffic; no re-reads counted)."""
+def algorithmic_work(w, counts, fused_shared=False, gather=False):
+    """Bytes and FLOPs each call must move / compute (unique HBM traffic; no re-reads counted).
+    gather: dispatch copies no rows and gate/up reads the token rows from x (each row once)."""
     import numpy as np
 
     b = 2 if w.dtype == "bf16" else 4
@@ -74,14 +77,15 @@ def algorithmic_work(w, counts, fused_shared=False):
     active = int((rng > 0).sum())
     work = {}
     work["route"] = dict(bytes=T * d * b + N * d * b + T * N * 4 + T * K * 8, flops=2 * T * d * N)
-    work["dispatch"] = dict(bytes=T * K * 4 * 3 + (T * d * b + R * d * b if F else 0), flops=0)
+    work["dispatch"] = dict(bytes=T * K * 4 * 3 + (T * d * b + R * d * b if F and not gather else 0), flops=0)
     if F:
-        work["gate_up"] = dict(bytes=active * 2 * F * d * b + R * d * b + R * F * b, flops=2 * R * d * 2 * F)
+        a_bytes = T * d * b if gather else R * d * b
+        work["gate_up"] = dict(bytes=active * 2 * F * d * b + a_bytes + R * F * b, flops=2 * R * d * 2 * F)
         work["down"] = dict(bytes=active * d * F * b + R * F * b + R * d * b, flops=2 * R * F * d)
         work["combine"] = dict(bytes=R * d * b + T * d * 4 + T * K * 8 + (T * d * b if w.F_shared else 0), flops=0)
     if w.F_shared:
         Fs = w.F_shared
-        gu = dict(bytes=2 * Fs * d * b + T * d * b + T * Fs * b, flops=2 * T * d * 2 * Fs)
+        gu = dict(bytes=2 * Fs * d * b + (0 if gather else T * d * b) + T * Fs * b, flops=2 * T * d * 2 * Fs)
         dn = dict(bytes=Fs * d * b + T * Fs * b + T * d * b, flops=2 * T * Fs * d)
         if fused_shared:
             # the shared expert runs inside the routed experts' gate/up and down launches
@@ -193,7 +197,8 @@ def main():
         args.workload]()
     torch.cuda.set_device(0)
     dv = H.device_inputs(w)
-    layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi)
+    layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi,
+                      gather={"auto": None, "gather": True, "copy": False}[args.rows])
     if w.F:
         # expert weights are packed once, at load time (outside the timed steps)
         (pg, pu, pd), ps = layer.pack_expert_weights(dv.w_gate, dv.w_up, dv.w_down, dv.shared)
@@ -239,7 +244,7 @@ def main():
     value = w.T * args.steps / (total_ms / 1000.0)
 
     counts = layer.counts.cpu().numpy()
-    work = algorithmic_work(w, counts, fused_shared=bool(w.F_shared) and layer.fuse_shared)
+    work = algorithmic_work(w, counts, fused_shared=bool(w.F_shared) and layer.fuse_shared, gather=layer.gather)
     dom = max((k for k in work if k in stage_us), key=lambda k: stage_us[k])
     t = stage_us[dom] * 1e-6
     wb, wf = work[dom]["bytes"], work[dom]["flops"]
@@ -282,7 +287,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "M": w.M, "k_per_group": w.Kp, "F": w.F,
-                   "F_shared": w.F_shared, "experts_computed": [w.e_lo, w.e_hi], "seed": w.seed},
+                   "F_shared": w.F_shared, "experts_computed": [w.e_lo, w.e_hi], "seed": w.seed,
+                   "rows": "gather" if layer.gather else "copy"},
         "roofline": roof,
         "stages": stages,
         "imbalance": {"moge_is_raw": int(layer.is_raw.item()),

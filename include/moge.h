@@ -241,6 +241,29 @@ moge_status_t moge_expert_down_with_shared(const moge_shape_t* shape, int32_t F_
                                            void* out_shared, hipStream_t stream);
 
 /*
+ * moge_expert_gate_up_gather -- moge_expert_gate_up (and, when F_shared > 0, the
+ * shared expert's gate/up over all T tokens in the same launch) reading the
+ * token rows straight from x through perm instead of from a tiled x_perm, so
+ * that moge_dispatch needs no row copy (call it with x = x_perm = NULL and
+ * inv/perm given).  bf16 only, d % 32 == 0.
+ *   x         [T][d] bf16 row-major (the layer input).
+ *   perm      [rows_cap] int32 from moge_dispatch (same e_lo, e_hi, rows_cap): the
+ *             token of each local row, -1 on padding rows.
+ *   offsets, e_lo, e_hi, rows_cap, w_gate, w_up, h: as moge_expert_gate_up.
+ *   F_shared  0 (no shared expert; ws_gate, ws_up, hs must be NULL) or the shared
+ *             expert's width (% 8 == 0) with ws_gate, ws_up packed F_shared x d
+ *             and hs tiled T x F_shared, as moge_expert_gate_up_with_shared.
+ * h (and hs) are bit-identical to moge_expert_gate_up(_with_shared) on the
+ * dispatched x_perm (x_tiled).  Errors: MOGE_ERR_DTYPE for float32,
+ * MOGE_ERR_SHAPE for d % 32 != 0 or a bad F_shared, MOGE_ERR_NULL / MOGE_ERR_ARG
+ * for missing or unexpected operands, plus those of moge_expert_gate_up.
+ */
+moge_status_t moge_expert_gate_up_gather(const moge_shape_t* shape, const void* x, const int32_t* perm,
+                                         const int32_t* offsets, int32_t e_lo, int32_t e_hi, int64_t rows_cap,
+                                         const void* w_gate, const void* w_up, void* h, int32_t F_shared,
+                                         const void* ws_gate, const void* ws_up, void* hs, hipStream_t stream);
+
+/*
  * moge_combine -- gate-weighted sum of the expert outputs back in token order.
  *   y[t] = sum over slots s (in slot order) with inv[t][s] >= 0 of
  *          gate[t][s] * o[inv[t][s]]   (+ shared_out[t] when not NULL), in float32.

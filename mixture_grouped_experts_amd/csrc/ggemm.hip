@@ -20,8 +20,12 @@
 //     third off the load time.  K is padded with zeros to a multiple of 32, so
 //     there is no ragged reduction step;
 //   * both panels go straight from global memory to a 4-stage LDS ring
-//     (global_load_lds_dwordx4, BK = 32), so every load has about two steps of
-//     MFMA work to arrive and no registers stage it; 64-byte LDS rows with an
+//     (global_load_lds_dwordx4, BK = 32), so every load has three steps of MFMA
+//     work to arrive and no registers stage it;
+//   * GEMM 1 can also take its token rows straight from the row-major x, each
+//     lane's address from perm (moge_expert_gate_up_gather): dispatch then never
+//     writes x_perm (R x d, 1 GB for 8192 tokens x 8 slots x 7680), and the rows
+//     come in at 64 B per row per step instead of as whole tiles; 64-byte LDS rows with an
 //     XOR swizzle keep the 16-byte fragment reads bank-conflict free at the
 //     LDS's full rate, which takes at least two waves per SIMD to reach;
 //   * a tile with few live rows (the last tile of an expert) skips the MFMAs of
@@ -56,6 +60,30 @@ constexpr int kGroupM = 4;                  // m-tiles per scheduling group
 
 __device__ __forceinline__ int swz(int r) { return lds_swz(r); }
 
+// How the token-row operand A is addressed.
+constexpr int kATiled = 0;   // tiled [rows][KP] (x_perm from dispatch, or h)
+constexpr int kAGather = 1;  // row-major x [arows][KP]; local row r is token perm[r] (-1: padding row)
+constexpr int kARows = 2;    // row-major x [arows][KP]; local row r is token r
+
+// Operands of one grouped GEMM problem.
+//   GEMM 1 (SWIGLU):  A = token rows (tiled x_perm, or x itself read through perm),
+//                     B0/B1 = packed gate/up [E][NOUT][KP], C = h tiled [rows][NPAD],
+//                     NPAD = NOUT rounded up to 32.
+//   GEMM 2:           A = h tiled [rows][KP], B0 = packed down [E][NOUT][KP], C = out [rows][NOUT].
+// KP = the reduction length rounded up to 32 (zero padded in tiled A and in B; a
+// row-major A needs KP == its row length, i.e. d % 32 == 0).
+struct GemmOperands {
+  const uint16_t* A;
+  const uint16_t* B0;
+  const uint16_t* B1;
+  uint16_t* C;
+  int NOUT;
+  int KP;
+  int amode;            // kATiled, kAGather or kARows
+  const int32_t* perm;  // kAGather: token of each local row
+  int64_t arows;        // kAGather, kARows: rows of x (out-of-range tokens read row 0)
+};
+
 // One tile: reduction loop and epilogue, 8 waves.  Wave (wm, wn), wm in {0,1},
 // wn in {0..3}, owns the token row blocks wm, wm+2, ..., wm+8 (32 rows each,
 // interleaved so a partly filled tile keeps the waves balanced) and 2 weight
@@ -70,12 +98,18 @@ __device__ __forceinline__ int swz(int r) { return lds_swz(r); }
 // Pipeline: global -> LDS directly (global_load_lds_dwordx4, no staging registers)
 // into a 4-stage ring.  Per step waves 0-3 move token rows wave*64 .. +64 and
 // waves 4-7 weight rows (wave-4)*64 .. +64 plus token rows 256 + (wave-4)*16 .. +16,
-// 64 B per row.  Step s is issued at step s-3 and each step waits (vmcnt) for its
-// own loads of step s+2, then one barrier, so every load has two steps of MFMA work
-// to land.  Two waves per SIMD keep the MFMA pipe fed across the barriers and give
-// the LDS enough concurrent readers to reach its full rate.
+// 64 B per row.  Step s is issued at step s-3 and read at step s only (no fragment
+// is read ahead across the barrier), so every load has three steps of MFMA work to
+// land; the end of each step waits (vmcnt) for its own loads of step s+1, then one
+// barrier.  Two waves per SIMD keep the MFMA pipe fed across the barriers and give
+// the LDS enough concurrent readers to reach its full rate.  Token rows come from
+// the tiled x_perm / h (one contiguous 1 KiB tile per instruction) or straight from
+// the row-major x through perm (16 rows x 64 B per instruction), which saves
+// materialising x_perm at all.
+
 template <bool SWIGLU, int NL>
-__device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint16_t* __restrict__ A, int64_t mband0,
+__device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __restrict__ lds,
+                                             const uint16_t* __restrict__ A, int64_t mband0,
                                              const uint16_t* __restrict__ wbase0, const uint16_t* __restrict__ wbase1,
                                              int wbands, int nkf, int mrows, int64_t row0, int n0, int NOUT, int NPAD,
                                              uint16_t* __restrict__ C) {
@@ -89,6 +123,7 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
   const int live_bands = (mrows + kTileRows - 1) / kTileRows;
   const uint16_t* dsrc[5];
   int lrow[5];  // first stage row of each instruction (wave-uniform)
+  const int astep = op.amode == kATiled ? kTileElems : kTileCols;  // token-row elements per step
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     lrow[j] = wtok ? wave * 64 + j * 16 : (j < 4 ? kBM + (wave - 4) * 64 + j * 16 : 256 + (wave - 4) * 16);
@@ -98,7 +133,14 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
     if (lrow[j] < kBM) {
       int band = lrow[j] / kTileRows;  // bands past the live rows re-read the last live band (never stored)
       if (band >= live_bands) band = live_bands - 1;
-      dsrc[j] = A + (mband0 + band) * nkf * kTileElems + inner;
+      if (op.amode == kATiled) {
+        dsrc[j] = A + (mband0 + band) * nkf * kTileElems + inner;
+      } else {  // row-major x: this lane's row is one token's row, 64 bytes of it per step
+        const int64_t row = (mband0 + band) * kTileRows + (lane >> 2);
+        int64_t tok = op.amode == kAGather ? (int64_t)op.perm[row] : row;
+        if (tok < 0 || tok >= op.arows) tok = 0;  // padding rows read token 0 (never stored)
+        dsrc[j] = A + tok * op.KP + c * 8;
+      }
     } else {
       const int r = lrow[j] - kBM;
       int band = (SWIGLU ? n0 + (r & 127) : n0 + r) / kTileRows;
@@ -111,12 +153,16 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
   // stage is read.
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int ks) {
-    const int k = ks < nkf ? ks * kTileElems : 0;
+    const int kq = ks < nkf ? ks : 0;
+    const int offa = kq * astep, offb = kq * kTileElems;
     const uint32_t st = lds0 + (uint32_t)((ks % kStages) * kStageB);
+    if (wtok) {  // four token-row instructions
 #pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      if (j == 4 && wtok) break;
-      dma_16x64(dsrc[j] + k, st + (uint32_t)(lrow[j] * kRowB));
+      for (int j = 0; j < 4; ++j) dma_16x64(dsrc[j] + offa, st + (uint32_t)(lrow[j] * kRowB));
+    } else {     // four weight-row instructions and one token-row instruction
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma_16x64_stream(dsrc[j] + offb, st + (uint32_t)(lrow[j] * kRowB));
+      dma_16x64(dsrc[4] + offa, st + (uint32_t)(lrow[4] * kRowB));
     }
   };
   const int kc = (lane >> 5);  // logical chunk of this lane inside a 16-element sub-step
@@ -160,32 +206,30 @@ __device__ __forceinline__ void tile_compute(char* __restrict__ lds, const uint1
   issue(0);
   issue(1);
   issue(2);
-  // steps 0 and 1 landed (this wave; token waves issue 4 loads per step, the others 5)
-  if (wtok) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(5));
+  // step 0 landed (this wave; token waves issue 4 loads per step, the others 5)
+  if (wtok) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
   __syncthreads();
-  if (NL) frag(0, 0, a0, b0);
   for (int ks = 0; ks < nkf; ++ks) {
     issue(ks + 3);
     if (NL) {
+      frag(ks, 0, a0, b0);
       frag(ks, 1, a1, b1);
       mfma(a0, b0);
-      frag(ks + 1, 0, a0, b0);
       mfma(a1, b1);
-      // interleave: each fragment read issues in the shadow of an MFMA
+      // the first half's reads, then the second half's reads each in the shadow of an MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, NL + 2, 0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = 0; i < 2 * NL; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-          if (i < 2 + NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
+      for (int i = 0; i < 2 * NL; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+        if (i < 2 + NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NL, 0);
     }
-    // step ks+2 landed (this wave) and this step's LDS reads are done, so the DMA
+    // step ks+1 landed (this wave) and this step's LDS reads are done, so the DMA
     // issued after the barrier may overwrite stage ks % 4
-    if (wtok) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(4));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(5));
+    if (wtok) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(8));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(10));
     __syncthreads();
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing reloads before LDS is reused
@@ -268,19 +312,7 @@ __device__ __forceinline__ void expert_segments(const int32_t* __restrict__ offs
   }
 }
 
-// Operands of one grouped GEMM problem.
-//   GEMM 1 (SWIGLU):  A = x_perm tiled [rows][KP], B0/B1 = packed gate/up [E][NOUT][KP],
-//                     C = h tiled [rows][NPAD] with NPAD = NOUT rounded up to 32.
-//   GEMM 2:           A = h tiled [rows][KP], B0 = packed down [E][NOUT][KP], C = out [rows][NOUT].
-// KP = the reduction length rounded up to 32 (zero padded in A and B).
-struct GemmOperands {
-  const uint16_t* A;
-  const uint16_t* B0;
-  const uint16_t* B1;
-  uint16_t* C;
-  int NOUT;
-  int KP;
-};
+
 
 // One persistent launch runs the tiles of two problems: the routed experts (problem
 // 0: segments from `offsets`) and, when rows1 > 0, one dense expert over rows1 rows
@@ -359,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
     const int nrb = (mrows + 31) / 32;
     const int nl = nrb > wm ? (nrb - wm + 1) / 2 : 0;
 #define MOGE_TILE(NLV)                                                                                          \
-  tile_compute<SWIGLU, NLV>(lds, op.A, mband0, wb0, wb1, wbands, nkf, mrows, row0, ncol0, op.NOUT, npad, op.C)
+  tile_compute<SWIGLU, NLV>(op, lds, op.A, mband0, wb0, wb1, wbands, nkf, mrows, row0, ncol0, op.NOUT, npad, op.C)
     switch (nl) {
       case 5: MOGE_TILE(5); break;
       case 4: MOGE_TILE(4); break;
@@ -462,10 +494,11 @@ static moge_status_t launch_ggemm(const GemmOperands& p0, const int32_t* offsets
   return check_launch(SWIGLU ? "ggemm_bf16_kernel<gate_up>" : "ggemm_bf16_kernel<down>");
 }
 
-static GemmOperands operands(const void* A, const void* B0, const void* B1, void* C, int NOUT, int KD) {
+static GemmOperands operands(const void* A, const void* B0, const void* B1, void* C, int NOUT, int KD,
+                             int amode = 0, const int32_t* perm = nullptr, int64_t arows = 0) {
   return GemmOperands{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
                       static_cast<const uint16_t*>(B1), static_cast<uint16_t*>(C), NOUT,
-                      (int)round_up(KD, kTileCols)};
+                      (int)round_up(KD, kTileCols), amode, perm, arows};
 }
 
 }  // namespace moge
@@ -576,5 +609,30 @@ extern "C" moge_status_t moge_expert_down_with_shared(const moge_shape_t* shape,
   const moge_shape_t& s = *shape;
   st = launch_ggemm<false>(operands(h, w_down, nullptr, out, s.d, s.F), offsets, e_lo, e_hi - e_lo, rows_cap,
                            operands(hs, ws_down, nullptr, out_shared, s.d, F_shared), s.T, stream);
+  return st == MOGE_OK ? ok() : st;
+}
+
+extern "C" moge_status_t moge_expert_gate_up_gather(const moge_shape_t* shape, const void* x, const int32_t* perm,
+                                                    const int32_t* offsets, int32_t e_lo, int32_t e_hi,
+                                                    int64_t rows_cap, const void* w_gate, const void* w_up, void* h,
+                                                    int32_t F_shared, const void* ws_gate, const void* ws_up, void* hs,
+                                                    hipStream_t stream) {
+  moge_status_t st = ffn_common_checks(shape, e_lo, e_hi, rows_cap);
+  if (st != MOGE_OK) return st;
+  const moge_shape_t& s = *shape;
+  if (s.dtype != MOGE_BF16) return fail(MOGE_ERR_DTYPE, "moge_expert_gate_up_gather is bf16 only");
+  if (s.d % kTileCols != 0) return fail(MOGE_ERR_SHAPE, "moge_expert_gate_up_gather needs d % 32 == 0");
+  if (!x || !perm || !offsets || !w_gate || !w_up || !h)
+    return fail(MOGE_ERR_NULL, "x, perm, offsets, w_gate, w_up and h are required");
+  if (F_shared < 0 || (F_shared > 0 && F_shared % 8 != 0))
+    return fail(MOGE_ERR_SHAPE, "F_shared must be 0 or a positive multiple of 8");
+  if (F_shared > 0 && (!ws_gate || !ws_up || !hs))
+    return fail(MOGE_ERR_NULL, "ws_gate, ws_up and hs are required when F_shared > 0");
+  if (F_shared == 0 && (ws_gate || ws_up || hs)) return fail(MOGE_ERR_ARG, "F_shared == 0 takes no shared operands");
+  const GemmOperands none{};
+  st = launch_ggemm<true>(operands(x, w_gate, w_up, h, s.F, s.d, kAGather, perm, s.T), offsets, e_lo, e_hi - e_lo,
+                          rows_cap,
+                          F_shared ? operands(x, ws_gate, ws_up, hs, F_shared, s.d, kARows, nullptr, s.T) : none,
+                          F_shared ? s.T : 0, stream);
   return st == MOGE_OK ? ok() : st;
 }

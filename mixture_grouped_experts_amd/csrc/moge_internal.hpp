@@ -96,6 +96,15 @@ __device__ __forceinline__ void dma_16x64(const void* src, uint32_t m0) {
                : "memory", "m0");
 }
 
+// The same with the non-temporal hint, for data read once (expert weights): it
+// streams through the caches instead of displacing data that is read again.
+__device__ __forceinline__ void dma_16x64_stream(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(m0))
+               : "memory", "m0");
+}
+
 // Number of lanes below the calling lane whose bit is set in `mask`.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

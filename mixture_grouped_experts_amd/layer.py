@@ -4,13 +4,17 @@ Order (Pangu Pro MoE, lsdiaocha.cn summary, section 1; Pangu Ultra MoE digests o
 reportify.cn for the shared expert):
 
   1. moge_route GROUPED   scores (stored), softmax over all N, top-K' in every group
-  2. moge_dispatch        counts, offsets, stable permutation, rows of [e_lo, e_hi)
-                          (tiled), and the tiled copy of x for the shared expert
-  3. moge_expert_gate_up_with_shared, moge_expert_down_with_shared
-                          SwiGLU experts on their row segments and the always-on shared
-                          expert over all tokens, in the same two launches (bf16); float32
-                          shapes use moge_expert_gate_up / _down and a one-expert
-                          moge_grouped_ffn for the shared expert
+  2. moge_dispatch        counts, offsets, stable permutation of [e_lo, e_hi); the rows
+                          themselves are copied (tiled x_perm, and the tiled x for the
+                          shared expert) only where step 3 cannot read them from x
+  3. moge_expert_gate_up_gather, moge_expert_down(_with_shared)
+                          SwiGLU experts on their row segments, the gate/up GEMM reading
+                          each row straight from x through perm, and the always-on shared
+                          expert over all tokens in the same two launches (bf16 with
+                          d % 32 == 0); other bf16 shapes use the tiled x_perm with
+                          moge_expert_gate_up_with_shared; float32 shapes use
+                          moge_expert_gate_up / _down and a one-expert moge_grouped_ffn for
+                          the shared expert
   4. moge_combine         gate-weighted sum (+ shared output) -> y (float32)
   5. moge_imbalance       per-group load and imbalance score (0 by construction)
   6. moge_route GLOBAL    the conventional top-K comparator from the stored scores,
@@ -30,7 +34,8 @@ from . import _lib as L
 
 class MoGELayer:
     def __init__(self, T: int, d: int, N: int, M: int, Kp: int, F: int, F_shared: int = 0, dtype: str = "bf16",
-                 e_lo: int = 0, e_hi: int | None = None, device="cuda", comparator: bool = True):
+                 e_lo: int = 0, e_hi: int | None = None, device="cuda", comparator: bool = True,
+                 gather: bool | None = None):
         self.dtype_code = L.BF16 if dtype == "bf16" else L.F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.shape = L.Shape(T, d, N, M, Kp, F, self.dtype_code)
@@ -42,6 +47,11 @@ class MoGELayer:
         self.e_lo, self.e_hi = e_lo, (N if e_hi is None else e_hi)
         self.F_shared = F_shared
         self.fuse_shared = dtype == "bf16"  # the fused routed + shared launches are bf16 only
+        # gate/up reads the token rows from x through perm (no row copy); None: wherever it can
+        can_gather = dtype == "bf16" and d % 32 == 0 and F > 0
+        if gather and not can_gather:
+            raise ValueError("reading rows through perm needs bf16, d % 32 == 0 and F > 0")
+        self.gather = can_gather if gather is None else bool(gather)
         self.comparator = comparator
         self.routing_only = F == 0
         dev = torch.device(device)
@@ -74,14 +84,14 @@ class MoGELayer:
             R = self.rows_cap
             self.inv = torch.empty(T, K, **i32)
             self.perm = torch.empty(R, **i32)
-            self.x_perm = torch.empty(L.tiled_elems(R, d), dtype=self.tdtype, device=dev)
+            self.x_perm = None if self.gather else torch.empty(L.tiled_elems(R, d), dtype=self.tdtype, device=dev)
             self.h = torch.empty(L.tiled_elems(R, F), dtype=self.tdtype, device=dev)
             self.o = torch.empty(R, d, dtype=self.tdtype, device=dev)
             self.y = torch.empty(T, d, **f32)
         if F_shared:
             self.sshape = L.Shape(T, d, 1, 1, 1, F_shared, self.dtype_code)
             self.soffsets = torch.tensor([0, T], **i32)
-            self.x_tiled = torch.empty(L.tiled_elems(T, d), dtype=self.tdtype, device=dev)
+            self.x_tiled = None if self.gather else torch.empty(L.tiled_elems(T, d), dtype=self.tdtype, device=dev)
             self.sh = torch.empty(L.tiled_elems(T, F_shared), dtype=self.tdtype, device=dev)
             self.so = torch.empty(T, d, dtype=self.tdtype, device=dev)
 
@@ -123,29 +133,47 @@ class MoGELayer:
                        self.ws, stream=stream)
             mk("dispatch")
         else:
-            L.dispatch(s, L.ROUTE_GROUPED, self.idx, x, self.e_lo, self.e_hi, self.rows_cap, self.counts,
-                       self.offsets, self.inv, self.perm, self.x_perm, self.ws,
-                       self.x_tiled if self.F_shared else None, stream)
-            mk("dispatch")
-            if self.F_shared and self.fuse_shared:
-                # routed and shared experts in the same two launches
-                L.expert_gate_up_with_shared(s, self.F_shared, self.x_perm, self.offsets, self.e_lo, self.e_hi,
-                                             self.rows_cap, w_gate, w_up, self.h, self.x_tiled, shared[0], shared[1],
-                                             self.sh, stream)
+            if self.gather:
+                L.dispatch(s, L.ROUTE_GROUPED, self.idx, None, self.e_lo, self.e_hi, self.rows_cap, self.counts,
+                           self.offsets, self.inv, self.perm, None, self.ws, None, stream)
+                mk("dispatch")
+                Fs = self.F_shared
+                L.expert_gate_up_gather(s, x, self.perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate,
+                                        w_up, self.h, Fs, shared[0] if Fs else None, shared[1] if Fs else None,
+                                        self.sh if Fs else None, stream)
                 mk("gate_up")
-                L.expert_down_with_shared(s, self.F_shared, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap,
-                                          w_down, self.o, self.sh, shared[2], self.so, stream)
+                if Fs:
+                    L.expert_down_with_shared(s, Fs, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down,
+                                              self.o, self.sh, shared[2], self.so, stream)
+                else:
+                    L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o,
+                                  stream)
                 mk("down")
             else:
-                L.expert_gate_up(s, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate, w_up,
-                                 self.h, stream)
-                mk("gate_up")
-                L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o, stream)
-                mk("down")
-                if self.F_shared:
-                    L.grouped_ffn(self.sshape, self.x_tiled, self.soffsets, 0, 1, self.T, shared[0], shared[1],
-                                  shared[2], self.sh, self.so, stream)
-                    mk("shared")
+                L.dispatch(s, L.ROUTE_GROUPED, self.idx, x, self.e_lo, self.e_hi, self.rows_cap, self.counts,
+                           self.offsets, self.inv, self.perm, self.x_perm, self.ws,
+                           self.x_tiled if self.F_shared else None, stream)
+                mk("dispatch")
+                if self.F_shared and self.fuse_shared:
+                    # routed and shared experts in the same two launches
+                    L.expert_gate_up_with_shared(s, self.F_shared, self.x_perm, self.offsets, self.e_lo,
+                                                 self.e_hi, self.rows_cap, w_gate, w_up, self.h, self.x_tiled,
+                                                 shared[0], shared[1], self.sh, stream)
+                    mk("gate_up")
+                    L.expert_down_with_shared(s, self.F_shared, self.h, self.offsets, self.e_lo, self.e_hi,
+                                              self.rows_cap, w_down, self.o, self.sh, shared[2], self.so, stream)
+                    mk("down")
+                else:
+                    L.expert_gate_up(s, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate,
+                                     w_up, self.h, stream)
+                    mk("gate_up")
+                    L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o,
+                                  stream)
+                    mk("down")
+                    if self.F_shared:
+                        L.grouped_ffn(self.sshape, self.x_tiled, self.soffsets, 0, 1, self.T, shared[0], shared[1],
+                                      shared[2], self.sh, self.so, stream)
+                        mk("shared")
             L.combine(s, self.o, self.inv, self.gate, self.rows_cap, self.so if self.F_shared else None, self.y,
                       stream)
             mk("combine")

@@ -125,6 +125,21 @@ def test_null_and_argument_errors_before_any_launch():
     assert lib.moge_grouped_ffn(sp, fake, fake, 0, 8, 64, fake, None, fake, fake, fake, None) == 3
     assert lib.moge_grouped_ffn(sp, fake, fake, -1, 8, 64, fake, fake, fake, fake, fake, None) == 1
     assert lib.moge_grouped_ffn(sp, fake, fake, 0, 8, 0, fake, fake, fake, fake, fake, None) == 7
+    lib.moge_expert_gate_up_gather.argtypes = [P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P, P,
+                                               ctypes.c_int32, P, P, P, P]
+    g = lib.moge_expert_gate_up_gather
+    d256 = S(d=256)
+    sg = ctypes.byref(d256)
+    assert g(ctypes.byref(S(d=256, dt=moge.F32)), fake, fake, fake, 0, 8, 64, fake, fake, fake, 0, None, None, None,
+             None) == 5                                                                   # bf16 only
+    assert g(ctypes.byref(S(d=200)), fake, fake, fake, 0, 8, 64, fake, fake, fake, 0, None, None, None, None) == 2
+    assert g(sg, None, fake, fake, 0, 8, 64, fake, fake, fake, 0, None, None, None, None) == 3     # no x
+    assert g(sg, fake, None, fake, 0, 8, 64, fake, fake, fake, 0, None, None, None, None) == 3     # no perm
+    assert g(sg, fake, fake, fake, 0, 8, 64, fake, fake, fake, 12, fake, fake, fake, None) == 2    # F_shared % 8
+    assert g(sg, fake, fake, fake, 0, 8, 64, fake, fake, fake, 64, fake, None, fake, None) == 3    # missing ws_up
+    assert g(sg, fake, fake, fake, 0, 8, 64, fake, fake, fake, 0, None, None, fake, None) == 1     # hs without F_s
+    assert g(sg, fake, fake, fake, 0, 9, 64, fake, fake, fake, 0, None, None, None, None) == 1     # e_hi > N
+    assert g(sg, fake, fake, fake, 0, 8, 0, fake, fake, fake, 0, None, None, None, None) == 7      # rows_cap
     lib.moge_combine.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P]
     assert lib.moge_combine(sp, fake, fake, None, 64, None, fake, None) == 3
     assert lib.moge_combine(sp, fake, fake, fake, 0, None, fake, None) == 7

@@ -168,3 +168,58 @@ def test_routed_and_shared_in_one_launch_bitexact(gpu):
     assert torch.equal(H.untile_rows(h1, cap, w.F)[live], H.untile_rows(h2, cap, w.F)[live])
     assert torch.equal(o1[live], o2[live])
     assert torch.equal(hs1, hs2) and torch.equal(so1, so2)
+
+
+@pytest.mark.parametrize("w", [
+    W.variant(MID, name="gather_shared_T333", F_shared=136, std_shared_down=0.02, T=333),
+    W.variant(MID, name="gather_range_3_11", e_lo=3, e_hi=11),
+    W.variant(MID, name="gather_shared_T1", F_shared=64, std_shared_down=0.02, T=1),
+    W.variant(MID, name="gather_T17_d512_N64_M8", T=17, d=512, N=64, M=8, Kp=1, F=1408, F_shared=256,
+              std_shared_down=0.02),
+], ids=lambda w: w.name)
+def test_gathered_gate_up_bitexact(gpu, w):
+    # reading the token rows from x through perm gives exactly the h of the tiled x_perm
+    dv = H.device_inputs(w)
+    hi = H.HostInputs(w)
+    idx, _, _ = oracle.route(H.oracle_logits_all(hi), w.M, w.Kp, "grouped")
+    s = moge.Shape(w.T, w.d, w.N, w.M, w.Kp, w.F, moge.BF16)
+    cap = moge.rows_bound(s, moge.ROUTE_GROUPED, w.e_lo, w.e_hi)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    dix = torch.from_numpy(idx).cuda()
+    ws = torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda")
+    Fs = w.F_shared
+
+    def disp(copy):
+        counts, offsets = torch.empty(w.N, **i32), torch.empty(w.N + 1, **i32)
+        inv, perm = torch.empty(w.T, w.K, **i32), torch.full((cap,), -7, **i32)
+        xp = torch.empty(moge.tiled_elems(cap, w.d), **bf) if copy else None
+        xt = torch.empty(moge.tiled_elems(w.T, w.d), **bf) if copy and Fs else None
+        moge.dispatch(s, moge.ROUTE_GROUPED, dix, dv.x if copy else None, w.e_lo, w.e_hi, cap, counts, offsets, inv,
+                      perm, xp, ws, x_tiled=xt)
+        return counts, offsets, inv, perm, xp, xt
+    c1, o1, inv1, p1, xp, xt = disp(True)
+    c2, o2, inv2, p2, _, _ = disp(False)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(o1, o2) and torch.equal(inv1, inv2) and torch.equal(p1, p2)
+    pg, pu = _pack(moge.BF16, dv.w_gate), _pack(moge.BF16, dv.w_up)   # experts e_lo .. e_hi-1
+    sg, su = (_pack(moge.BF16, m.unsqueeze(0)) for m in dv.shared[:2]) if Fs else (None, None)
+    h1 = torch.full((moge.tiled_elems(cap, w.F),), 3.0, **bf)
+    h2 = torch.full((moge.tiled_elems(cap, w.F),), 5.0, **bf)
+    hs1 = torch.full((moge.tiled_elems(w.T, Fs),), 3.0, **bf) if Fs else None
+    hs2 = torch.full((moge.tiled_elems(w.T, Fs),), 5.0, **bf) if Fs else None
+    if Fs:
+        moge.expert_gate_up_with_shared(s, Fs, xp, o1, w.e_lo, w.e_hi, cap, pg, pu, h1, xt, sg, su, hs1)
+    else:
+        moge.expert_gate_up(s, xp, o1, w.e_lo, w.e_hi, cap, pg, pu, h1)
+    moge.expert_gate_up_gather(s, dv.x, p2, o2, w.e_lo, w.e_hi, cap, pg, pu, h2, Fs, sg, su, hs2)
+    torch.cuda.synchronize()
+    counts = c1.cpu().numpy()
+    P = H.segment_bases(counts, w.e_lo, w.e_hi)
+    live = torch.from_numpy(_live_rows(w, counts, P)).long().cuda()
+    if live.numel():
+        assert torch.equal(H.untile_rows(h1, cap, w.F, keep_pad_cols=True)[live],
+                          H.untile_rows(h2, cap, w.F, keep_pad_cols=True)[live])
+    if Fs:   # rows T .. (rounded up to 16) of the tiled hs are never written
+        assert torch.equal(H.untile_rows(hs1, w.T, Fs, keep_pad_cols=True),
+                           H.untile_rows(hs2, w.T, Fs, keep_pad_cols=True))

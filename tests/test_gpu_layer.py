@@ -83,6 +83,14 @@ def test_layer_mid_shared_and_range(gpu):
     check_layer(w)
 
 
+def test_layer_shared_tiled_rows(gpu):
+    # hidden size not a multiple of 32: dispatch copies the rows (tiled x_perm and x) for the fused launches
+    w = W.variant(W.decode(), name="mid_shared_d264", T=257, d=264, N=32, M=4, Kp=1, F=136, F_shared=264,
+                  std_shared_down=0.02)
+    layer, _ = check_layer(w)
+    assert not layer.gather
+
+
 def test_layer_decode(gpu):
     check_layer(W.decode())
 
@@ -129,7 +137,8 @@ def test_layer_deterministic(gpu):
     for _ in range(2):
         y = layer.forward(dv.x, dv.w_router, dv.bias, dv.w_gate, dv.w_up, dv.w_down)
         torch.cuda.synchronize()
-        outs.append((y.clone(), layer.idx.clone(), layer.inv.clone(), layer.x_perm.clone(), layer.o.clone()))
+        outs.append((y.clone(), layer.idx.clone(), layer.inv.clone(), layer.perm.clone(), layer.h.clone(),
+                     layer.o.clone()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
 
