@@ -36,6 +36,37 @@ __device__ __forceinline__ void load8<float>(const float* p, float* v) {
   }
 }
 
+// 8 elements as loaded (kept raw until every load of a batch is in flight).
+template <typename OT>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  u32x4_t u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ __forceinline__ void fma_into(float g, float* acc) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(g, __uint_as_float(u[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(g, __uint_as_float(u[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    }
+  }
+};
+template <>
+struct Raw8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4_t*>(p);
+    b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  }
+  __device__ __forceinline__ void fma_into(float g, float* acc) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = fmaf(g, a[i], acc[i]);
+      acc[4 + i] = fmaf(g, b[i], acc[4 + i]);
+    }
+  }
+};
+
 constexpr int kCombineCols = 512;  // columns per wave item: 64 lanes x 8
 constexpr int kCombineBatch = 8;   // slots whose rows are loaded together
 
@@ -69,22 +100,30 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int K, int d, c
         rv = -1;
         gv = 0.f;
       }
-      const int nb = K - s0 < 64 ? K - s0 : 64;
-      for (int j0 = 0; j0 < nb; j0 += kCombineBatch) {
-        float v[kCombineBatch][8];
+      // the slots that contribute, in slot order, 8 at a time: their row loads are all
+      // issued before any is used; slots outside the computed experts cost nothing
+      uint64_t todo = __builtin_amdgcn_ballot_w64(rv >= 0);
+      while (todo) {
+        int r[kCombineBatch];
         float g[kCombineBatch];
-        bool use[kCombineBatch];
 #pragma unroll
-        for (int j = 0; j < kCombineBatch; ++j) {  // all loads of the batch issued before any is used
-          const int r = __builtin_amdgcn_readlane(rv, j0 + j);
-          use[j] = r >= 0;
-          g[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j0 + j));
-          load8<OT>(o + (int64_t)(use[j] ? r : 0) * d + cl, v[j]);  // unused slots read row 0 and drop it
+        for (int j = 0; j < kCombineBatch; ++j) {
+          r[j] = -1;
+          g[j] = 0.f;
+          if (todo) {
+            const int sl = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            r[j] = __builtin_amdgcn_readlane(rv, sl);
+            g[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), sl));
+          }
         }
+        Raw8<OT> v[kCombineBatch];
 #pragma unroll
         for (int j = 0; j < kCombineBatch; ++j)
+          if (r[j] >= 0) v[j].load(o + (int64_t)r[j] * d + cl);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], use[j] ? v[j][i] : 0.f, acc[i]);
+        for (int j = 0; j < kCombineBatch; ++j)
+          if (r[j] >= 0) v[j].fma_into(g[j], acc);
       }
     }
     if (!live) continue;
