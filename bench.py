@@ -64,9 +64,10 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read_per_launch": n, "bytes_written_per_launch": n, "launches": 3}))
 
 
-def algorithmic_work(w, counts, fused_shared=False, gather=False):
+def algorithmic_work(w, counts, fused_shared=False, gather=False, fused_combine=False):
     """Bytes and FLOPs each call must move / compute (unique HBM traffic; no re-reads counted).
-    gather: dispatch copies no rows and gate/up reads the token rows from x (each row once)."""
+    gather: dispatch copies no rows and gate/up reads the token rows from x (each row once).
+    fused_combine: the down GEMM writes y itself (one row per token, no combine pass)."""
     import numpy as np
 
     b = 2 if w.dtype == "bf16" else 4
@@ -83,6 +84,9 @@ def algorithmic_work(w, counts, fused_shared=False, gather=False):
         work["gate_up"] = dict(bytes=active * 2 * F * d * b + a_bytes + R * F * b, flops=2 * R * d * 2 * F)
         work["down"] = dict(bytes=active * d * F * b + R * F * b + R * d * b, flops=2 * R * F * d)
         work["combine"] = dict(bytes=R * d * b + T * d * 4 + T * K * 8 + (T * d * b if w.F_shared else 0), flops=0)
+        if fused_combine:
+            work["down"] = dict(bytes=active * d * F * b + R * F * b + T * d * 4 + T * 4 + R * 4, flops=2 * R * F * d)
+            del work["combine"]
     if w.F_shared:
         Fs = w.F_shared
         gu = dict(bytes=2 * Fs * d * b + (0 if gather else T * d * b) + T * Fs * b, flops=2 * T * d * 2 * Fs)
@@ -244,7 +248,8 @@ def main():
     value = w.T * args.steps / (total_ms / 1000.0)
 
     counts = layer.counts.cpu().numpy()
-    work = algorithmic_work(w, counts, fused_shared=bool(w.F_shared) and layer.fuse_shared, gather=layer.gather)
+    work = algorithmic_work(w, counts, fused_shared=bool(w.F_shared) and layer.fuse_shared, gather=layer.gather,
+                            fused_combine=layer.fuse_combine)
     dom = max((k for k in work if k in stage_us), key=lambda k: stage_us[k])
     t = stage_us[dom] * 1e-6
     wb, wf = work[dom]["bytes"], work[dom]["flops"]

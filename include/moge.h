@@ -264,6 +264,27 @@ moge_status_t moge_expert_gate_up_gather(const moge_shape_t* shape, const void* 
                                          const void* ws_gate, const void* ws_up, void* hs, hipStream_t stream);
 
 /*
+ * moge_expert_down_combine -- moge_expert_down followed by moge_combine, in one
+ * launch, for a device's share of exactly one group with k_per_group == 1 (the
+ * expert-parallel layout that places one group per device: [P1] section 1).
+ * Then every token has exactly one row in [e_lo, e_hi), and GEMM 2's epilogue
+ * writes y[t] = gate[t][g] * o[row of t] itself (g = e_lo / (N/M), o rounded to
+ * bf16 first, then one float32 multiply), so o is never stored and no combine
+ * pass runs.  bf16 only; no shared expert (add it with moge_combine's form if
+ * needed).
+ *   h, offsets, e_lo, e_hi, rows_cap, w_down: as moge_expert_down.
+ *   perm [rows_cap] int32 from moge_dispatch; gate [T][K] float32 from moge_route.
+ *   y    [T][d] float32, every row written.
+ * y is bit-identical to moge_expert_down + moge_combine(shared_out = NULL).
+ * Errors: MOGE_ERR_DTYPE for float32; MOGE_ERR_ARG unless k_per_group == 1 and
+ * [e_lo, e_hi) is one whole group; MOGE_ERR_NULL for a missing operand; plus
+ * those of moge_expert_down.
+ */
+moge_status_t moge_expert_down_combine(const moge_shape_t* shape, const void* h, const int32_t* offsets,
+                                       int32_t e_lo, int32_t e_hi, int64_t rows_cap, const void* w_down,
+                                       const int32_t* perm, const float* gate, float* y, hipStream_t stream);
+
+/*
  * moge_combine -- gate-weighted sum of the expert outputs back in token order.
  *   y[t] = sum over slots s (in slot order) with inv[t][s] >= 0 of
  *          gate[t][s] * o[inv[t][s]]   (+ shared_out[t] when not NULL), in float32.

@@ -33,7 +33,7 @@ STAGE_DISPATCH = 1
 EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_weight_elems",
            "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_grouped_ffn",
            "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
-           "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_version",
+           "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_expert_down_combine", "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_version",
            "moge_last_error")
 
 
@@ -90,6 +90,8 @@ _lib.moge_expert_down_with_shared.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I6
 _lib.moge_expert_down_with_shared.restype = ctypes.c_int
 _lib.moge_expert_gate_up_gather.argtypes = [_SP, _P, _P, _P, _I32, _I32, _I64, _P, _P, _P, _I32, _P, _P, _P, _P]
 _lib.moge_expert_gate_up_gather.restype = ctypes.c_int
+_lib.moge_expert_down_combine.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P]
+_lib.moge_expert_down_combine.restype = ctypes.c_int
 _lib.moge_combine.argtypes = [_SP, _P, _P, _P, _I64, _P, _P, _P]
 _lib.moge_combine.restype = ctypes.c_int
 _lib.moge_imbalance.argtypes = [_SP, _P, _P, _P, _P, _P]
@@ -272,6 +274,19 @@ def expert_gate_up_gather(shape: Shape, x, perm, offsets, e_lo: int, e_hi: int, 
         _ptr(ws_up, "ws_up", et, packed_weight_elems(F_shared, d) if F_shared else 0, optional=True),
         _ptr(hs, "hs", et, tiled_elems(T, F_shared) if F_shared else 0, optional=True), _stream(stream))
     _check("moge_expert_gate_up_gather", st)
+
+
+def expert_down_combine(shape: Shape, h, offsets, e_lo: int, e_hi: int, rows_cap: int, w_down, perm, gate, y,
+                        stream=None) -> None:
+    T, d, F, K = shape.T, shape.d, shape.F, shape.K
+    E = e_hi - e_lo
+    et = _elem_dtype(shape)
+    st = _lib.moge_expert_down_combine(
+        ctypes.byref(shape), _ptr(h, "h", et, tiled_elems(rows_cap, F)),
+        _ptr(offsets, "offsets", torch.int32, shape.N + 1), e_lo, e_hi, rows_cap,
+        _ptr(w_down, "w_down", et, E * packed_weight_elems(d, F)), _ptr(perm, "perm", torch.int32, rows_cap),
+        _ptr(gate, "gate", torch.float32, T * K), _ptr(y, "y", torch.float32, T * d), _stream(stream))
+    _check("moge_expert_down_combine", st)
 
 
 def expert_down_with_shared(shape: Shape, F_shared: int, h, offsets, e_lo: int, e_hi: int, rows_cap: int, w_down, out,

@@ -80,8 +80,14 @@ struct GemmOperands {
   int NOUT;
   int KP;
   int amode;            // kATiled, kAGather or kARows
-  const int32_t* perm;  // kAGather: token of each local row
+  const int32_t* perm;  // kAGather: token of each local row; combine epilogue: the same for C's rows
   int64_t arows;        // kAGather, kARows: rows of x (out-of-range tokens read row 0)
+  // GEMM 2 only, when Y is set: instead of storing row r of C, the epilogue writes the
+  // combined output y[t] = gate[t][gslot] * C[r] (float32, row-major [T][NOUT]) for the token
+  // t = perm[r] that owns the row (each token owns exactly one row of the problem).
+  float* Y;
+  const float* gate;
+  int gstride, gslot;
 };
 
 // One tile: reduction loop and epilogue, 8 waves.  Wave (wm, wn), wm in {0,1},
@@ -242,6 +248,13 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
     const int trow = (wm + 2 * t) * 32 + (lane & 31);
     if (trow < mrows) {
       const int64_t row = row0 + trow;
+      int64_t ytok = -1;
+      float yg = 0.f;
+      if (!SWIGLU && op.Y) {  // combine epilogue: the row's token and its gate
+        ytok = op.perm[row];
+        if (ytok >= 0 && ytok < op.arows) yg = op.gate[ytok * op.gstride + op.gslot];
+        else ytok = -1;       // (a live row always has a token; never store out of range)
+      }
 #pragma unroll
       for (int cb = 0; cb < (SWIGLU ? 1 : 2); ++cb) {
 #pragma unroll
@@ -260,11 +273,19 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
               }
               hv[i] = f32_to_bf16(v);
             }
-            uint2 pk;
-            pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-            pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-            uint16_t* dst = SWIGLU ? C + tiled_index(row, col, NPAD) : C + row * NOUT + col;
-            *reinterpret_cast<uint2*>(dst) = pk;
+            if (!SWIGLU && op.Y) {
+              // y = gate * o with o rounded to bf16 first, exactly as the separate combine pass
+              f32x4_t yv;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) yv[i] = fmaf(yg, bf16_to_f32(hv[i]), 0.f);
+              if (ytok >= 0) *reinterpret_cast<f32x4_t*>(op.Y + ytok * NOUT + col) = yv;
+            } else {
+              uint2 pk;
+              pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+              pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+              uint16_t* dst = SWIGLU ? C + tiled_index(row, col, NPAD) : C + row * NOUT + col;
+              *reinterpret_cast<uint2*>(dst) = pk;
+            }
           }
         }
       }
@@ -498,7 +519,7 @@ static GemmOperands operands(const void* A, const void* B0, const void* B1, void
                              int amode = 0, const int32_t* perm = nullptr, int64_t arows = 0) {
   return GemmOperands{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
                       static_cast<const uint16_t*>(B1), static_cast<uint16_t*>(C), NOUT,
-                      (int)round_up(KD, kTileCols), amode, perm, arows};
+                      (int)round_up(KD, kTileCols), amode, perm, arows, nullptr, nullptr, 0, 0};
 }
 
 }  // namespace moge
@@ -634,5 +655,30 @@ extern "C" moge_status_t moge_expert_gate_up_gather(const moge_shape_t* shape, c
                           rows_cap,
                           F_shared ? operands(x, ws_gate, ws_up, hs, F_shared, s.d, kARows, nullptr, s.T) : none,
                           F_shared ? s.T : 0, stream);
+  return st == MOGE_OK ? ok() : st;
+}
+
+extern "C" moge_status_t moge_expert_down_combine(const moge_shape_t* shape, const void* h, const int32_t* offsets,
+                                                  int32_t e_lo, int32_t e_hi, int64_t rows_cap, const void* w_down,
+                                                  const int32_t* perm, const float* gate, float* y,
+                                                  hipStream_t stream) {
+  moge_status_t st = ffn_common_checks(shape, e_lo, e_hi, rows_cap);
+  if (st != MOGE_OK) return st;
+  const moge_shape_t& s = *shape;
+  if (s.dtype != MOGE_BF16) return fail(MOGE_ERR_DTYPE, "moge_expert_down_combine is bf16 only");
+  const int G = s.N / s.M;
+  if (s.k_per_group != 1 || e_lo % G != 0 || e_hi != e_lo + G)
+    return fail(MOGE_ERR_ARG, "moge_expert_down_combine needs k_per_group == 1 and [e_lo, e_hi) one whole group");
+  if (!h || !offsets || !w_down || !perm || !gate || !y)
+    return fail(MOGE_ERR_NULL, "h, offsets, w_down, perm, gate and y are required");
+  GemmOperands p = operands(h, w_down, nullptr, nullptr, s.d, s.F);
+  p.perm = perm;
+  p.arows = s.T;
+  p.Y = y;
+  p.gate = gate;
+  p.gstride = s.M;       // K = M slots per token (k_per_group == 1)
+  p.gslot = e_lo / G;    // the slot of this group
+  const GemmOperands none{};
+  st = launch_ggemm<false>(p, offsets, e_lo, e_hi - e_lo, rows_cap, none, 0, stream);
   return st == MOGE_OK ? ok() : st;
 }

@@ -15,7 +15,9 @@ reportify.cn for the shared expert):
                           moge_expert_gate_up_with_shared; float32 shapes use
                           moge_expert_gate_up / _down and a one-expert moge_grouped_ffn for
                           the shared expert
-  4. moge_combine         gate-weighted sum (+ shared output) -> y (float32)
+  4. moge_combine         gate-weighted sum (+ shared output) -> y (float32); for one whole group
+                          with K' = 1 and no shared expert GEMM 2 writes y itself
+                          (moge_expert_down_combine)
   5. moge_imbalance       per-group load and imbalance score (0 by construction)
   6. moge_route GLOBAL    the conventional top-K comparator from the stored scores,
      moge_dispatch        its counts only, and moge_imbalance of that load -- with expert
@@ -52,6 +54,11 @@ class MoGELayer:
         if gather and not can_gather:
             raise ValueError("reading rows through perm needs bf16, d % 32 == 0 and F > 0")
         self.gather = can_gather if gather is None else bool(gather)
+        # one whole group with K' = 1 and no shared expert: every token owns exactly one row, so
+        # GEMM 2's epilogue writes y itself (moge_expert_down_combine) and no combine pass runs
+        G = N // M
+        self.fuse_combine = (dtype == "bf16" and F > 0 and not F_shared and Kp == 1 and self.e_lo % G == 0
+                             and self.e_hi == self.e_lo + G)
         self.comparator = comparator
         self.routing_only = F == 0
         dev = torch.device(device)
@@ -86,7 +93,7 @@ class MoGELayer:
             self.perm = torch.empty(R, **i32)
             self.x_perm = None if self.gather else torch.empty(L.tiled_elems(R, d), dtype=self.tdtype, device=dev)
             self.h = torch.empty(L.tiled_elems(R, F), dtype=self.tdtype, device=dev)
-            self.o = torch.empty(R, d, dtype=self.tdtype, device=dev)
+            self.o = None if self.fuse_combine else torch.empty(R, d, dtype=self.tdtype, device=dev)
             self.y = torch.empty(T, d, **f32)
         if F_shared:
             self.sshape = L.Shape(T, d, 1, 1, 1, F_shared, self.dtype_code)
@@ -145,6 +152,9 @@ class MoGELayer:
                 if Fs:
                     L.expert_down_with_shared(s, Fs, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down,
                                               self.o, self.sh, shared[2], self.so, stream)
+                elif self.fuse_combine:
+                    L.expert_down_combine(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down,
+                                          self.perm, self.gate, self.y, stream)
                 else:
                     L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o,
                                   stream)
@@ -167,16 +177,21 @@ class MoGELayer:
                     L.expert_gate_up(s, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate,
                                      w_up, self.h, stream)
                     mk("gate_up")
-                    L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o,
-                                  stream)
+                    if self.fuse_combine:
+                        L.expert_down_combine(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down,
+                                              self.perm, self.gate, self.y, stream)
+                    else:
+                        L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o,
+                                      stream)
                     mk("down")
                     if self.F_shared:
                         L.grouped_ffn(self.sshape, self.x_tiled, self.soffsets, 0, 1, self.T, shared[0], shared[1],
                                       shared[2], self.sh, self.so, stream)
                         mk("shared")
-            L.combine(s, self.o, self.inv, self.gate, self.rows_cap, self.so if self.F_shared else None, self.y,
-                      stream)
-            mk("combine")
+            if not self.fuse_combine:
+                L.combine(s, self.o, self.inv, self.gate, self.rows_cap, self.so if self.F_shared else None, self.y,
+                          stream)
+                mk("combine")
         L.imbalance(s, self.counts, self.group_load, self.is_raw, self.is_norm, stream)
         mk("imbalance")
         if self.comparator:

@@ -140,6 +140,18 @@ def test_null_and_argument_errors_before_any_launch():
     assert g(sg, fake, fake, fake, 0, 8, 64, fake, fake, fake, 0, None, None, fake, None) == 1     # hs without F_s
     assert g(sg, fake, fake, fake, 0, 9, 64, fake, fake, fake, 0, None, None, None, None) == 1     # e_hi > N
     assert g(sg, fake, fake, fake, 0, 8, 0, fake, fake, fake, 0, None, None, None, None) == 7      # rows_cap
+    lib.moge_expert_down_combine.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P, P, P, P, P]
+    dc = lib.moge_expert_down_combine
+    grp = ctypes.byref(S(N=8, M=4, Kp=1))                                                # groups of 2 experts
+    assert dc(ctypes.byref(S(N=8, M=4, Kp=1, dt=moge.F32)), fake, fake, 2, 4, 64, fake, fake, fake, fake,
+              None) == 5                                                                  # bf16 only
+    assert dc(ctypes.byref(S(N=8, M=4, Kp=2)), fake, fake, 2, 4, 64, fake, fake, fake, fake, None) == 1  # K' = 2
+    assert dc(grp, fake, fake, 2, 3, 64, fake, fake, fake, fake, None) == 1              # half a group
+    assert dc(grp, fake, fake, 1, 3, 64, fake, fake, fake, fake, None) == 1              # straddles two groups
+    assert dc(grp, fake, fake, 0, 8, 64, fake, fake, fake, fake, None) == 1              # all groups
+    assert dc(grp, fake, fake, 2, 4, 64, fake, fake, None, fake, None) == 3              # no gate
+    assert dc(grp, fake, fake, 2, 4, 64, fake, None, fake, fake, None) == 3              # no perm
+    assert dc(grp, fake, fake, 2, 4, 0, fake, fake, fake, fake, None) == 7               # rows_cap
     lib.moge_combine.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P]
     assert lib.moge_combine(sp, fake, fake, None, 64, None, fake, None) == 3
     assert lib.moge_combine(sp, fake, fake, fake, 0, None, fake, None) == 7

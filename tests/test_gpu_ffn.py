@@ -223,3 +223,38 @@ def test_gathered_gate_up_bitexact(gpu, w):
     if Fs:   # rows T .. (rounded up to 16) of the tiled hs are never written
         assert torch.equal(H.untile_rows(hs1, w.T, Fs, keep_pad_cols=True),
                            H.untile_rows(hs2, w.T, Fs, keep_pad_cols=True))
+
+
+@pytest.mark.parametrize("w", [
+    W.variant(MID, name="fused_group1_T333", T=333, Kp=1, e_lo=4, e_hi=8),
+    W.variant(MID, name="fused_group0_T2000_N64", T=2000, d=256, N=64, M=8, Kp=1, F=136, e_lo=0, e_hi=8,
+              std_bias=2.0),
+    W.variant(MID, name="fused_T1", T=1, Kp=1, e_lo=12, e_hi=16),
+], ids=lambda w: w.name)
+def test_down_combine_bitexact(gpu, w):
+    # one whole group with K' = 1: GEMM 2 writing y itself equals GEMM 2 + the combine pass bit for bit
+    dv = H.device_inputs(w)
+    hi = H.HostInputs(w)
+    idx, gate, _ = oracle.route(H.oracle_logits_all(hi), w.M, w.Kp, "grouped")
+    s = moge.Shape(w.T, w.d, w.N, w.M, w.Kp, w.F, moge.BF16)
+    cap = moge.rows_bound(s, moge.ROUTE_GROUPED, w.e_lo, w.e_hi)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    counts, offsets = torch.empty(w.N, **i32), torch.empty(w.N + 1, **i32)
+    inv, perm = torch.empty(w.T, w.K, **i32), torch.empty(cap, **i32)
+    ws = torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda")
+    moge.dispatch(s, moge.ROUTE_GROUPED, torch.from_numpy(idx).cuda(), None, w.e_lo, w.e_hi, cap, counts, offsets,
+                  inv, perm, None, ws)
+    pg, pu, pd = _pack(moge.BF16, dv.w_gate), _pack(moge.BF16, dv.w_up), _pack(moge.BF16, dv.w_down)
+    h = torch.empty(moge.tiled_elems(cap, w.F), **bf)
+    moge.expert_gate_up_gather(s, dv.x, perm, offsets, w.e_lo, w.e_hi, cap, pg, pu, h)
+    g = torch.from_numpy(gate.astype(np.float32)).cuda()
+    o = torch.empty(cap, w.d, **bf)
+    y1 = torch.full((w.T, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    y2 = torch.full((w.T, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    moge.expert_down(s, h, offsets, w.e_lo, w.e_hi, cap, pd, o)
+    moge.combine(s, o, inv, g, cap, None, y1)
+    moge.expert_down_combine(s, h, offsets, w.e_lo, w.e_hi, cap, pd, perm, g, y2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y2).all()                       # every token's row written
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))

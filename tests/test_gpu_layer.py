@@ -91,6 +91,13 @@ def test_layer_shared_tiled_rows(gpu):
     assert not layer.gather
 
 
+def test_layer_one_group_combined_in_gemm(gpu):
+    # one device's share of one group with K' = 1: GEMM 2 writes y (no combine pass)
+    w = W.variant(W.decode(), name="group1_fused", T=300, Kp=1, e_lo=8, e_hi=16, std_bias=1.0)
+    layer, _ = check_layer(w)
+    assert layer.fuse_combine and layer.o is None
+
+
 def test_layer_decode(gpu):
     check_layer(W.decode())
 
