@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--workload", default="ultra", choices=["ultra", "group0", "decode", "routing", "tiny", "pro"])
     p.add_argument("--rows", default="auto", choices=["auto", "gather", "copy"],
                    help="gate/up token rows: read from x through perm, or copied by dispatch (auto: the layer's choice)")
+    p.add_argument("--tiles", default="auto", choices=["auto", "tall", "wide"],
+                   help="expert-GEMM tile shape: 320x256 (tall), 96x512 (wide), or the library's choice")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -192,6 +194,7 @@ def main():
     import numpy as np
     import torch
 
+    import mixture_grouped_experts_amd as moge
     from mixture_grouped_experts_amd.layer import MoGELayer
     from synth import workloads as W
     from tests import moge_harness as H
@@ -203,6 +206,7 @@ def main():
     dv = H.device_inputs(w)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi,
                       gather={"auto": None, "gather": True, "copy": False}[args.rows])
+    moge.set_gemm_tiles({"auto": moge.TILES_AUTO, "tall": moge.TILES_TALL, "wide": moge.TILES_WIDE}[args.tiles])
     if w.F:
         # expert weights are packed once, at load time (outside the timed steps)
         (pg, pu, pd), ps = layer.pack_expert_weights(dv.w_gate, dv.w_up, dv.w_down, dv.shared)
@@ -293,7 +297,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "M": w.M, "k_per_group": w.Kp, "F": w.F,
                    "F_shared": w.F_shared, "experts_computed": [w.e_lo, w.e_hi], "seed": w.seed,
-                   "rows": "gather" if layer.gather else "copy"},
+                   "rows": "gather" if layer.gather else "copy",
+                   "tiles": (args.tiles if args.tiles != "auto"
+                             else "wide" if w.T * w.M * w.Kp <= 64 * w.N else "tall")},
         "roofline": roof,
         "stages": stages,
         "imbalance": {"moge_is_raw": int(layer.is_raw.item()),

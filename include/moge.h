@@ -285,6 +285,23 @@ moge_status_t moge_expert_down_combine(const moge_shape_t* shape, const void* h,
                                        const int32_t* perm, const float* gate, float* y, hipStream_t stream);
 
 /*
+ * moge_set_gemm_tiles -- the tile shape of the bf16 expert GEMMs for the calls that
+ * follow, process-wide (a tuning and testing knob; the default needs no call).
+ *   MOGE_TILES_AUTO  320 x 256 tiles, or 96 x 512 when the routed experts average
+ *                    at most 64 rows (T * M * k_per_group <= 64 * N): few rows per
+ *                    expert (decode), where the wide tiles keep twice the weight
+ *                    bytes in flight per CU -- the grouped matmul's switch to a
+ *                    matrix-vector-like mode by workload ([P1] section 3, SwiftGMM).
+ *   MOGE_TILES_TALL  always 320 x 256;  MOGE_TILES_WIDE  always 96 x 512.
+ * Every output is bit-identical under all three (same reduction order).
+ * Errors: MOGE_ERR_ARG for any other value.
+ */
+#define MOGE_TILES_AUTO 0
+#define MOGE_TILES_TALL 1
+#define MOGE_TILES_WIDE 2
+moge_status_t moge_set_gemm_tiles(int32_t tiles);
+
+/*
  * moge_combine -- gate-weighted sum of the expert outputs back in token order.
  *   y[t] = sum over slots s (in slot order) with inv[t][s] >= 0 of
  *          gate[t][s] * o[inv[t][s]]   (+ shared_out[t] when not NULL), in float32.

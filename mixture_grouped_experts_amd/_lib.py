@@ -29,11 +29,15 @@ F32 = 1
 ROUTE_GROUPED = 0
 ROUTE_GLOBAL = 1
 STAGE_DISPATCH = 1
+TILES_AUTO = 0
+TILES_TALL = 1
+TILES_WIDE = 2
 
 EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_weight_elems",
            "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_grouped_ffn",
            "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
-           "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_expert_down_combine", "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_version",
+           "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_expert_down_combine",
+           "moge_set_gemm_tiles", "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_version",
            "moge_last_error")
 
 
@@ -92,6 +96,8 @@ _lib.moge_expert_gate_up_gather.argtypes = [_SP, _P, _P, _P, _I32, _I32, _I64, _
 _lib.moge_expert_gate_up_gather.restype = ctypes.c_int
 _lib.moge_expert_down_combine.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P]
 _lib.moge_expert_down_combine.restype = ctypes.c_int
+_lib.moge_set_gemm_tiles.argtypes = [_I32]
+_lib.moge_set_gemm_tiles.restype = ctypes.c_int
 _lib.moge_combine.argtypes = [_SP, _P, _P, _P, _I64, _P, _P, _P]
 _lib.moge_combine.restype = ctypes.c_int
 _lib.moge_imbalance.argtypes = [_SP, _P, _P, _P, _P, _P]
@@ -274,6 +280,11 @@ def expert_gate_up_gather(shape: Shape, x, perm, offsets, e_lo: int, e_hi: int, 
         _ptr(ws_up, "ws_up", et, packed_weight_elems(F_shared, d) if F_shared else 0, optional=True),
         _ptr(hs, "hs", et, tiled_elems(T, F_shared) if F_shared else 0, optional=True), _stream(stream))
     _check("moge_expert_gate_up_gather", st)
+
+
+def set_gemm_tiles(tiles: int) -> None:
+    """Process-wide tile shape of the bf16 expert GEMMs: TILES_AUTO (default), TILES_TALL or TILES_WIDE."""
+    _check("moge_set_gemm_tiles", _lib.moge_set_gemm_tiles(tiles))
 
 
 def expert_down_combine(shape: Shape, h, offsets, e_lo: int, e_hi: int, rows_cap: int, w_down, perm, gate, y,

@@ -44,18 +44,41 @@
 // shapes only).
 #include <math.h>
 
+#include <atomic>
+
 #include "moge_internal.hpp"
 
 namespace moge {
 
-constexpr int kBM = 320;                    // token rows per tile (10 blocks of 32)
-constexpr int kBW = 256;                    // weight rows per tile
 constexpr int kBK = 32;                     // reduction step (elements)
 constexpr int kRowB = kBK * 2;              // 64-byte LDS rows (unpadded; chunks are XOR-swizzled)
-constexpr int kStageB = (kBM + kBW) * kRowB;  // 36 KiB per stage
 constexpr int kStages = 4;
-constexpr size_t kGemmLds = (size_t)kStages * kStageB;  // 144 KiB
 constexpr int kThreads = 512;               // 8 waves: two per SIMD
+constexpr int kMaxBM = 320;                 // largest token-row tile
+
+// Two tile shapes; every wave owns 2 weight blocks of 32 rows and the token blocks
+// wm, wm + WMG, wm + 2 WMG, ... of the tile (WMG wave rows x 8 / WMG wave columns):
+//   WMG = 2: 320 token rows x 256 weight rows (5 token blocks per wave) -- the
+//            general case, where an expert's rows fill a 320-row tile;
+//   WMG = 1: 96 token rows x 512 weight rows (3 token blocks per wave) -- few rows
+//            per expert (decode): twice the weight bytes per step, so each CU keeps
+//            twice as many weight bytes in flight and the weight stream runs nearer
+//            the HBM rate.
+// Both stage 64-byte rows of BM + BW rows per step in a 4-stage ring.
+template <int WMG>
+struct TileShape;
+template <>
+struct TileShape<2> {
+  static constexpr int kBlocks = 5, BM = 320, BW = 256;
+};
+template <>
+struct TileShape<1> {
+  static constexpr int kBlocks = 3, BM = 96, BW = 512;
+};
+template <int WMG>
+constexpr int stage_bytes() { return (TileShape<WMG>::BM + TileShape<WMG>::BW) * kRowB; }  // 36 / 38 KiB
+template <int WMG>
+constexpr size_t gemm_lds() { return (size_t)kStages * stage_bytes<WMG>(); }  // 144 / 152 KiB
 constexpr int kGroupM = 4;                  // m-tiles per scheduling group
 
 __device__ __forceinline__ int swz(int r) { return lds_swz(r); }
@@ -113,30 +136,38 @@ struct GemmOperands {
 // the row-major x through perm (16 rows x 64 B per instruction), which saves
 // materialising x_perm at all.
 
-template <bool SWIGLU, int NL>
+template <bool SWIGLU, int NL, int WMG>
 __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __restrict__ lds,
                                              const uint16_t* __restrict__ A, int64_t mband0,
                                              const uint16_t* __restrict__ wbase0, const uint16_t* __restrict__ wbase1,
                                              int wbands, int nkf, int mrows, int64_t row0, int n0, int NOUT, int NPAD,
                                              uint16_t* __restrict__ C) {
+  constexpr int BM = TileShape<WMG>::BM, BW = TileShape<WMG>::BW, NB = TileShape<WMG>::kBlocks;
+  constexpr int kStageB = stage_bytes<WMG>();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
-  const int wm = wave & 1, wn = wave >> 1;
-  // DMA sources: instruction j < 4 moves the 16 stage rows at lrow[j] .. +16 (one
-  // tile of 16 rows x 32 columns); waves 4-7 have a fifth instruction (token rows
-  // 256.. of the tile).  Lane l brings 16 bytes of row lrow[j] + l/4.
-  const bool wtok = wave < 4;
+  const int wm = wave % WMG, wn = wave / WMG;
+  // DMA sources: instruction j moves the 16 stage rows at lrow[j] .. +16 (one tile of
+  // 16 rows x 32 columns); lane l brings 16 bytes of row lrow[j] + l/4.
+  //   320 x 256: waves 0-3 move token rows wave*64 .. +64 (4 instructions); waves
+  //              4-7 weight rows (wave-4)*64 .. +64 and token rows 256 + (wave-4)*16;
+  //   96 x 512:  every wave moves weight rows wave*64 .. +64; waves 0-5 also token
+  //              rows wave*16 .. +16.
+  // wtok: this wave's first four instructions are token rows; five: it issues five.
+  const bool wtok = WMG == 2 && wave < 4;
+  const bool five = WMG == 2 ? wave >= 4 : wave < BM / kTileRows;
   const int live_bands = (mrows + kTileRows - 1) / kTileRows;
   const uint16_t* dsrc[5];
   int lrow[5];  // first stage row of each instruction (wave-uniform)
   const int astep = op.amode == kATiled ? kTileElems : kTileCols;  // token-row elements per step
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
-    lrow[j] = wtok ? wave * 64 + j * 16 : (j < 4 ? kBM + (wave - 4) * 64 + j * 16 : 256 + (wave - 4) * 16);
-    const int srow = lrow[j] + (lane >> 2);  // stage row (token rows 0..319, weight rows 320..575)
+    if (WMG == 2) lrow[j] = wtok ? wave * 64 + j * 16 : (j < 4 ? BM + (wave - 4) * 64 + j * 16 : 256 + (wave - 4) * 16);
+    else lrow[j] = j < 4 ? BM + wave * 64 + j * 16 : (five ? wave * 16 : 0);
+    const int srow = lrow[j] + (lane >> 2);  // stage row (token rows 0..BM-1, then weight rows)
     const int c = (lane & 3) ^ swz(srow);    // 16-byte chunk of the 32-column tile row fetched by this lane
     const int inner = (lane >> 2) * kTileCols + c * 8;
-    if (lrow[j] < kBM) {
+    if (lrow[j] < BM) {
       int band = lrow[j] / kTileRows;  // bands past the live rows re-read the last live band (never stored)
       if (band >= live_bands) band = live_bands - 1;
       if (op.amode == kATiled) {
@@ -148,10 +179,10 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
         dsrc[j] = A + tok * op.KP + c * 8;
       }
     } else {
-      const int r = lrow[j] - kBM;
-      int band = (SWIGLU ? n0 + (r & 127) : n0 + r) / kTileRows;
+      const int r = lrow[j] - BM;  // GEMM 1: rows < BW/2 are gate rows, the rest the up rows of the same columns
+      int band = (SWIGLU ? n0 + (r & (BW / 2 - 1)) : n0 + r) / kTileRows;
       if (band >= wbands) band = wbands - 1;
-      dsrc[j] = (SWIGLU && r >= 128 ? wbase1 : wbase0) + (int64_t)band * nkf * kTileElems + inner;
+      dsrc[j] = (SWIGLU && r >= BW / 2 ? wbase1 : wbase0) + (int64_t)band * nkf * kTileElems + inner;
     }
   }
   // Step ks into stage ks % 4 (steps past the last full step reload step 0); the
@@ -165,19 +196,19 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
     if (wtok) {  // four token-row instructions
 #pragma unroll
       for (int j = 0; j < 4; ++j) dma_16x64(dsrc[j] + offa, st + (uint32_t)(lrow[j] * kRowB));
-    } else {     // four weight-row instructions and one token-row instruction
+    } else {     // four weight-row instructions and (five) one token-row instruction
 #pragma unroll
       for (int j = 0; j < 4; ++j) dma_16x64_stream(dsrc[j] + offb, st + (uint32_t)(lrow[j] * kRowB));
-      dma_16x64(dsrc[4] + offa, st + (uint32_t)(lrow[4] * kRowB));
+      if (WMG == 2 || five) dma_16x64(dsrc[4] + offa, st + (uint32_t)(lrow[4] * kRowB));
     }
   };
   const int kc = (lane >> 5);  // logical chunk of this lane inside a 16-element sub-step
   int arow[5], brow[2];
 #pragma unroll
-  for (int t = 0; t < 5; ++t) arow[t] = (wm + 2 * t) * 32 + (lane & 31);
+  for (int t = 0; t < 5; ++t) arow[t] = (wm + WMG * t) * 32 + (lane & 31);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
-    brow[cb] = kBM + (SWIGLU ? cb * 128 + wn * 32 : wn * 64 + cb * 32) + (lane & 31);
+    brow[cb] = BM + (SWIGLU ? cb * (BW / 2) + wn * 32 : wn * 64 + cb * 32) + (lane & 31);
   auto frag = [&](int ks, int kk, bf16x8_t (&a)[5], bf16x8_t (&b)[2]) {
     const char* sa = lds + (ks % kStages) * kStageB;
     const char* sb = sa;
@@ -192,7 +223,7 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
                                                                              ((c ^ swz(arow[t])) << 4)));
   };
   f32x16_t acc[NL > 0 ? NL : 1][2];
-  static_assert(NL <= 5, "five row blocks per wave at most");
+  static_assert(NL <= NB, "row blocks per wave");
 #pragma unroll
   for (int t = 0; t < (NL > 0 ? NL : 1); ++t)
 #pragma unroll
@@ -212,9 +243,9 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   issue(0);
   issue(1);
   issue(2);
-  // step 0 landed (this wave; token waves issue 4 loads per step, the others 5)
-  if (wtok) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
+  // step 0 landed (this wave issues 4 or 5 loads per step)
+  if (five) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
   __syncthreads();
   for (int ks = 0; ks < nkf; ++ks) {
     issue(ks + 3);
@@ -234,8 +265,8 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
     }
     // step ks+1 landed (this wave) and this step's LDS reads are done, so the DMA
     // issued after the barrier may overwrite stage ks % 4
-    if (wtok) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(8));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(10));
+    if (five) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(10));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(8));
     __syncthreads();
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing reloads before LDS is reused
@@ -245,7 +276,7 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   // the zero rows of the packed weights); GEMM 2 writes row-major [row][NOUT].
 #pragma unroll
   for (int t = 0; t < NL; ++t) {
-    const int trow = (wm + 2 * t) * 32 + (lane & 31);
+    const int trow = (wm + WMG * t) * 32 + (lane & 31);
     if (trow < mrows) {
       const int64_t row = row0 + trow;
       int64_t ytok = -1;
@@ -343,10 +374,11 @@ __device__ __forceinline__ void expert_segments(const int32_t* __restrict__ offs
 // evenly through the list was measured to cost 50% more HBM reads: tiles of unequal
 // length let the workgroups drift apart, so the 16 column tiles of a routed expert no
 // longer run together and its row panel leaves L2 between uses.)
-template <bool SWIGLU>
+template <bool SWIGLU, int WMG>
 __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, const int32_t* __restrict__ offsets,
                                                               int e_lo, int E, int64_t rows_cap, GemmOperands p1,
                                                               int rows1) {
+  constexpr int kBM = TileShape<WMG>::BM, kBW = TileShape<WMG>::BW;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int tp[kMaxExperts];     // inclusive prefix of tiles per expert
   __shared__ int erow[kMaxExperts];   // rows per expert, clipped to rows_cap
@@ -407,15 +439,16 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
     const int npad = (int)round_up(op.NOUT, kTileCols);
     const int nkf = op.KP / kTileCols;
 
-    // live row blocks of this wave (wave-uniform): block wm + 2t is live if it starts below mrows
-    const int wm = wave & 1;
+    // live row blocks of this wave (wave-uniform): block wm + WMG t is live if it starts below mrows
+    const int wm = wave % WMG;
     const int nrb = (mrows + 31) / 32;
-    const int nl = nrb > wm ? (nrb - wm + 1) / 2 : 0;
+    const int nl = nrb > wm ? (nrb - wm + WMG - 1) / WMG : 0;
 #define MOGE_TILE(NLV)                                                                                          \
-  tile_compute<SWIGLU, NLV>(op, lds, op.A, mband0, wb0, wb1, wbands, nkf, mrows, row0, ncol0, op.NOUT, npad, op.C)
+  tile_compute<SWIGLU, NLV, WMG>(op, lds, op.A, mband0, wb0, wb1, wbands, nkf, mrows, row0, ncol0, op.NOUT, npad, \
+                                 op.C)
     switch (nl) {
-      case 5: MOGE_TILE(5); break;
-      case 4: MOGE_TILE(4); break;
+      case 5: if constexpr (TileShape<WMG>::kBlocks >= 5) MOGE_TILE(5); break;
+      case 4: if constexpr (TileShape<WMG>::kBlocks >= 4) MOGE_TILE(4); break;
       case 3: MOGE_TILE(3); break;
       case 2: MOGE_TILE(2); break;
       case 1: MOGE_TILE(1); break;
@@ -498,21 +531,40 @@ static int device_cus() {
 }
 
 // rows1 = 0: routed problem only.
-template <bool SWIGLU>
-static moge_status_t launch_ggemm(const GemmOperands& p0, const int32_t* offsets, int e_lo, int E, int64_t rows_cap,
-                                  const GemmOperands& p1, int rows1, hipStream_t stream) {
-  moge_status_t st = raise_dynamic_lds(reinterpret_cast<const void*>(ggemm_bf16_kernel<SWIGLU>), kGemmLds,
+template <bool SWIGLU, int WMG>
+static moge_status_t launch_ggemm_shape(const GemmOperands& p0, const int32_t* offsets, int e_lo, int E,
+                                        int64_t rows_cap, const GemmOperands& p1, int rows1, hipStream_t stream) {
+  constexpr int kBM = TileShape<WMG>::BM, kBW = TileShape<WMG>::BW;
+  moge_status_t st = raise_dynamic_lds(reinterpret_cast<const void*>(ggemm_bf16_kernel<SWIGLU, WMG>), gemm_lds<WMG>(),
                                        "ggemm_bf16_kernel");
   if (st != MOGE_OK) return st;
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
   const int64_t upper = ((rows_cap + kBM - 1) / kBM + E) * ((p0.NOUT + BNO - 1) / BNO) +
                         ((int64_t)rows1 + kBM - 1) / kBM * ((p1.NOUT + BNO - 1) / BNO);  // >= live tiles
-  int64_t grid = device_cus();  // one 144 KiB-LDS workgroup per CU
+  int64_t grid = device_cus();  // one 144-152 KiB-LDS workgroup per CU
   if (upper < grid) grid = upper;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL(ggemm_bf16_kernel<SWIGLU>, dim3((unsigned)grid), dim3(kThreads), kGemmLds, stream, p0, offsets,
-                     e_lo, E, rows_cap, p1, rows1);
+  hipLaunchKernelGGL((ggemm_bf16_kernel<SWIGLU, WMG>), dim3((unsigned)grid), dim3(kThreads), gemm_lds<WMG>(), stream,
+                     p0, offsets, e_lo, E, rows_cap, p1, rows1);
   return check_launch(SWIGLU ? "ggemm_bf16_kernel<gate_up>" : "ggemm_bf16_kernel<down>");
+}
+
+static std::atomic<int> g_tiles{MOGE_TILES_AUTO};
+
+// The tile shape: the 96 x 512 tiles when the routed experts average at most 64 rows
+// (T K / N, exact per group under MoGE routing), else 320 x 256; or as set by
+// moge_set_gemm_tiles.
+static bool wide_tiles(const moge_shape_t& s) {
+  const int t = g_tiles.load(std::memory_order_relaxed);
+  if (t != MOGE_TILES_AUTO) return t == MOGE_TILES_WIDE;
+  return (int64_t)s.T * s.M * s.k_per_group <= (int64_t)64 * s.N;
+}
+
+template <bool SWIGLU>
+static moge_status_t launch_ggemm(const moge_shape_t& s, const GemmOperands& p0, const int32_t* offsets, int e_lo,
+                                  int E, int64_t rows_cap, const GemmOperands& p1, int rows1, hipStream_t stream) {
+  if (wide_tiles(s)) return launch_ggemm_shape<SWIGLU, 1>(p0, offsets, e_lo, E, rows_cap, p1, rows1, stream);
+  return launch_ggemm_shape<SWIGLU, 2>(p0, offsets, e_lo, E, rows_cap, p1, rows1, stream);
 }
 
 static GemmOperands operands(const void* A, const void* B0, const void* B1, void* C, int NOUT, int KD,
@@ -532,7 +584,7 @@ static moge_status_t ffn_common_checks(const moge_shape_t* shape, int32_t e_lo, 
   if (shape->F <= 0) return fail(MOGE_ERR_SHAPE, "the expert FFN needs F > 0");
   if (e_lo < 0 || e_hi > shape->N || e_lo >= e_hi) return fail(MOGE_ERR_ARG, "need 0 <= e_lo < e_hi <= N");
   if (rows_cap < 1) return fail(MOGE_ERR_CAPACITY, "rows_cap must be >= 1");
-  if (rows_cap >= (int64_t(1) << 31) - kBM) return fail(MOGE_ERR_CAPACITY, "rows_cap must be < 2^31 - 320");
+  if (rows_cap >= (int64_t(1) << 31) - kMaxBM) return fail(MOGE_ERR_CAPACITY, "rows_cap must be < 2^31 - 320");
   return MOGE_OK;
 }
 
@@ -551,7 +603,7 @@ extern "C" moge_status_t moge_expert_gate_up(const moge_shape_t* shape, const vo
   const moge_shape_t& s = *shape;
   if (s.dtype == MOGE_BF16) {
     const GemmOperands none{};
-    st = launch_ggemm<true>(operands(x_perm, w_gate, w_up, h, s.F, s.d), offsets, e_lo, e_hi - e_lo, rows_cap, none,
+    st = launch_ggemm<true>(s, operands(x_perm, w_gate, w_up, h, s.F, s.d), offsets, e_lo, e_hi - e_lo, rows_cap, none,
                             0, stream);
   } else {
     hipLaunchKernelGGL(ffn_f32_gateup_kernel, dim3((unsigned)grid_1d(rows_cap * round_up(s.F, kTileCols))), dim3(256),
@@ -572,7 +624,7 @@ extern "C" moge_status_t moge_expert_down(const moge_shape_t* shape, const void*
   const moge_shape_t& s = *shape;
   if (s.dtype == MOGE_BF16) {
     const GemmOperands none{};
-    st = launch_ggemm<false>(operands(h, w_down, nullptr, out, s.d, s.F), offsets, e_lo, e_hi - e_lo, rows_cap, none,
+    st = launch_ggemm<false>(s, operands(h, w_down, nullptr, out, s.d, s.F), offsets, e_lo, e_hi - e_lo, rows_cap, none,
                              0, stream);
   } else {
     hipLaunchKernelGGL(ffn_f32_down_kernel, dim3((unsigned)grid_1d(rows_cap * s.d)), dim3(256), 0, stream,
@@ -614,7 +666,7 @@ extern "C" moge_status_t moge_expert_gate_up_with_shared(const moge_shape_t* sha
   if (!x_perm || !offsets || !w_gate || !w_up || !h || !x_tiled || !ws_gate || !ws_up || !hs)
     return fail(MOGE_ERR_NULL, "every operand is required");
   const moge_shape_t& s = *shape;
-  st = launch_ggemm<true>(operands(x_perm, w_gate, w_up, h, s.F, s.d), offsets, e_lo, e_hi - e_lo, rows_cap,
+  st = launch_ggemm<true>(s, operands(x_perm, w_gate, w_up, h, s.F, s.d), offsets, e_lo, e_hi - e_lo, rows_cap,
                           operands(x_tiled, ws_gate, ws_up, hs, F_shared, s.d), s.T, stream);
   return st == MOGE_OK ? ok() : st;
 }
@@ -628,7 +680,7 @@ extern "C" moge_status_t moge_expert_down_with_shared(const moge_shape_t* shape,
   if (!h || !offsets || !w_down || !out || !hs || !ws_down || !out_shared)
     return fail(MOGE_ERR_NULL, "every operand is required");
   const moge_shape_t& s = *shape;
-  st = launch_ggemm<false>(operands(h, w_down, nullptr, out, s.d, s.F), offsets, e_lo, e_hi - e_lo, rows_cap,
+  st = launch_ggemm<false>(s, operands(h, w_down, nullptr, out, s.d, s.F), offsets, e_lo, e_hi - e_lo, rows_cap,
                            operands(hs, ws_down, nullptr, out_shared, s.d, F_shared), s.T, stream);
   return st == MOGE_OK ? ok() : st;
 }
@@ -651,7 +703,7 @@ extern "C" moge_status_t moge_expert_gate_up_gather(const moge_shape_t* shape, c
     return fail(MOGE_ERR_NULL, "ws_gate, ws_up and hs are required when F_shared > 0");
   if (F_shared == 0 && (ws_gate || ws_up || hs)) return fail(MOGE_ERR_ARG, "F_shared == 0 takes no shared operands");
   const GemmOperands none{};
-  st = launch_ggemm<true>(operands(x, w_gate, w_up, h, s.F, s.d, kAGather, perm, s.T), offsets, e_lo, e_hi - e_lo,
+  st = launch_ggemm<true>(s, operands(x, w_gate, w_up, h, s.F, s.d, kAGather, perm, s.T), offsets, e_lo, e_hi - e_lo,
                           rows_cap,
                           F_shared ? operands(x, ws_gate, ws_up, hs, F_shared, s.d, kARows, nullptr, s.T) : none,
                           F_shared ? s.T : 0, stream);
@@ -679,6 +731,13 @@ extern "C" moge_status_t moge_expert_down_combine(const moge_shape_t* shape, con
   p.gstride = s.M;       // K = M slots per token (k_per_group == 1)
   p.gslot = e_lo / G;    // the slot of this group
   const GemmOperands none{};
-  st = launch_ggemm<false>(p, offsets, e_lo, e_hi - e_lo, rows_cap, none, 0, stream);
+  st = launch_ggemm<false>(s, p, offsets, e_lo, e_hi - e_lo, rows_cap, none, 0, stream);
   return st == MOGE_OK ? ok() : st;
+}
+
+extern "C" moge_status_t moge_set_gemm_tiles(int32_t tiles) {
+  if (tiles != MOGE_TILES_AUTO && tiles != MOGE_TILES_TALL && tiles != MOGE_TILES_WIDE)
+    return fail(MOGE_ERR_ARG, "tiles must be MOGE_TILES_AUTO, MOGE_TILES_TALL or MOGE_TILES_WIDE");
+  g_tiles.store(tiles, std::memory_order_relaxed);
+  return ok();
 }

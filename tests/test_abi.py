@@ -152,6 +152,9 @@ def test_null_and_argument_errors_before_any_launch():
     assert dc(grp, fake, fake, 2, 4, 64, fake, fake, None, fake, None) == 3              # no gate
     assert dc(grp, fake, fake, 2, 4, 64, fake, None, fake, fake, None) == 3              # no perm
     assert dc(grp, fake, fake, 2, 4, 0, fake, fake, fake, fake, None) == 7               # rows_cap
+    lib.moge_set_gemm_tiles.argtypes = [ctypes.c_int32]
+    assert lib.moge_set_gemm_tiles(3) == 1 and lib.moge_set_gemm_tiles(-1) == 1
+    assert lib.moge_set_gemm_tiles(0) == 0                                               # back to the default
     lib.moge_combine.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P]
     assert lib.moge_combine(sp, fake, fake, None, 64, None, fake, None) == 3
     assert lib.moge_combine(sp, fake, fake, fake, 0, None, fake, None) == 7

@@ -258,3 +258,53 @@ def test_down_combine_bitexact(gpu, w):
     torch.cuda.synchronize()
     assert torch.isfinite(y2).all()                       # every token's row written
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("w", [
+    W.decode(),                                                                          # 64 rows per expert
+    W.variant(MID, name="tiles_shared_T333", F_shared=136, std_shared_down=0.02, T=333),
+    W.variant(MID, name="tiles_range_T700", T=700, e_lo=3, e_hi=11, F=1408),
+    W.variant(MID, name="tiles_group_fused", T=333, Kp=1, e_lo=4, e_hi=8),
+], ids=lambda w: w.name)
+def test_tile_shapes_bitexact(gpu, w):
+    # the 320 x 256 and the 96 x 512 tiles compute every output element identically
+    dv = H.device_inputs(w)
+    hi = H.HostInputs(w)
+    idx, gate, _ = oracle.route(H.oracle_logits_all(hi), w.M, w.Kp, "grouped")
+    s = moge.Shape(w.T, w.d, w.N, w.M, w.Kp, w.F, moge.BF16)
+    cap = moge.rows_bound(s, moge.ROUTE_GROUPED, w.e_lo, w.e_hi)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    counts, offsets = torch.empty(w.N, **i32), torch.empty(w.N + 1, **i32)
+    inv, perm = torch.empty(w.T, w.K, **i32), torch.empty(cap, **i32)
+    ws = torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda")
+    moge.dispatch(s, moge.ROUTE_GROUPED, torch.from_numpy(idx).cuda(), None, w.e_lo, w.e_hi, cap, counts, offsets,
+                  inv, perm, None, ws)
+    pg, pu, pd = _pack(moge.BF16, dv.w_gate), _pack(moge.BF16, dv.w_up), _pack(moge.BF16, dv.w_down)
+    Fs = w.F_shared
+    sg, su, sd = (_pack(moge.BF16, m.unsqueeze(0)) for m in dv.shared) if Fs else (None, None, None)
+    g = torch.from_numpy(gate.astype(np.float32)).cuda()
+    fused = w.Kp == 1 and not Fs and w.e_hi - w.e_lo == w.N // w.M and w.e_lo % (w.N // w.M) == 0
+    outs = []
+    try:
+        for tiles in (moge.TILES_TALL, moge.TILES_WIDE):
+            moge.set_gemm_tiles(tiles)
+            h = torch.zeros(moge.tiled_elems(cap, w.F), **bf)
+            hs = torch.zeros(moge.tiled_elems(w.T, Fs), **bf) if Fs else None
+            o = torch.zeros(cap, w.d, **bf)
+            so = torch.zeros(w.T, w.d, **bf) if Fs else None
+            y = torch.zeros(w.T, w.d, dtype=torch.float32, device="cuda")
+            moge.expert_gate_up_gather(s, dv.x, perm, offsets, w.e_lo, w.e_hi, cap, pg, pu, h, Fs, sg, su, hs)
+            if Fs:
+                moge.expert_down_with_shared(s, Fs, h, offsets, w.e_lo, w.e_hi, cap, pd, o, hs, sd, so)
+            else:
+                moge.expert_down(s, h, offsets, w.e_lo, w.e_hi, cap, pd, o)
+            if fused:
+                moge.expert_down_combine(s, h, offsets, w.e_lo, w.e_hi, cap, pd, perm, g, y)
+            torch.cuda.synchronize()
+            outs.append((h, o, hs, so, y))
+    finally:
+        moge.set_gemm_tiles(moge.TILES_AUTO)
+    for a, b in zip(*outs):
+        if a is not None:
+            assert torch.equal(a, b)
