@@ -114,7 +114,8 @@ struct GemmOperands {
 };
 
 // One tile: reduction loop and epilogue, 8 waves.  Wave (wm, wn), wm in {0,1},
-// wn in {0..3}, owns the token row blocks wm, wm+2, ..., wm+8 (32 rows each,
+// wn in {0..3} (320 x 256 tiles; wm = wave / 4, so each SIMD runs one wave of each
+// half), owns the token row blocks wm, wm+2, ..., wm+8 (32 rows each,
 // interleaved so a partly filled tile keeps the waves balanced) and 2 weight
 // blocks of 32 rows (GEMM 1: the gate and the up rows of the same 32 h columns;
 // GEMM 2: 64 output columns).  NL of its row blocks hold live rows; the others
@@ -146,7 +147,9 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   constexpr int kStageB = stage_bytes<WMG>();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
-  const int wm = wave % WMG, wn = wave / WMG;
+  // the two waves on a SIMD (w and w + 4) take different token-row halves, so an odd
+  // number of live row blocks still gives every SIMD the same MFMA count
+  const int wm = WMG == 2 ? wave >> 2 : 0, wn = WMG == 2 ? wave & 3 : wave;
   // DMA sources: instruction j moves the 16 stage rows at lrow[j] .. +16 (one tile of
   // 16 rows x 32 columns); lane l brings 16 bytes of row lrow[j] + l/4.
   //   320 x 256: waves 0-3 move token rows wave*64 .. +64 (4 instructions); waves
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
     const int nkf = op.KP / kTileCols;
 
     // live row blocks of this wave (wave-uniform): block wm + WMG t is live if it starts below mrows
-    const int wm = wave % WMG;
+    const int wm = WMG == 2 ? wave >> 2 : 0;
     const int nrb = (mrows + 31) / 32;
     const int nl = nrb > wm ? (nrb - wm + WMG - 1) / WMG : 0;
 #define MOGE_TILE(NLV)                                                                                          \

@@ -199,7 +199,15 @@ __device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int 
 // of loads in flight per workgroup and no staging registers; x is read exactly
 // once.  One barrier per step.  The epilogue keeps the TM x NP score tile in LDS
 // for the softmax and the per-group choice.
-template <int TM, int NP, int S, int WV>
+//
+// PARTS > 1 (N > 128, scores stored): the experts are split in PARTS slices of NP;
+// workgroup b computes slice b % PARTS of token tile b / PARTS and only writes its
+// scores, and a second pass (route_select_kernel) makes the choice.  Workgroup b
+// runs on XCD b % 8, so each XCD needs only its slice of the router matrix (1-2 MB
+// at N = 256, d = 7680), which then stays in that XCD's 4 MB L2 instead of being
+// fetched from the last-level cache by every workgroup, and the tile can take more
+// tokens, so more of each step's loads are token rows streaming from HBM.
+template <int TM, int NP, int S, int WV, int PARTS>
 __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, int N, int n_groups, int k,
                                                         const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ w,
@@ -218,7 +226,8 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tb = wave % TB, es = wave / TB;
-  const int64_t t0 = (int64_t)blockIdx.x * TM;
+  const int64_t t0 = (int64_t)(blockIdx.x / PARTS) * TM;
+  const int e0 = (int)(blockIdx.x % PARTS) * NP;  // first expert of this workgroup
   const int nkf = d / 32;                        // full steps; a ragged tail follows the loop
   const bool many = (NI % WV == 0) || wave < (NI % WV);  // this wave issues CH loads per step, else CL
 
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
       if (t > T - 1) t = T - 1;
       src[j] = x + t * d + c * 8;
     } else {
-      int e = srow - TM;
+      int e = e0 + srow - TM;
       if (e > N - 1) e = N - 1;
       src[j] = w + (int64_t)e * d + c * 8;
     }
@@ -323,6 +332,19 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
     __syncthreads();
   }
 
+  if (PARTS > 1) {  // scores of this slice only, straight to logits (the choice is a second pass)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int col = e0 + es * 64 + cb * 32 + (lane & 31);
+      const float b = (bias && col < N) ? bias[col] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = t0 + tb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (col < N && row < T) logits_out[row * N + col] = acc[cb][r] + b;
+      }
+    }
+    return;
+  }
   // scores -> LDS tile [TM][NP + 1] (odd row stride); padded experts get -inf
   constexpr int LD = NP + 1;
   float* lt = reinterpret_cast<float*>(lds);
@@ -340,20 +362,20 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   tile_epilogue(lt, LD, TM, t0, T, N, n_groups, k, logits_out, idx, gate);
 }
 
-template <int TM, int NP, int S, int WV>
+template <int TM, int NP, int S, int WV, int PARTS = 1>
 static moge_status_t launch_route_dma(const moge_shape_t& s, int n_groups, int k, const void* x, const void* w,
                                       const float* bias, float* logits, int32_t* idx, float* gate,
                                       hipStream_t stream) {
   constexpr size_t ring = (size_t)S * (TM + NP) * 64;
   constexpr size_t tile = (size_t)TM * (NP + 1) * 4;
   constexpr size_t lds = ring > tile ? ring : tile;
-  const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV>);
+  const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV, PARTS>);
   moge_status_t st = raise_dynamic_lds(kern, lds, "route_dma_kernel");
   if (st != MOGE_OK) return st;
-  const int64_t grid = ((int64_t)s.T + TM - 1) / TM;
-  hipLaunchKernelGGL((route_dma_kernel<TM, NP, S, WV>), dim3((unsigned)grid), dim3(64 * WV), lds, stream, (int64_t)s.T, s.d,
-                     s.N, n_groups, k, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias,
-                     logits, idx, gate);
+  const int64_t grid = ((int64_t)s.T + TM - 1) / TM * PARTS;
+  hipLaunchKernelGGL((route_dma_kernel<TM, NP, S, WV, PARTS>), dim3((unsigned)grid), dim3(64 * WV), lds, stream,
+                     (int64_t)s.T, s.d, s.N, n_groups, k, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(w), bias, logits, idx, gate);
   return check_launch("route_dma_kernel");
 }
 
@@ -507,7 +529,8 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
   const int n_groups = mode == MOGE_ROUTE_GROUPED ? s.M : 1;
   const int k = mode == MOGE_ROUTE_GROUPED ? s.k_per_group : s.M * s.k_per_group;
 
-  if (!x) {
+  // the choice from stored scores (caller scores, or the split scores pass below)
+  auto select = [&]() -> moge_status_t {
     if (lane_parallel_choice(s.N, n_groups, k)) {
       const int64_t grid = ((int64_t)s.T + kSelTokens - 1) / kSelTokens;
       const size_t lds = sizeof(float) * kSelTokens * (size_t)(s.N + 1);
@@ -523,7 +546,11 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
                          sizeof(float) * kSelTokensWide * (size_t)s.N, stream, (int64_t)s.T, s.N, n_groups, k, logits,
                          idx, gate);
     }
-    st = check_launch("route_select_kernel");
+    return check_launch("route_select_kernel");
+  };
+
+  if (!x) {
+    st = select();
   } else if (s.dtype == MOGE_F32) {
     const int64_t grid = ((int64_t)s.T + kF32Tokens - 1) / kF32Tokens;
     hipLaunchKernelGGL(route_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (int64_t)s.T, s.d, s.N,
@@ -547,6 +574,9 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
       st = launch_route_dma<128, 64, 6, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
     } else if (s.N <= 128) {
       st = launch_route_dma<64, 128, 6, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+    } else if (logits) {  // N > 128 with the scores stored: the sliced scores pass, then the choice
+      st = launch_route_dma<64, 128, 8, 4, 2>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+      if (st == MOGE_OK) st = select();
     } else {
       st = launch_route_dma<32, 256, 7, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
     }
