@@ -2,22 +2,23 @@
 // the gather of token rows into expert order (dropless: every (token, slot) pair
 // gets a row; Pangu Ultra MoE digests on reportify.cn, dropless training).
 //
-// Four launches, no atomics on anything that decides an order:
+// Up to four launches; the only atomics are a count and a bitwise OR, whose results
+// do not depend on their order, so every output is deterministic:
 //   1. dispatch_hist_kernel   one workgroup per block of 64 tokens counts its
 //                             assignments per expert (LDS integer histogram).
 //   2. dispatch_scan_kernel   one workgroup per expert scans that expert's block
 //                             counts -> per-block starting rows and counts[e].
-//   3. dispatch_permute_kernel one workgroup per token block (one token per lane):
-//                             offsets from counts, then wave w takes the experts
-//                             e = w (mod 4): a ballot loop over its distinct experts
-//                             gives every (token, slot) its row = block base + number
-//                             of lower lanes that chose the same expert, so rows of
-//                             an expert stay in ascending token order -> inv, perm.
-//                             The four waves work on disjoint experts at once.
+//   3. dispatch_permute_kernel one workgroup per token block: offsets from counts;
+//                             each expert's 64-bit mask of the block's tokens that
+//                             chose it (LDS OR); then every (token, slot) gets its
+//                             row = segment start + rows of the expert in earlier
+//                             blocks + popcount of the mask below the token, so rows
+//                             of an expert stay in ascending token order -> inv, perm.
 //   4. dispatch_copy_kernel   one wave per token reads its row from HBM once and
 //                             writes it to all of its slots' rows (16-byte stores)
 //                             in the tiled layout the expert GEMMs read, plus the
-//                             token-order tiled copy the shared expert reads.
+//                             token-order tiled copy the shared expert reads (only
+//                             when the expert GEMMs cannot read the rows from x).
 // Every expert's rows start on a 16-row boundary (P(e) in moge.h), so a 16-row
 // tile of the GEMM operands never mixes experts.
 #include "moge_internal.hpp"
@@ -69,9 +70,10 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ bprefix, int32_t* __restrict__ offsets_out,
     int32_t* __restrict__ inv, int32_t* __restrict__ perm) {
   // inv == nullptr: offsets only (launched with one workgroup)
-  extern __shared__ int lds[];
+  extern __shared__ __attribute__((aligned(16))) int lds[];
   const int KS = K + 1;  // odd row stride: lanes of a wave hit distinct banks
-  int* keys = lds;
+  uint64_t* emask = reinterpret_cast<uint64_t*>(lds);  // per expert: the block's tokens that chose it
+  int* keys = reinterpret_cast<int*>(emask + N);
   int* offs = keys + kTB * KS;
   int* base = offs + (N + 1);
   int* pbase = base + N;  // P(e): first local row of expert e (16-row aligned segments)
@@ -111,7 +113,10 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
         if ((int64_t)r < rows_cap) perm[r] = -1;
     }
   }
-  // stage this block's expert ids (token tl = lane); slots of other experts get inv = -1
+  for (int e = threadIdx.x; e < N; e += 256) emask[e] = 0;
+  __syncthreads();
+  // stage this block's expert ids (token tl = i / K); slots of other experts get inv = -1;
+  // every in-range choice sets its token's bit in the expert's mask (OR: order-independent)
   for (int i = threadIdx.x; i < kTB * K; i += 256) {
     const int tl = i / K, s = i - tl * K;
     const int64_t t = t0 + tl;
@@ -120,39 +125,23 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
       e = idx[t * K + s];
       if ((unsigned)e >= (unsigned)N) e = -1;
       if (e < e_lo || e >= e_hi) inv[t * K + s] = -1;
+      else atomicOr(reinterpret_cast<unsigned long long*>(&emask[e]), 1ull << tl);
     }
     keys[tl * KS + s] = e;
   }
   __syncthreads();
 
-  // wave w: experts e in [e_lo, e_hi) with e % 4 == w, one distinct expert per iteration
-  {
-    const int64_t t = t0 + lane;
-    const int* my = keys + lane * KS;
-    uint64_t pending = 0;
-    for (int s = 0; s < K; ++s) {
-      const int e = my[s];
-      if (e >= e_lo && e < e_hi && (e & 3) == wave) pending |= (1ull << s);
-    }
-    while (true) {
-      const uint64_t pm = __ballot(pending != 0);
-      if (pm == 0) break;
-      const int leader = __builtin_ctzll(pm);
-      const int first = pending ? my[__builtin_ctzll(pending)] : 0;
-      const int e = __builtin_amdgcn_readlane(first, leader);
-      int slot = -1;
-      for (int s = 0; s < K; ++s)
-        if (((pending >> s) & 1ull) && my[s] == e) slot = s;
-      const uint64_t m = __ballot(slot >= 0);
-      if (slot >= 0) {
-        int r = pbase[e] + base[e] + lanes_below(m);  // local row in the padded numbering
-        if ((int64_t)r >= rows_cap || r < 0) r = -1;
-        inv[t * K + slot] = r;
-        if (r >= 0) perm[r] = (int32_t)t;
-        pending &= ~(1ull << slot);
-      }
-      // (a token holds an expert at most once, so expert e is done in this one pass)
-    }
+  // row of (token, slot) = P(e) + rows of e in earlier blocks + tokens of this block
+  // before it that chose e (a token holds an expert at most once): stable token order
+  for (int i = threadIdx.x; i < kTB * K; i += 256) {
+    const int tl = i / K, s = i - tl * K;
+    const int e = keys[tl * KS + s];
+    if (e < e_lo || e >= e_hi) continue;  // (also e = -1: token past T or invalid id)
+    const int64_t t = t0 + tl;
+    int r = pbase[e] + base[e] + __popcll(emask[e] & ((1ull << tl) - 1ull));  // local row, padded numbering
+    if ((int64_t)r >= rows_cap || r < 0) r = -1;
+    inv[t * K + s] = r;
+    if (r >= 0) perm[r] = (int32_t)t;
   }
 }
 
@@ -235,7 +224,8 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3((unsigned)s.N), dim3(256), 0, stream, nb, bcount, bprefix, counts);
   if ((st = check_launch("dispatch_scan_kernel")) != MOGE_OK) return st;
 
-  const size_t lds = sizeof(int) * ((size_t)kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + (size_t)(s.N + 1));
+  const size_t lds = sizeof(uint64_t) * (size_t)s.N +
+                     sizeof(int) * ((size_t)kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + (size_t)(s.N + 1));
   if (lds > 64 * 1024) {
     st = raise_dynamic_lds(reinterpret_cast<const void*>(dispatch_permute_kernel), lds, "dispatch_permute_kernel");
     if (st != MOGE_OK) return st;
