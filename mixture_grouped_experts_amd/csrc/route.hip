@@ -511,6 +511,93 @@ __global__ __launch_bounds__(256) void route_select_kernel(int64_t T, int N, int
   }
 }
 
+// ----------------------------------------------------------------------------
+// Caller-supplied scores, global top-K (one group) with K <= 32: one lane per token,
+// 64 tokens per single-wave workgroup.  The 64 score rows are staged in LDS with an
+// odd row stride (conflict-free row reads); each lane then walks its own row: the
+// maximum, the softmax denominator, and a sorted register list of the KMAX best
+// (score desc, expert asc: a later equal score never displaces an earlier one),
+// kept by a branch-free insertion network.  No cross-lane reduction at all, so a
+// wave chooses for 64 tokens at once.
+constexpr int kLaneTokens = 64;
+template <int KMAX>
+__global__ __launch_bounds__(64) void route_select_lane_kernel(int64_t T, int N, int k,
+                                                               const float* __restrict__ logits,
+                                                               int32_t* __restrict__ idx, float* __restrict__ gate) {
+  extern __shared__ float lt[];  // [kLaneTokens][N + 1]
+  const int lane = threadIdx.x;
+  const int ld = N + 1;
+  const int64_t t0 = (int64_t)blockIdx.x * kLaneTokens;
+  const int64_t nrows = (T - t0) < kLaneTokens ? (T - t0) : kLaneTokens;
+  const float* src = logits + t0 * N;  // the tile's rows are contiguous
+  const int total = (int)nrows * N;
+  int i = lane;
+#pragma unroll 4
+  for (; i < total; i += 64) {
+    const int r = i / N;
+    lt[r * ld + (i - r * N)] = src[i];
+  }
+  __syncthreads();
+  const int64_t t = t0 + lane;
+  if (t >= T) return;
+  const float* row = lt + lane * ld;
+  // pass 1: the maximum; pass 2: the denominator (8 interleaved partial sums, then a tree)
+  float mp[8] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY, -INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  int e8 = 0;
+  for (; e8 + 8 <= N; e8 += 8)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mp[j] = fmaxf(mp[j], row[e8 + j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (e8 + j < N) mp[j] = fmaxf(mp[j], row[e8 + j]);
+  const float m = fmaxf(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])), fmaxf(fmaxf(mp[4], mp[5]), fmaxf(mp[6], mp[7])));
+  float zp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (e8 = 0; e8 + 8 <= N; e8 += 8)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zp[j] += expf(row[e8 + j] - m);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (e8 + j < N) zp[j] += expf(row[e8 + j] - m);
+  const float z = ((zp[0] + zp[1]) + (zp[2] + zp[3])) + ((zp[4] + zp[5]) + (zp[6] + zp[7]));
+  // pass 3: the KMAX best, in expert order (8 scores read ahead at a time)
+  float bv[KMAX];
+  int bi[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    bv[j] = -INFINITY;
+    bi[j] = -1;
+  }
+  auto insert = [&](float v, int e) {
+    // position of v: below every entry >= v; entries below it move down one place
+#pragma unroll
+    for (int j = KMAX - 1; j > 0; --j) {
+      const bool up = v > bv[j - 1];  // v lands above j - 1: entry j - 1 moves to j
+      const bool here = v > bv[j];
+      bv[j] = up ? bv[j - 1] : (here ? v : bv[j]);
+      bi[j] = up ? bi[j - 1] : (here ? e : bi[j]);
+    }
+    if (v > bv[0]) {
+      bv[0] = v;
+      bi[0] = e;
+    }
+  };
+  for (e8 = 0; e8 + 8 <= N; e8 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = row[e8 + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) insert(v[j], e8 + j);
+  }
+  for (; e8 < N; ++e8) insert(row[e8], e8);
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    if (r < k) {
+      idx[t * k + r] = bi[r];
+      gate[t * k + r] = expf(bv[r] - m) / z;
+    }
+  }
+}
+
 }  // namespace moge
 
 using namespace moge;
@@ -531,6 +618,27 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
 
   // the choice from stored scores (caller scores, or the split scores pass below)
   auto select = [&]() -> moge_status_t {
+    if (n_groups == 1 && k <= 32 && !lane_parallel_choice(s.N, n_groups, k)) {
+      const int64_t grid = ((int64_t)s.T + kLaneTokens - 1) / kLaneTokens;
+      const size_t lds = sizeof(float) * kLaneTokens * (size_t)(s.N + 1);
+      const void* kern = k <= 8    ? reinterpret_cast<const void*>(route_select_lane_kernel<8>)
+                         : k <= 16 ? reinterpret_cast<const void*>(route_select_lane_kernel<16>)
+                                   : reinterpret_cast<const void*>(route_select_lane_kernel<32>);
+      if (lds > 64 * 1024) {
+        st = raise_dynamic_lds(kern, lds, "route_select_lane_kernel");
+        if (st != MOGE_OK) return st;
+      }
+      if (k <= 8)
+        hipLaunchKernelGGL(route_select_lane_kernel<8>, dim3((unsigned)grid), dim3(64), lds, stream, (int64_t)s.T,
+                           s.N, k, logits, idx, gate);
+      else if (k <= 16)
+        hipLaunchKernelGGL(route_select_lane_kernel<16>, dim3((unsigned)grid), dim3(64), lds, stream, (int64_t)s.T,
+                           s.N, k, logits, idx, gate);
+      else
+        hipLaunchKernelGGL(route_select_lane_kernel<32>, dim3((unsigned)grid), dim3(64), lds, stream, (int64_t)s.T,
+                           s.N, k, logits, idx, gate);
+      return check_launch("route_select_lane_kernel");
+    }
     if (lane_parallel_choice(s.N, n_groups, k)) {
       const int64_t grid = ((int64_t)s.T + kSelTokens - 1) / kSelTokens;
       const size_t lds = sizeof(float) * kSelTokens * (size_t)(s.N + 1);
