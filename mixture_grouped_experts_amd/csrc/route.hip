@@ -512,16 +512,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(int64_t T, int N, int
 }
 
 // ----------------------------------------------------------------------------
-// Caller-supplied scores, global top-K (one group) with K <= 32: one lane per token,
-// 64 tokens per single-wave workgroup.  The 64 score rows are staged in LDS with an
-// odd row stride (conflict-free row reads); each lane then walks its own row: the
-// maximum, the softmax denominator, and a sorted register list of the KMAX best
-// (score desc, expert asc: a later equal score never displaces an earlier one),
-// kept by a branch-free insertion network.  No cross-lane reduction at all, so a
-// wave chooses for 64 tokens at once.
+// Caller-supplied scores, k <= 32 per group: one lane per token, 64 tokens per
+// single-wave workgroup.  The 64 score rows are staged in LDS with an odd row stride
+// (conflict-free row reads); each lane then walks its own row: the maximum, the
+// softmax denominator, and for every group a sorted register list of the KMAX best
+// of that group (score desc, expert asc: a later equal score never displaces an
+// earlier one), kept by a branch-free insertion network.  No cross-lane reduction
+// at all, so a wave chooses for 64 tokens at once.
 constexpr int kLaneTokens = 64;
 template <int KMAX>
-__global__ __launch_bounds__(64) void route_select_lane_kernel(int64_t T, int N, int k,
+__global__ __launch_bounds__(64) void route_select_lane_kernel(int64_t T, int N, int n_groups, int k,
                                                                const float* __restrict__ logits,
                                                                int32_t* __restrict__ idx, float* __restrict__ gate) {
   extern __shared__ float lt[];  // [kLaneTokens][N + 1]
@@ -559,14 +559,10 @@ __global__ __launch_bounds__(64) void route_select_lane_kernel(int64_t T, int N,
   for (int j = 0; j < 8; ++j)
     if (e8 + j < N) zp[j] += expf(row[e8 + j] - m);
   const float z = ((zp[0] + zp[1]) + (zp[2] + zp[3])) + ((zp[4] + zp[5]) + (zp[6] + zp[7]));
-  // pass 3: the KMAX best, in expert order (8 scores read ahead at a time)
+  // pass 3, per group: its KMAX best, in expert order (8 scores read ahead at a time)
+  const int G = N / n_groups, K = n_groups * k;
   float bv[KMAX];
   int bi[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    bv[j] = -INFINITY;
-    bi[j] = -1;
-  }
   auto insert = [&](float v, int e) {
     // position of v: below every entry >= v; entries below it move down one place
 #pragma unroll
@@ -581,19 +577,27 @@ __global__ __launch_bounds__(64) void route_select_lane_kernel(int64_t T, int N,
       bi[0] = e;
     }
   };
-  for (e8 = 0; e8 + 8 <= N; e8 += 8) {
-    float v[8];
+  for (int g = 0; g < n_groups; ++g) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = row[e8 + j];
+    for (int j = 0; j < KMAX; ++j) {
+      bv[j] = -INFINITY;
+      bi[j] = -1;
+    }
+    const int ge = (g + 1) * G;
+    for (e8 = g * G; e8 + 8 <= ge; e8 += 8) {
+      float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) insert(v[j], e8 + j);
-  }
-  for (; e8 < N; ++e8) insert(row[e8], e8);
+      for (int j = 0; j < 8; ++j) v[j] = row[e8 + j];
 #pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    if (r < k) {
-      idx[t * k + r] = bi[r];
-      gate[t * k + r] = expf(bv[r] - m) / z;
+      for (int j = 0; j < 8; ++j) insert(v[j], e8 + j);
+    }
+    for (; e8 < ge; ++e8) insert(row[e8], e8);
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      if (r < k) {
+        idx[t * K + g * k + r] = bi[r];
+        gate[t * K + g * k + r] = expf(bv[r] - m) / z;
+      }
     }
   }
 }
@@ -618,25 +622,26 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
 
   // the choice from stored scores (caller scores, or the split scores pass below)
   auto select = [&]() -> moge_status_t {
-    if (n_groups == 1 && k <= 32 && !lane_parallel_choice(s.N, n_groups, k)) {
+    if (k <= 32) {  // one lane per token
       const int64_t grid = ((int64_t)s.T + kLaneTokens - 1) / kLaneTokens;
       const size_t lds = sizeof(float) * kLaneTokens * (size_t)(s.N + 1);
-      const void* kern = k <= 8    ? reinterpret_cast<const void*>(route_select_lane_kernel<8>)
-                         : k <= 16 ? reinterpret_cast<const void*>(route_select_lane_kernel<16>)
-                                   : reinterpret_cast<const void*>(route_select_lane_kernel<32>);
-      if (lds > 64 * 1024) {
-        st = raise_dynamic_lds(kern, lds, "route_select_lane_kernel");
-        if (st != MOGE_OK) return st;
-      }
-      if (k <= 8)
-        hipLaunchKernelGGL(route_select_lane_kernel<8>, dim3((unsigned)grid), dim3(64), lds, stream, (int64_t)s.T,
-                           s.N, k, logits, idx, gate);
-      else if (k <= 16)
-        hipLaunchKernelGGL(route_select_lane_kernel<16>, dim3((unsigned)grid), dim3(64), lds, stream, (int64_t)s.T,
-                           s.N, k, logits, idx, gate);
-      else
-        hipLaunchKernelGGL(route_select_lane_kernel<32>, dim3((unsigned)grid), dim3(64), lds, stream, (int64_t)s.T,
-                           s.N, k, logits, idx, gate);
+#define MOGE_SEL(KM)                                                                                              \
+  do {                                                                                                            \
+    if (lds > 64 * 1024) {                                                                                        \
+      st = raise_dynamic_lds(reinterpret_cast<const void*>(route_select_lane_kernel<KM>), lds,                     \
+                             "route_select_lane_kernel");                                                         \
+      if (st != MOGE_OK) return st;                                                                               \
+    }                                                                                                             \
+    hipLaunchKernelGGL(route_select_lane_kernel<KM>, dim3((unsigned)grid), dim3(64), lds, stream, (int64_t)s.T,  \
+                       s.N, n_groups, k, logits, idx, gate);                                                      \
+  } while (0)
+      if (k <= 1) MOGE_SEL(1);
+      else if (k <= 2) MOGE_SEL(2);
+      else if (k <= 4) MOGE_SEL(4);
+      else if (k <= 8) MOGE_SEL(8);
+      else if (k <= 16) MOGE_SEL(16);
+      else MOGE_SEL(32);
+#undef MOGE_SEL
       return check_launch("route_select_lane_kernel");
     }
     if (lane_parallel_choice(s.N, n_groups, k)) {
