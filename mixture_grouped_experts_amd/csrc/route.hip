@@ -513,31 +513,42 @@ __global__ __launch_bounds__(256) void route_select_kernel(int64_t T, int N, int
 
 // ----------------------------------------------------------------------------
 // Caller-supplied scores, k <= 32 per group: one lane per token, 64 tokens per
-// single-wave workgroup.  The 64 score rows are staged in LDS with an odd row stride
-// (conflict-free row reads); each lane then walks its own row: the maximum, the
+// workgroup.  All four waves stage the 64 score rows in LDS (16-byte loads; odd row
+// stride, so the row reads are conflict-free); then wave 0 chooses, each lane
+// walking its own row: the maximum, the
 // softmax denominator, and for every group a sorted register list of the KMAX best
 // of that group (score desc, expert asc: a later equal score never displaces an
 // earlier one), kept by a branch-free insertion network.  No cross-lane reduction
 // at all, so a wave chooses for 64 tokens at once.
 constexpr int kLaneTokens = 64;
 template <int KMAX>
-__global__ __launch_bounds__(64) void route_select_lane_kernel(int64_t T, int N, int n_groups, int k,
+__global__ __launch_bounds__(256) void route_select_lane_kernel(int64_t T, int N, int n_groups, int k,
                                                                const float* __restrict__ logits,
                                                                int32_t* __restrict__ idx, float* __restrict__ gate) {
   extern __shared__ float lt[];  // [kLaneTokens][N + 1]
-  const int lane = threadIdx.x;
   const int ld = N + 1;
   const int64_t t0 = (int64_t)blockIdx.x * kLaneTokens;
   const int64_t nrows = (T - t0) < kLaneTokens ? (T - t0) : kLaneTokens;
   const float* src = logits + t0 * N;  // the tile's rows are contiguous
   const int total = (int)nrows * N;
-  int i = lane;
+  if ((N & 3) == 0) {  // 16-byte loads (rows start on 16-byte boundaries)
 #pragma unroll 4
-  for (; i < total; i += 64) {
-    const int r = i / N;
-    lt[r * ld + (i - r * N)] = src[i];
+    for (int i = threadIdx.x * 4; i < total; i += 1024) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + i);
+      const int r = i / N, c = i - r * N;  // c % 4 == 0 and c + 3 < N: the 4 values share a row
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lt[r * ld + c + j] = v[j];
+    }
+  } else {
+#pragma unroll 4
+    for (int i = threadIdx.x; i < total; i += 256) {
+      const int r = i / N;
+      lt[r * ld + (i - r * N)] = src[i];
+    }
   }
   __syncthreads();
+  if (threadIdx.x >= 64) return;  // wave 0 chooses
+  const int lane = threadIdx.x;
   const int64_t t = t0 + lane;
   if (t >= T) return;
   const float* row = lt + lane * ld;
@@ -632,7 +643,7 @@ extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, con
                              "route_select_lane_kernel");                                                         \
       if (st != MOGE_OK) return st;                                                                               \
     }                                                                                                             \
-    hipLaunchKernelGGL(route_select_lane_kernel<KM>, dim3((unsigned)grid), dim3(64), lds, stream, (int64_t)s.T,  \
+    hipLaunchKernelGGL(route_select_lane_kernel<KM>, dim3((unsigned)grid), dim3(256), lds, stream, (int64_t)s.T, \
                        s.N, n_groups, k, logits, idx, gate);                                                      \
   } while (0)
       if (k <= 1) MOGE_SEL(1);
