@@ -12,22 +12,23 @@
 //     workgroup (two waves per SIMD) owns a 320-row x 256-weight-row tile (GEMM 1:
 //     128 gate + 128 up rows of the same 128 h columns, so the SwiGLU is fused into
 //     the epilogue; GEMM 2: 256 output columns), each wave a 160 x 64 part of it;
-//   * both operands are in the tiled layout (16 x 32 tiles of 1 KiB, see moge.h):
-//     the token rows as written by dispatch and the weights as packed once at
-//     load time, so every load instruction moves one contiguous 1 KiB tile
-//     (one burst per 16 rows, one address-translation page per instruction)
-//     instead of 16 half cache lines of 16 long rows; this alone took about a
-//     third off the load time.  K is padded with zeros to a multiple of 32, so
-//     there is no ragged reduction step;
+//     when the experts average at most 64 rows (decode) a 96 x 512 tile instead,
+//     which streams twice the weight bytes per step -- SwiftGMM's switch of mode by
+//     workload;
+//   * the weights are packed once at load time into the tiled layout (16 x 32
+//     tiles of 1 KiB, see moge.h), so every weight load instruction moves one
+//     contiguous 1 KiB tile (one burst per 16 rows, one address-translation page
+//     per instruction) instead of 16 half cache lines of 16 long rows; K is padded
+//     with zeros to a multiple of 32, so there is no ragged reduction step;
+//   * GEMM 1 takes its token rows straight from the row-major x, each lane's
+//     address from perm (moge_expert_gate_up_gather), so dispatch never writes an
+//     x_perm (R x d, 1 GB for 8192 tokens x 8 slots x 7680); or from a tiled x_perm
+//     where that cannot apply (float32, d % 32 != 0).  GEMM 2 reads the tiled h;
 //   * both panels go straight from global memory to a 4-stage LDS ring
 //     (global_load_lds_dwordx4, BK = 32), so every load has three steps of MFMA
-//     work to arrive and no registers stage it;
-//   * GEMM 1 can also take its token rows straight from the row-major x, each
-//     lane's address from perm (moge_expert_gate_up_gather): dispatch then never
-//     writes x_perm (R x d, 1 GB for 8192 tokens x 8 slots x 7680), and the rows
-//     come in at 64 B per row per step instead of as whole tiles; 64-byte LDS rows with an
-//     XOR swizzle keep the 16-byte fragment reads bank-conflict free at the
-//     LDS's full rate, which takes at least two waves per SIMD to reach;
+//     work to arrive and no registers stage it; 64-byte LDS rows with an XOR
+//     swizzle keep the 16-byte fragment reads bank-conflict free at the LDS's full
+//     rate, which takes at least two waves per SIMD to reach;
 //   * a tile with few live rows (the last tile of an expert) skips the MFMAs of
 //     its empty 32-row blocks; the row blocks are interleaved over the waves;
 //   * a persistent grid walks a device-built tile list (no host sync on the
@@ -38,8 +39,8 @@
 //     XCD b % 8), so that sharing happens in that XCD's L2;
 //   * the weight fragment is the MFMA's first operand, so each lane ends with 4
 //     consecutive output columns of one token row: the epilogue (SwiGLU for
-//     GEMM 1, into the tiled h; GEMM 2 into the row-major expert output) packs
-//     them into 8-byte stores straight to HBM.
+//     GEMM 1, into the tiled h; GEMM 2 into the row-major expert output, or
+//     straight into y for one-group shares) packs them into 8- or 16-byte stores.
 // float32 shapes use a plain vector-ALU kernel pair on the same layouts (small
 // shapes only).
 #include <math.h>

@@ -7,20 +7,25 @@
 // group are kept, which puts exactly K' of the token's assignments on each device.
 //
 // gfx950 design
-//   * bf16 scores: x [T][d] is streamed from HBM exactly once.  A workgroup of 4
-//     waves owns TM tokens x NP (N rounded up to 64, 128 or 256) experts, TM*NP =
-//     8192; each wave owns a 32-token x 64-expert block and accumulates it with
+//   * bf16 scores: x [T][d] is streamed from HBM once.  A workgroup of 4 waves owns
+//     TM tokens x NP experts (128 x 64, 64 x 128 or 32 x 256 by N), TM*NP = 8192;
+//     each wave owns a 32-token x 64-expert block and accumulates it with
 //     v_mfma_f32_32x32x16_bf16 (float32 accumulate).  Token rows and router rows go
-//     from global memory straight into a 6- or 7-stage LDS ring with direct-to-LDS
+//     from global memory straight into a 6- to 8-stage LDS ring with direct-to-LDS
 //     loads, several 32-element steps ahead, so each workgroup keeps tens of KiB of
-//     x in flight (what HBM needs to stream at full rate) without staging
-//     registers; the router slab of a step is shared by the workgroup's waves.
-//     Few tokens (fewer 128-token tiles than CUs): a split-K kernel whose operands
-//     go straight from global memory into MFMA registers.
+//     x in flight without staging registers; the router slab of a step is shared by
+//     the workgroup's waves.  Few tokens (fewer 128-token tiles than CUs, N <= 128):
+//     a split-K kernel whose operands go straight from global memory into MFMA
+//     registers.
 //   * Epilogue in the same kernel: the TM x N score tile goes to LDS, the optional
-//     score store is coalesced, and one wave per token does the softmax (wave-wide
-//     max and sum) and the per-group rank count that picks the top-K'.
-//   * float32 shapes and caller-supplied scores use the same epilogue.
+//     score store is coalesced, and the choice runs lane-parallel (one lane per
+//     token and group) or, for wide groups, one wave per token.
+//   * N > 128 with the scores stored: the experts are split in two halves over the
+//     XCDs (each XCD's L2 keeps its half of the router matrix), the kernel only
+//     writes scores, and the choice is a second pass.
+//   * The choice from stored scores (that pass, the global comparator, caller
+//     scores) runs one lane per token with a sorted register list per group.
+//   * float32 shapes use a vector-ALU scores kernel with the same epilogue.
 #include <math.h>
 
 #include "moge_internal.hpp"
