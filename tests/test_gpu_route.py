@@ -94,7 +94,7 @@ def test_route_from_x(gpu, w):
 def test_route_ties_and_edge_shapes(gpu):
     rng = np.random.default_rng(0)
     cases = [(1, 8, 4, 1), (33, 64, 8, 2), (100, 16, 1, 5), (70, 12, 3, 4), (129, 256, 8, 1), (64, 256, 4, 8),
-             (65, 128, 2, 3)]
+             (65, 128, 2, 3), (77, 15, 5, 2), (40, 6, 3, 1), (200, 250, 5, 7)]    # (N not a multiple of 4)
     for T, N, M, Kp in cases:
         w = W.variant(W.routing(), T=T, N=N, M=M, Kp=Kp)
         lg = rng.integers(-2, 3, size=(T, N)).astype(np.float32)        # heavy ties
