@@ -14,6 +14,7 @@ on, between consecutive library calls inside the timed steps.  The dominant kern
 its algorithmic bytes (weights + activations it must move) and FLOPs per launch.
 
     python bench.py [--steps K] [--warmup W] [--workload ultra|group0|decode|routing|tiny|pro]
+                    [--tokens T] [--rows auto|gather|copy] [--tiles auto|tall|wide]
                     [--no-cpu-baseline] [--cpu-seconds S]
 """
 from __future__ import annotations
@@ -44,6 +45,8 @@ def parse():
                    help="gate/up token rows: read from x through perm, or copied by dispatch (auto: the layer's choice)")
     p.add_argument("--tiles", default="auto", choices=["auto", "tall", "wide"],
                    help="expert-GEMM tile shape: 320x256 (tall), 96x512 (wide), or the library's choice")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="run the workload's shape with this many tokens instead (its name records the count)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -202,6 +205,11 @@ def main():
     w = {"ultra": W.ultra, "group0": W.group0, "decode": W.decode, "routing": W.routing, "tiny": W.tiny,
          "pro": W.pro}[
         args.workload]()
+    if args.tokens:
+        import re
+
+        w = W.variant(w, T=args.tokens, e_lo=w.e_lo, e_hi=w.e_hi,
+                      name=re.sub(r"_T\d+_", f"_T{args.tokens}_", w.name))
     torch.cuda.set_device(0)
     dv = H.device_inputs(w)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi,

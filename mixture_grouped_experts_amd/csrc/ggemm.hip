@@ -523,14 +523,17 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(const float* __restri
   }
 }
 
+// CUs of the current device, queried once per process (thread-safe static init);
+// the persistent grids are sized to it (any size is correct, this one fills the chip).
+static int query_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
 static int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
+  static const int cus = query_cus();
   return cus;
 }
 
