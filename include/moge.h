@@ -19,7 +19,8 @@
  *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     never allocates or frees device memory and keeps no per-call state.
+ *     never allocates or frees device memory and keeps no per-call state (its
+ *     one process-wide setting is the tile-shape knob, moge_set_gemm_tiles).
  *   - Tensors are contiguous.  x, logits, idx, gate, inv, the expert outputs
  *     and y are row-major; the operands of the expert GEMMs use the tiled
  *     layout described at moge_tiled_elems.  Weights come in the
