@@ -2,8 +2,9 @@
 // the gather of token rows into expert order (dropless: every (token, slot) pair
 // gets a row; Pangu Ultra MoE digests on reportify.cn, dropless training).
 //
-// Up to four launches; the only atomics are a count and a bitwise OR, whose results
-// do not depend on their order, so every output is deterministic:
+// Up to four launches (two for T * K <= 8192: dispatch_small_kernel does 1-3 in
+// one workgroup); the only atomics are a count and a bitwise OR, whose results do not
+// depend on their order, so every output is deterministic:
 //   1. dispatch_hist_kernel   one workgroup per block of 64 tokens counts its
 //                             assignments per expert (LDS integer histogram).
 //   2. dispatch_scan_kernel   one workgroup per expert scans that expert's block
@@ -145,6 +146,103 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
   }
 }
 
+// Small batches (T * K <= kSmallSlots): counts, offsets, inv and perm in one launch
+// of one 1024-thread workgroup.  Every expert id is read once into LDS (with the
+// counts, an LDS histogram); the permutation then takes the tokens in chunks of 64
+// in order, each chunk ranking its tokens by the same per-expert masks and popcounts
+// as dispatch_permute_kernel and then advancing each expert's running row count, so
+// the rows are those of the multi-block path.
+constexpr int kSmallSlots = 8192;
+constexpr int kSmallThreads = 1024;
+__global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(int64_t T, int K, int N,
+                                                                       const int32_t* __restrict__ idx, int e_lo,
+                                                                       int e_hi, int64_t rows_cap,
+                                                                       int32_t* __restrict__ counts_out,
+                                                                       int32_t* __restrict__ offsets_out,
+                                                                       int32_t* __restrict__ inv,
+                                                                       int32_t* __restrict__ perm) {
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  const int KS = K + 1;                                 // odd row stride
+  uint64_t* emask = reinterpret_cast<uint64_t*>(lds);  // per expert: the chunk's tokens that chose it
+  int* keys = reinterpret_cast<int*>(emask + N);      // [T][K + 1]
+  int* cnt = keys + T * KS;                            // [N]
+  int* base = cnt + N;                                 // [N]: rows of e in earlier chunks
+  int* pbase = base + N;                               // [N + 1]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < N; e += kSmallThreads) {
+    cnt[e] = 0;
+    base[e] = 0;
+  }
+  __syncthreads();
+  for (int j = tid; j < (int)T * K; j += kSmallThreads) {
+    int e = idx[j];
+    if ((unsigned)e >= (unsigned)N) e = -1;
+    else atomicAdd(&cnt[e], 1);
+    keys[(j / K) * KS + j % K] = e;
+  }
+  __syncthreads();
+  if (tid < 64) {  // wave 0: offsets (all experts) and P(e) (16-row aligned segments of [e_lo, e_hi))
+    const int lane = tid;
+    int run = 0, prun = 0;
+    for (int c = 0; c < N; c += 64) {
+      const int e = c + lane;
+      const int v = e < N ? cnt[e] : 0;
+      const int vp = (e >= e_lo && e < e_hi) ? (v + kSegAlign - 1) / kSegAlign * kSegAlign : 0;
+      int incl = v, pincl = vp;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(incl, off, 64), pu = __shfl_up(pincl, off, 64);
+        if (lane >= off) {
+          incl += u;
+          pincl += pu;
+        }
+      }
+      const int ex = run + incl - v, pex = prun + pincl - vp;
+      if (e < N) {
+        counts_out[e] = v;
+        offsets_out[e] = ex;
+        pbase[e] = pex;
+      }
+      if (inv && e >= e_lo && e < e_hi)  // padding rows of the segment
+        for (int r = pex + v; r < pex + vp; ++r)
+          if ((int64_t)r < rows_cap) perm[r] = -1;
+      run += __shfl(incl, 63, 64);
+      prun += __shfl(pincl, 63, 64);
+    }
+    if (lane == 0) {
+      offsets_out[N] = run;
+      pbase[N] = prun;
+    }
+  }
+  if (!inv) return;
+  __syncthreads();
+  for (int t0 = 0; t0 < (int)T; t0 += kTB) {
+    for (int e = tid; e < N; e += kSmallThreads) emask[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < kTB * K; i += kSmallThreads) {
+      const int tl = i / K, s = i - tl * K, t = t0 + tl;
+      if (t >= (int)T) continue;
+      const int e = keys[t * KS + s];
+      if (e < e_lo || e >= e_hi) inv[(int64_t)t * K + s] = -1;
+      else atomicOr(reinterpret_cast<unsigned long long*>(&emask[e]), 1ull << tl);
+    }
+    __syncthreads();
+    for (int i = tid; i < kTB * K; i += kSmallThreads) {
+      const int tl = i / K, s = i - tl * K, t = t0 + tl;
+      if (t >= (int)T) continue;
+      const int e = keys[t * KS + s];
+      if (e < e_lo || e >= e_hi) continue;
+      int r = pbase[e] + base[e] + __popcll(emask[e] & ((1ull << tl) - 1ull));  // local row, padded numbering
+      if ((int64_t)r >= rows_cap || r < 0) r = -1;
+      inv[(int64_t)t * K + s] = r;
+      if (r >= 0) perm[r] = t;
+    }
+    __syncthreads();
+    for (int e = tid; e < N; e += kSmallThreads) base[e] += __popcll(emask[e]);
+    __syncthreads();
+  }
+}
+
 // Row gather: one wave per token reads x[t] once (16-byte chunks, 8 in flight per
 // lane) and writes it to every row that inv gives the token, in the tiled layout
 // (a 16-byte chunk never straddles a tile; padding columns are written as zeros),
@@ -191,6 +289,33 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(int64_t T, int K, co
 
 using namespace moge;
 
+// Multi-block path: histogram per 64-token block, scan per expert over blocks, permutation.
+static moge_status_t dispatch_blocks_path(const moge_shape_t& s, int K, const int32_t* idx, int32_t e_lo,
+                                          int32_t e_hi, int64_t rows_cap, int32_t* counts, int32_t* offsets,
+                                          int32_t* inv, int32_t* perm, void* ws, hipStream_t stream) {
+  moge_status_t st;
+  const int64_t nb = dispatch_blocks(s.T);
+  int32_t* bcount = static_cast<int32_t*>(ws);
+  int32_t* bprefix = bcount + (int64_t)s.N * nb;
+
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nb), dim3(256), 0, stream, (int64_t)s.T, K, s.N, nb, idx,
+                     bcount);
+  if ((st = check_launch("dispatch_hist_kernel")) != MOGE_OK) return st;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3((unsigned)s.N), dim3(256), 0, stream, nb, bcount, bprefix, counts);
+  if ((st = check_launch("dispatch_scan_kernel")) != MOGE_OK) return st;
+
+  const size_t lds = sizeof(uint64_t) * (size_t)s.N +
+                     sizeof(int) * ((size_t)kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + (size_t)(s.N + 1));
+  if (lds > 64 * 1024) {
+    st = raise_dynamic_lds(reinterpret_cast<const void*>(dispatch_permute_kernel), lds, "dispatch_permute_kernel");
+    if (st != MOGE_OK) return st;
+  }
+  hipLaunchKernelGGL(dispatch_permute_kernel, dim3(inv ? (unsigned)nb : 1u), dim3(256), lds, stream, (int64_t)s.T, K, s.N, nb,
+                     idx, e_lo, e_hi, rows_cap, counts, bprefix, offsets, inv, perm);
+  st = check_launch("dispatch_permute_kernel");
+  return st;
+}
+
 extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
                                        int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts,
                                        int32_t* offsets, int32_t* inv, int32_t* perm, void* x_perm, void* x_tiled,
@@ -213,26 +338,16 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   const size_t need = moge_workspace_size(shape, MOGE_STAGE_DISPATCH);
   if (!ws || ws_bytes < need) return fail(MOGE_ERR_WORKSPACE, "dispatch workspace missing or too small");
 
-  const int64_t nb = dispatch_blocks(s.T);
-  int32_t* bcount = static_cast<int32_t*>(ws);
-  int32_t* bprefix = bcount + (int64_t)s.N * nb;
-  const int esz = s.dtype == MOGE_BF16 ? 2 : 4;
-
-  hipLaunchKernelGGL(dispatch_hist_kernel, dim3((unsigned)nb), dim3(256), 0, stream, (int64_t)s.T, K, s.N, nb, idx,
-                     bcount);
-  if ((st = check_launch("dispatch_hist_kernel")) != MOGE_OK) return st;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3((unsigned)s.N), dim3(256), 0, stream, nb, bcount, bprefix, counts);
-  if ((st = check_launch("dispatch_scan_kernel")) != MOGE_OK) return st;
-
-  const size_t lds = sizeof(uint64_t) * (size_t)s.N +
-                     sizeof(int) * ((size_t)kTB * (K + 1) + (size_t)(s.N + 1) + (size_t)s.N + (size_t)(s.N + 1));
-  if (lds > 64 * 1024) {
-    st = raise_dynamic_lds(reinterpret_cast<const void*>(dispatch_permute_kernel), lds, "dispatch_permute_kernel");
-    if (st != MOGE_OK) return st;
+  if ((int64_t)s.T * K <= kSmallSlots) {  // one workgroup does counts, offsets and the permutation
+    const size_t slds = sizeof(uint64_t) * (size_t)s.N +
+                        sizeof(int) * ((size_t)s.T * (K + 1) + (size_t)s.N * 3 + 1);  // <= 51 KiB
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallThreads), slds, stream, (int64_t)s.T, K, s.N, idx,
+                       e_lo, e_hi, rows_cap, counts, offsets, inv, perm);
+    st = check_launch("dispatch_small_kernel");
+  } else {
+    st = dispatch_blocks_path(s, K, idx, e_lo, e_hi, rows_cap, counts, offsets, inv, perm, ws, stream);
   }
-  hipLaunchKernelGGL(dispatch_permute_kernel, dim3(inv ? (unsigned)nb : 1u), dim3(256), lds, stream, (int64_t)s.T, K, s.N, nb,
-                     idx, e_lo, e_hi, rows_cap, counts, bprefix, offsets, inv, perm);
-  st = check_launch("dispatch_permute_kernel");
+  const int esz = s.dtype == MOGE_BF16 ? 2 : 4;
   if (st == MOGE_OK && x) {
     int64_t grid = ((int64_t)s.T + 3) / 4;
     if (grid > 16384) grid = 16384;

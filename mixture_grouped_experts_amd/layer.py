@@ -21,7 +21,9 @@ reportify.cn for the shared expert):
   5. moge_imbalance       per-group load and imbalance score (0 by construction)
   6. moge_route GLOBAL    the conventional top-K comparator from the stored scores,
      moge_dispatch        its counts only, and moge_imbalance of that load -- with expert
-                          FFNs, on a second stream right after step 1, overlapping steps 2-5.
+                          FFNs, on a second stream: it starts when step 1's scores exist and
+                          overlaps steps 2-5 (its calls are enqueued after step 2's, so the
+                          GPU never waits on them).
 
 Buffers are allocated once here (torch supplies device memory); ``forward`` only issues
 library calls, so it allocates nothing and does not synchronise.  Expert weights are
@@ -78,6 +80,7 @@ class MoGELayer:
             # the comparator only needs the stored scores: with expert FFNs to hide behind it
             # runs on a second stream (default priority), with a workspace of its own
             self.side = torch.cuda.Stream(device=dev) if F else None
+            self.route_done = torch.cuda.Event() if F else None
             self.gws = torch.empty(max(L.workspace_size(self.shape), 4), dtype=torch.uint8, device=dev)
             self.gidx = torch.empty(T, K, **i32)
             self.ggate = torch.empty(T, K, **f32)
@@ -131,9 +134,16 @@ class MoGELayer:
             L.dispatch(s, L.ROUTE_GLOBAL, self.gidx, None, 0, self.N, 0, self.gcounts, self.goffsets, None, None,
                        None, self.gws, stream=on)
             L.imbalance(s, self.gcounts, self.g_group_load, self.g_is_raw, self.g_is_norm, on)
-        if self.comparator and self.side is not None:
-            self.side.wait_stream(main)  # after the scores exist; joined back before the step ends
-            comparator(self.side)
+        side = self.side if self.comparator else None
+        if side is not None:
+            self.route_done.record(main)  # the comparator needs only the scores
+
+        def side_comparator():
+            # enqueued after the layer's own dispatch, so the GPU never waits on these host calls;
+            # it runs beside the layer from the moment the scores exist and is joined at the end
+            if side is not None:
+                side.wait_event(self.route_done)
+                comparator(side)
         stream = main
         if self.routing_only:
             L.dispatch(s, L.ROUTE_GROUPED, self.idx, None, 0, self.N, 0, self.counts, self.offsets, None, None, None,
@@ -144,6 +154,7 @@ class MoGELayer:
                 L.dispatch(s, L.ROUTE_GROUPED, self.idx, None, self.e_lo, self.e_hi, self.rows_cap, self.counts,
                            self.offsets, self.inv, self.perm, None, self.ws, None, stream)
                 mk("dispatch")
+                side_comparator()
                 Fs = self.F_shared
                 L.expert_gate_up_gather(s, x, self.perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate,
                                         w_up, self.h, Fs, shared[0] if Fs else None, shared[1] if Fs else None,
@@ -164,6 +175,7 @@ class MoGELayer:
                            self.offsets, self.inv, self.perm, self.x_perm, self.ws,
                            self.x_tiled if self.F_shared else None, stream)
                 mk("dispatch")
+                side_comparator()
                 if self.F_shared and self.fuse_shared:
                     # routed and shared experts in the same two launches
                     L.expert_gate_up_with_shared(s, self.F_shared, self.x_perm, self.offsets, self.e_lo,
