@@ -9,9 +9,12 @@ Default workload: the Pangu Ultra MoE shape (T=8192 tokens, hidden 7680, 256 rou
 groups, K'=1, expert width 2048, one shared expert of width 2048, bf16), the largest layer
 configuration that runs on one GPU.
 
-Prints ONE JSON line.  Per-call times come from HIP events recorded on the stream the kernels run
-on, between consecutive library calls inside the timed steps.  The dominant kernel's roofline uses
-its algorithmic bytes (weights + activations it must move) and FLOPs per launch.
+Prints ONE JSON line.  The last warm-up step is marked with a HIP event after every library call
+(on the stream the kernels run on) to find the dominant call; the K timed steps then carry events
+only around that call, so the timed region is the layer with next to no host work added, and its
+roofline uses the call's event-measured duration with its algorithmic bytes (weights +
+activations it must move) and FLOPs per launch.  The per-stage table comes from K more steps
+with every call marked, after the timed region.
 
     python bench.py [--steps K] [--warmup W] [--workload ultra|group0|decode|routing|tiny|pro]
                     [--tokens T] [--rows auto|gather|copy] [--tiles auto|tall|wide]
@@ -222,47 +225,72 @@ def main():
         torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step(marks=None):
+    def step(marks=None, only=None):
+        """One layer forward; with `marks`, a stream event after each library call (or only after
+        the calls named in `only`)."""
         rec = None
         if marks is not None:
             def rec(name):
-                ev = torch.cuda.Event(enable_timing=True)
-                ev.record(stream)
-                marks.append((name, ev))
+                if only is None or name in only:
+                    ev = torch.cuda.Event(enable_timing=True)
+                    ev.record(stream)
+                    marks.append((name, ev))
         layer.forward(dv.x, dv.w_router, dv.bias, dv.w_gate, dv.w_up, dv.w_down, dv.shared, mark=rec)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def run_marked(n, only=None):
+        """n steps, each with a begin event and the requested marks; returns their per-stage times (ms)."""
+        per = []
+        for _ in range(n):
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            marks = [("begin", ev0)]
+            step(marks, only)
+            per.append(marks)
+        torch.cuda.synchronize()
+        out = {}
+        for marks in per:
+            for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
+                out.setdefault(n1, []).append(e0.elapsed_time(e1))
+        return out
 
-    per_step = []
+    for _ in range(max(args.warmup - 1, 0)):
+        step()
+    # one marked warm-up step names the dominant stage and the call before it
+    probe = run_marked(1)
+    counts = layer.counts.cpu().numpy()
+    work = algorithmic_work(w, counts, fused_shared=bool(w.F_shared) and layer.fuse_shared, gather=layer.gather,
+                            fused_combine=layer.fuse_combine)
+    order = list(probe)
+    dom = max((k for k in work if k in probe), key=lambda k: probe[k][0])
+    prev = order[order.index(dom) - 1] if order.index(dom) > 0 else "begin"
+
+    # the timed region: exactly K steps with events only around the dominant stage's call
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
+    per_step = []
     for _ in range(args.steps):
-        marks = [("begin", None)]
         ev0 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        marks[0] = ("begin", ev0)
-        step(marks)
+        marks = [("begin", ev0)]
+        step(marks, only={prev, dom})
         per_step.append(marks)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-
-    stage_ms = {}
+    dom_ms = []
     for marks in per_step:
-        for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
-            stage_ms.setdefault(n1, []).append(e0.elapsed_time(e1))
-    stage_us = {k: 1000.0 * float(np.mean(v)) for k, v in stage_ms.items()}
+        names = [n for n, _ in marks]
+        e0 = marks[names.index(prev)][1]
+        e1 = marks[names.index(dom)][1]
+        dom_ms.append(e0.elapsed_time(e1))
     ms_per_step = total_ms / args.steps
     value = w.T * args.steps / (total_ms / 1000.0)
 
-    counts = layer.counts.cpu().numpy()
-    work = algorithmic_work(w, counts, fused_shared=bool(w.F_shared) and layer.fuse_shared, gather=layer.gather,
-                            fused_combine=layer.fuse_combine)
-    dom = max((k for k in work if k in stage_us), key=lambda k: stage_us[k])
+    # the per-stage table from K more steps with every call marked (outside the timed region)
+    stage_us = {k: 1000.0 * float(np.mean(v)) for k, v in run_marked(args.steps).items()}
+    stage_us[dom] = 1000.0 * float(np.mean(dom_ms))  # the dominant stage as timed inside the timed region
     t = stage_us[dom] * 1e-6
     wb, wf = work[dom]["bytes"], work[dom]["flops"]
     inten = wf / wb if wb else 0.0

@@ -213,3 +213,16 @@ class MoGELayer:
                 comparator(main)
             mk("global_comparator")
         return None if self.routing_only else self.y
+
+    def capture(self, x, w_router, bias, w_gate=None, w_up=None, w_down=None, shared=None, warmup: int = 1):
+        """Records one ``forward`` on these tensors into a HIP graph and returns it; ``g.replay()``
+        then enqueues the whole layer (both streams) with one host call.  The library calls
+        allocate nothing and set no memory, so the recorded work is exactly the forward's kernels.
+        The inputs are bound by address: refill the same tensors between replays."""
+        for _ in range(warmup):  # one-time setup (LDS limits, CU count) happens outside the capture
+            self.forward(x, w_router, bias, w_gate, w_up, w_down, shared)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.forward(x, w_router, bias, w_gate, w_up, w_down, shared)
+        return g
