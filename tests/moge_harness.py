@@ -26,6 +26,15 @@ def tol_ok(gpu: np.ndarray, ref: np.ndarray):
     return err <= bound, err, bound
 
 
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """Run-to-run equality of whole buffers, padding included: compared as raw bytes, since rows
+    that no kernel writes keep whatever the allocator handed out, NaN patterns among them, and
+    NaN never compares equal as a number."""
+    if a.shape != b.shape or a.dtype != b.dtype:
+        return False
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
 # ---- the tiled operand layout and padded row numbering of include/moge.h, restated here
 # from that header's definition (test side; the library is not consulted)
 

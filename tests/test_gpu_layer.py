@@ -147,7 +147,7 @@ def test_layer_deterministic(gpu):
         outs.append((y.clone(), layer.idx.clone(), layer.inv.clone(), layer.perm.clone(), layer.h.clone(),
                      layer.o.clone()))
     for a, b in zip(*outs):
-        assert torch.equal(a, b)
+        assert H.same_bits(a, b)
 
 
 def test_abi_errors_on_gpu(gpu):
