@@ -106,6 +106,7 @@ struct GemmOperands {
   int amode;            // kATiled, kAGather or kARows
   const int32_t* perm;  // kAGather: token of each local row; combine epilogue: the same for C's rows
   int64_t arows;        // kAGather, kARows: rows of x (out-of-range tokens read row 0)
+  int64_t prows;        // kAGather: entries of perm (rows past them read token 0)
   // GEMM 2 only, when Y is set: instead of storing row r of C, the epilogue writes the
   // combined output y[t] = gate[t][gslot] * C[r] (float32, row-major [T][NOUT]) for the token
   // t = perm[r] that owns the row (each token owns exactly one row of the problem).
@@ -164,23 +165,42 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   const uint16_t* dsrc[5];
   int lrow[5];  // first stage row of each instruction (wave-uniform)
   const int astep = op.amode == kATiled ? kTileElems : kTileCols;  // token-row elements per step
+  // local token row of this lane's 16 bytes in each instruction; bands past the live
+  // rows re-read the last live band (never stored)
+  int64_t trow[5];
+  int chunk[5];
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     if (WMG == 2) lrow[j] = wtok ? wave * 64 + j * 16 : (j < 4 ? BM + (wave - 4) * 64 + j * 16 : 256 + (wave - 4) * 16);
     else lrow[j] = j < 4 ? BM + wave * 64 + j * 16 : (five ? wave * 16 : 0);
     const int srow = lrow[j] + (lane >> 2);  // stage row (token rows 0..BM-1, then weight rows)
-    const int c = (lane & 3) ^ swz(srow);    // 16-byte chunk of the 32-column tile row fetched by this lane
-    const int inner = (lane >> 2) * kTileCols + c * 8;
+    chunk[j] = (lane & 3) ^ swz(srow);       // 16-byte chunk of the 32-column tile row fetched by this lane
+    int band = lrow[j] < BM ? lrow[j] / kTileRows : 0;
+    if (band >= live_bands) band = live_bands - 1;
+    trow[j] = (mband0 + band) * kTileRows + (lane >> 2);
+  }
+  // gathered rows: the five tokens are loaded together (one wait), from indices kept
+  // inside perm (a band may run past the last of its entries)
+  int64_t tok[5];
+  if (op.amode == kAGather) {
+    int32_t t32[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) t32[j] = op.perm[trow[j] < op.prows ? trow[j] : op.prows - 1];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) tok[j] = trow[j] < op.prows ? (int64_t)t32[j] : -1;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) tok[j] = trow[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int inner = (lane >> 2) * kTileCols + chunk[j] * 8;
     if (lrow[j] < BM) {
-      int band = lrow[j] / kTileRows;  // bands past the live rows re-read the last live band (never stored)
-      if (band >= live_bands) band = live_bands - 1;
       if (op.amode == kATiled) {
-        dsrc[j] = A + (mband0 + band) * nkf * kTileElems + inner;
+        dsrc[j] = A + (trow[j] >> 4) * nkf * kTileElems + inner;
       } else {  // row-major x: this lane's row is one token's row, 64 bytes of it per step
-        const int64_t row = (mband0 + band) * kTileRows + (lane >> 2);
-        int64_t tok = op.amode == kAGather ? (int64_t)op.perm[row] : row;
-        if (tok < 0 || tok >= op.arows) tok = 0;  // padding rows read token 0 (never stored)
-        dsrc[j] = A + tok * op.KP + c * 8;
+        const int64_t t = tok[j] < 0 || tok[j] >= op.arows ? 0 : tok[j];  // padding rows read token 0 (never stored)
+        dsrc[j] = A + t * op.KP + chunk[j] * 8;
       }
     } else {
       const int r = lrow[j] - BM;  // GEMM 1: rows < BW/2 are gate rows, the rest the up rows of the same columns
@@ -575,10 +595,10 @@ static moge_status_t launch_ggemm(const moge_shape_t& s, const GemmOperands& p0,
 }
 
 static GemmOperands operands(const void* A, const void* B0, const void* B1, void* C, int NOUT, int KD,
-                             int amode = 0, const int32_t* perm = nullptr, int64_t arows = 0) {
+                             int amode = 0, const int32_t* perm = nullptr, int64_t arows = 0, int64_t prows = 0) {
   return GemmOperands{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
                       static_cast<const uint16_t*>(B1), static_cast<uint16_t*>(C), NOUT,
-                      (int)round_up(KD, kTileCols), amode, perm, arows, nullptr, nullptr, 0, 0};
+                      (int)round_up(KD, kTileCols), amode, perm, arows, prows, nullptr, nullptr, 0, 0};
 }
 
 }  // namespace moge
@@ -710,7 +730,7 @@ extern "C" moge_status_t moge_expert_gate_up_gather(const moge_shape_t* shape, c
     return fail(MOGE_ERR_NULL, "ws_gate, ws_up and hs are required when F_shared > 0");
   if (F_shared == 0 && (ws_gate || ws_up || hs)) return fail(MOGE_ERR_ARG, "F_shared == 0 takes no shared operands");
   const GemmOperands none{};
-  st = launch_ggemm<true>(s, operands(x, w_gate, w_up, h, s.F, s.d, kAGather, perm, s.T), offsets, e_lo, e_hi - e_lo,
+  st = launch_ggemm<true>(s, operands(x, w_gate, w_up, h, s.F, s.d, kAGather, perm, s.T, rows_cap), offsets, e_lo, e_hi - e_lo,
                           rows_cap,
                           F_shared ? operands(x, ws_gate, ws_up, hs, F_shared, s.d, kARows, nullptr, s.T) : none,
                           F_shared ? s.T : 0, stream);

@@ -225,6 +225,46 @@ def test_gathered_gate_up_bitexact(gpu, w):
                            H.untile_rows(hs2, w.T, Fs, keep_pad_cols=True))
 
 
+def test_gathered_gate_up_clipped_capacity(gpu):
+    # a capacity below the padded rows, not a multiple of 16: the last segments are cut at
+    # rows_cap in both row sources alike, and perm holds exactly rows_cap entries
+    w = W.variant(MID, name="gather_clipped")
+    print(f"[gather clipped] {w.name}", flush=True)
+    dv = H.device_inputs(w)
+    idx, _, _ = oracle.route(H.oracle_logits_all(H.HostInputs(w)), w.M, w.Kp, "grouped")
+    s = moge.Shape(w.T, w.d, w.N, w.M, w.Kp, w.F, moge.BF16)
+    cap = moge.rows_bound(s, moge.ROUTE_GROUPED, 0, w.N)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    counts, offsets = torch.empty(w.N, **i32), torch.empty(w.N + 1, **i32)
+    inv, perm = torch.empty(w.T, w.K, **i32), torch.empty(cap, **i32)
+    xp = torch.empty(moge.tiled_elems(cap, w.d), **bf)
+    ws = torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda")
+    moge.dispatch(s, moge.ROUTE_GROUPED, torch.from_numpy(idx).cuda(), dv.x, 0, w.N, cap, counts, offsets, inv, perm,
+                  xp, ws)
+    torch.cuda.synchronize()
+    cn = counts.cpu().numpy()
+    P = H.segment_bases(cn, 0, w.N)
+    padded = int(P[-1])                          # P has N + 1 entries: the last is the padded total
+    cap2 = padded - 21
+    assert cap2 % 16 and cap2 < P[-2] + cn[-1]   # the last expert is cut inside one of its 16-row bands
+    perm2 = perm[:cap2].clone()
+    pg, pu = _pack(moge.BF16, dv.w_gate), _pack(moge.BF16, dv.w_up)
+    h1 = torch.full((moge.tiled_elems(cap2, w.F),), 3.0, **bf)
+    h2 = torch.full((moge.tiled_elems(cap2, w.F),), 5.0, **bf)
+    moge.expert_gate_up(s, xp, offsets, 0, w.N, cap2, pg, pu, h1)
+    moge.expert_gate_up_gather(s, dv.x, perm2, offsets, 0, w.N, cap2, pg, pu, h2, 0, None, None, None)
+    torch.cuda.synchronize()
+    live = _live_rows(w, cn, P)
+    live = torch.from_numpy(live[live < cap2]).long().cuda()
+    a = H.untile_rows(h1, cap2, w.F, keep_pad_cols=True)[live]
+    b = H.untile_rows(h2, cap2, w.F, keep_pad_cols=True)[live]
+    assert torch.equal(a, b)
+    # rows at and past rows_cap are never written
+    tail = H.untile_rows(h2, (cap2 + 15) // 16 * 16, w.F, keep_pad_cols=True)[cap2:]
+    assert bool((tail == 5.0).all())
+
+
 @pytest.mark.parametrize("w", [
     W.variant(MID, name="fused_group1_T333", T=333, Kp=1, e_lo=4, e_hi=8),
     W.variant(MID, name="fused_group0_T2000_N64", T=2000, d=256, N=64, M=8, Kp=1, F=136, e_lo=0, e_hi=8,
