@@ -8,7 +8,7 @@
 // (Pangu Pro MoE, lsdiaocha.cn summary, section 3): it is bound by weight
 // traffic at high concurrency and double-buffers its loads.  That kernel was
 // written for Ascend; on gfx950 the same ideas become:
-//   * bf16 v_mfma_f32_32x32x16_bf16 with float32 accumulators; a 512-thread
+//   * bf16 v_mfma_f32_16x16x32_bf16 with float32 accumulators; a 512-thread
 //     workgroup (two waves per SIMD) owns a 320-row x 256-weight-row tile (GEMM 1:
 //     128 gate + 128 up rows of the same 128 h columns, so the SwiGLU is fused into
 //     the epilogue; GEMM 2: 256 output columns), each wave a 160 x 64 part of it;
@@ -30,7 +30,9 @@
 //     swizzle keep the 16-byte fragment reads bank-conflict free at the LDS's full
 //     rate, which takes at least two waves per SIMD to reach;
 //   * a tile with few live rows (the last tile of an expert) skips the MFMAs of
-//     its empty 32-row blocks; the row blocks are interleaved over the waves;
+//     its empty 16-row blocks, so an expert's tail costs at most 15 rows of padding
+//     work (a 32-row MFMA block wasted about 6% of the work at 256 rows per
+//     expert); the row blocks are interleaved over the waves;
 //   * a persistent grid walks a device-built tile list (no host sync on the
 //     expert counts): every workgroup derives the per-expert tile counts from
 //     `offsets` in LDS.  Tiles of one expert are ordered in groups of 4 m-tiles,
@@ -57,11 +59,11 @@ constexpr int kStages = 4;
 constexpr int kThreads = 512;               // 8 waves: two per SIMD
 constexpr int kMaxBM = 320;                 // largest token-row tile
 
-// Two tile shapes; every wave owns 2 weight blocks of 32 rows and the token blocks
+// Two tile shapes; every wave owns 64 weight rows and the 16-row token blocks
 // wm, wm + WMG, wm + 2 WMG, ... of the tile (WMG wave rows x 8 / WMG wave columns):
-//   WMG = 2: 320 token rows x 256 weight rows (5 token blocks per wave) -- the
+//   WMG = 2: 320 token rows x 256 weight rows (10 token blocks per wave) -- the
 //            general case, where an expert's rows fill a 320-row tile;
-//   WMG = 1: 96 token rows x 512 weight rows (3 token blocks per wave) -- few rows
+//   WMG = 1: 96 token rows x 512 weight rows (6 token blocks per wave) -- few rows
 //            per expert (decode): twice the weight bytes per step, so each CU keeps
 //            twice as many weight bytes in flight and the weight stream runs nearer
 //            the HBM rate.
@@ -70,11 +72,11 @@ template <int WMG>
 struct TileShape;
 template <>
 struct TileShape<2> {
-  static constexpr int kBlocks = 5, BM = 320, BW = 256;
+  static constexpr int kBlocks = 10, BM = 320, BW = 256;  // kBlocks: 16-row token blocks per wave
 };
 template <>
 struct TileShape<1> {
-  static constexpr int kBlocks = 3, BM = 96, BW = 512;
+  static constexpr int kBlocks = 6, BM = 96, BW = 512;
 };
 template <int WMG>
 constexpr int stage_bytes() { return (TileShape<WMG>::BM + TileShape<WMG>::BW) * kRowB; }  // 36 / 38 KiB
@@ -117,9 +119,9 @@ struct GemmOperands {
 
 // One tile: reduction loop and epilogue, 8 waves.  Wave (wm, wn), wm in {0,1},
 // wn in {0..3} (320 x 256 tiles; wm = wave / 4, so each SIMD runs one wave of each
-// half), owns the token row blocks wm, wm+2, ..., wm+8 (32 rows each,
-// interleaved so a partly filled tile keeps the waves balanced) and 2 weight
-// blocks of 32 rows (GEMM 1: the gate and the up rows of the same 32 h columns;
+// half), owns the token row blocks wm, wm+2, ..., wm+18 (16 rows each,
+// interleaved so a partly filled tile keeps the waves balanced) and 4 weight
+// quarters of 16 rows (GEMM 1: the gate and the up rows of the same 32 h columns;
 // GEMM 2: 64 output columns).  NL of its row blocks hold live rows; the others
 // skip their MFMAs.  A tile spans 320 token rows so that an expert whose row
 // count is a little above 256 (the common case when the rows spread evenly over
@@ -226,43 +228,33 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
       if (WMG == 2 || five) dma_16x64(dsrc[4] + offa, st + (uint32_t)(lrow[4] * kRowB));
     }
   };
-  const int kc = (lane >> 5);  // logical chunk of this lane inside a 16-element sub-step
-  int arow[5], brow[2];
+  // Fragments of one 32-column step for v_mfma_f32_16x16x32_bf16: lane l holds 8
+  // consecutive columns (16-byte chunk l/16) of row l%16 of a 16-row block, for the
+  // weight operand (the MFMA's first) and the token operand alike; the product block
+  // gives lane l 4 consecutive weight rows 4(l/16) .. +3 (output columns) of token row
+  // l%16.  Token blocks of 16 rows keep a partly filled expert tail to at most 15
+  // padding rows of MFMA work.  Weight quarters q of 16 rows: GEMM 1: q = 0, 1 the gate
+  // rows of the wave's 32 columns, q = 2, 3 the up rows of the same columns; GEMM 2:
+  // q = 0..3 the wave's 64 output columns.
+  const int kq = lane >> 4;
+  int arow[NB], brow[4];
 #pragma unroll
-  for (int t = 0; t < 5; ++t) arow[t] = (wm + WMG * t) * 32 + (lane & 31);
+  for (int t = 0; t < NB; ++t) arow[t] = (wm + WMG * t) * 16 + (lane & 15);
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-    brow[cb] = BM + (SWIGLU ? cb * (BW / 2) + wn * 32 : wn * 64 + cb * 32) + (lane & 31);
-  auto frag = [&](int ks, int kk, bf16x8_t (&a)[5], bf16x8_t (&b)[2]) {
-    const char* sa = lds + (ks % kStages) * kStageB;
-    const char* sb = sa;
-    const int c = kk * 2 + kc;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-      b[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sb + brow[cb] * kRowB +
-                                                                              ((c ^ swz(brow[cb])) << 4)));
-#pragma unroll
-    for (int t = 0; t < NL; ++t)
-      a[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sa + arow[t] * kRowB +
-                                                                             ((c ^ swz(arow[t])) << 4)));
+  for (int q = 0; q < 4; ++q)
+    brow[q] = BM + (SWIGLU ? (q >> 1) * (BW / 2) + wn * 32 + (q & 1) * 16 : wn * 64 + q * 16) + (lane & 15);
+  auto rd = [&](const char* st, int row) {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + row * kRowB + ((kq ^ swz(row)) << 4)));
   };
-  f32x16_t acc[NL > 0 ? NL : 1][2];
+  f32x4_t acc[NL > 0 ? NL : 1][4];
   static_assert(NL <= NB, "row blocks per wave");
 #pragma unroll
   for (int t = 0; t < (NL > 0 ? NL : 1); ++t)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][cb][r] = 0.f;
-  auto mfma = [&](const bf16x8_t (&a)[5], const bf16x8_t (&b)[2]) {
-#pragma unroll
-    for (int t = 0; t < NL; ++t)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        acc[t][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[cb], a[t], acc[t][cb], 0, 0, 0);
-  };
+      for (int r = 0; r < 4; ++r) acc[t][q][r] = 0.f;
 
-  bf16x8_t a0[5], b0[2], a1[5], b1[2];
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // nothing of the previous tile in flight
   issue(0);
   issue(1);
@@ -274,18 +266,24 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   for (int ks = 0; ks < nkf; ++ks) {
     issue(ks + 3);
     if (NL) {
-      frag(ks, 0, a0, b0);
-      frag(ks, 1, a1, b1);
-      mfma(a0, b0);
-      mfma(a1, b1);
-      // the first half's reads, then the second half's reads each in the shadow of an MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, NL + 2, 0);
+      const char* st = lds + (ks % kStages) * kStageB;
+      bf16x8_t bq[4], at[NB];
 #pragma unroll
-      for (int i = 0; i < 2 * NL; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-        if (i < 2 + NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      for (int q = 0; q < 4; ++q) bq[q] = rd(st, brow[q]);
+#pragma unroll
+      for (int t = 0; t < NL; ++t) at[t] = rd(st, arow[t]);
+#pragma unroll
+      for (int t = 0; t < NL; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[q], at[t], acc[t][q], 0, 0, 0);
+      // the weight quarters and the first two token blocks, then each block's four MFMAs
+      // with the read of the block two ahead in their shadow
+      __builtin_amdgcn_sched_group_barrier(0x100, NL >= 2 ? 6 : 5, 0);
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (t + 2 < NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NL, 0);
     }
     // step ks+1 landed (this wave) and this step's LDS reads are done, so the DMA
     // issued after the barrier may overwrite stage ks % 4
@@ -300,7 +298,7 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   // the zero rows of the packed weights); GEMM 2 writes row-major [row][NOUT].
 #pragma unroll
   for (int t = 0; t < NL; ++t) {
-    const int trow = (wm + WMG * t) * 32 + (lane & 31);
+    const int trow = (wm + WMG * t) * 16 + (lane & 15);
     if (trow < mrows) {
       const int64_t row = row0 + trow;
       int64_t ytok = -1;
@@ -311,36 +309,33 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
         else ytok = -1;       // (a live row always has a token; never store out of range)
       }
 #pragma unroll
-      for (int cb = 0; cb < (SWIGLU ? 1 : 2); ++cb) {
+      for (int qo = 0; qo < (SWIGLU ? 2 : 4); ++qo) {
+        const int col = n0 + (SWIGLU ? wn * 32 : wn * 64) + qo * 16 + kq * 4;
+        if (col < (SWIGLU ? NPAD : NOUT)) {
+          uint16_t hv[4];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = n0 + (SWIGLU ? wn * 32 : wn * 64 + cb * 32) + g4 * 8 + (lane >> 5) * 4;
-          if (col < (SWIGLU ? NPAD : NOUT)) {
-            uint16_t hv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float v;
-              if (SWIGLU) {
-                const float gv = acc[t][0][g4 * 4 + i], uv = acc[t][1][g4 * 4 + i];
-                v = gv / (1.f + expf(-gv)) * uv;
-              } else {
-                v = acc[t][cb][g4 * 4 + i];
-              }
-              hv[i] = f32_to_bf16(v);
-            }
-            if (!SWIGLU && op.Y) {
-              // y = gate * o with o rounded to bf16 first, exactly as the separate combine pass
-              f32x4_t yv;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) yv[i] = fmaf(yg, bf16_to_f32(hv[i]), 0.f);
-              if (ytok >= 0) *reinterpret_cast<f32x4_t*>(op.Y + ytok * NOUT + col) = yv;
+          for (int i = 0; i < 4; ++i) {
+            float v;
+            if (SWIGLU) {
+              const float gv = acc[t][qo][i], uv = acc[t][2 + qo][i];
+              v = gv / (1.f + expf(-gv)) * uv;
             } else {
-              uint2 pk;
-              pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-              pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-              uint16_t* dst = SWIGLU ? C + tiled_index(row, col, NPAD) : C + row * NOUT + col;
-              *reinterpret_cast<uint2*>(dst) = pk;
+              v = acc[t][qo][i];
             }
+            hv[i] = f32_to_bf16(v);
+          }
+          if (!SWIGLU && op.Y) {
+            // y = gate * o with o rounded to bf16 first, exactly as the separate combine pass
+            f32x4_t yv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yv[i] = fmaf(yg, bf16_to_f32(hv[i]), 0.f);
+            if (ytok >= 0) *reinterpret_cast<f32x4_t*>(op.Y + ytok * NOUT + col) = yv;
+          } else {
+            uint2 pk;
+            pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+            pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+            uint16_t* dst = SWIGLU ? C + tiled_index(row, col, NPAD) : C + row * NOUT + col;
+            *reinterpret_cast<uint2*>(dst) = pk;
           }
         }
       }
@@ -465,14 +460,19 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
 
     // live row blocks of this wave (wave-uniform): block wm + WMG t is live if it starts below mrows
     const int wm = WMG == 2 ? wave >> 2 : 0;
-    const int nrb = (mrows + 31) / 32;
+    const int nrb = (mrows + 15) / 16;
     const int nl = nrb > wm ? (nrb - wm + WMG - 1) / WMG : 0;
 #define MOGE_TILE(NLV)                                                                                          \
   tile_compute<SWIGLU, NLV, WMG>(op, lds, op.A, mband0, wb0, wb1, wbands, nkf, mrows, row0, ncol0, op.NOUT, npad, \
                                  op.C)
     switch (nl) {
-      case 5: if constexpr (TileShape<WMG>::kBlocks >= 5) MOGE_TILE(5); break;
-      case 4: if constexpr (TileShape<WMG>::kBlocks >= 4) MOGE_TILE(4); break;
+      case 10: if constexpr (TileShape<WMG>::kBlocks >= 10) MOGE_TILE(10); break;
+      case 9: if constexpr (TileShape<WMG>::kBlocks >= 9) MOGE_TILE(9); break;
+      case 8: if constexpr (TileShape<WMG>::kBlocks >= 8) MOGE_TILE(8); break;
+      case 7: if constexpr (TileShape<WMG>::kBlocks >= 7) MOGE_TILE(7); break;
+      case 6: MOGE_TILE(6); break;
+      case 5: MOGE_TILE(5); break;
+      case 4: MOGE_TILE(4); break;
       case 3: MOGE_TILE(3); break;
       case 2: MOGE_TILE(2); break;
       case 1: MOGE_TILE(1); break;
