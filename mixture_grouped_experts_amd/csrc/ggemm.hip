@@ -83,6 +83,7 @@ constexpr int stage_bytes() { return (TileShape<WMG>::BM + TileShape<WMG>::BW) *
 template <int WMG>
 constexpr size_t gemm_lds() { return (size_t)kStages * stage_bytes<WMG>(); }  // 144 / 152 KiB
 constexpr int kGroupM = 4;                  // m-tiles per scheduling group
+constexpr int kAhead = 3;                   // token-block fragment reads issued ahead of the MFMAs
 
 __device__ __forceinline__ int swz(int r) { return lds_swz(r); }
 
@@ -276,13 +277,14 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
       for (int t = 0; t < NL; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[q], at[t], acc[t][q], 0, 0, 0);
-      // the weight quarters and the first two token blocks, then each block's four MFMAs
-      // with the read of the block two ahead in their shadow
-      __builtin_amdgcn_sched_group_barrier(0x100, NL >= 2 ? 6 : 5, 0);
+      // the weight quarters and the first three token blocks, then each block's four
+      // MFMAs with the read of the block three ahead in their shadow (one or two ahead,
+      // no hints, or all reads first were measured 1-7% slower)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 + (NL < kAhead ? NL : kAhead), 0);
 #pragma unroll
       for (int t = 0; t < NL; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        if (t + 2 < NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (t + kAhead < NL) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
     // step ks+1 landed (this wave) and this step's LDS reads are done, so the DMA
