@@ -136,6 +136,23 @@ def test_layer_one_expert_range(gpu):
     check_layer(w)
 
 
+def test_layer_empty_expert_range(gpu):
+    # a computed range that no token chooses: every GEMM's routed tile list is empty, and y is
+    # the shared expert's output alone, or all zeros without one
+    base = W.variant(W.decode(), name="empty_range", T=300, Kp=1, std_bias=20.0, F_shared=264,
+                     std_shared_down=0.02)
+    ridx, _, _ = oracle.route(H.oracle_logits_all(H.HostInputs(base)), base.M, base.Kp, "grouped")
+    empty = np.flatnonzero(np.bincount(ridx.ravel(), minlength=base.N) == 0)
+    assert empty.size, "a bias of std 20 leaves some experts unchosen"
+    e = int(empty[0])
+    for fs in (264, 0):
+        w = W.variant(base, name=f"empty_range_e{e}_Fs{fs}", e_lo=e, e_hi=e + 1, F_shared=fs)
+        layer, y = check_layer(w)
+        assert int(layer.counts[e].item()) == 0
+        if not fs:
+            assert bool((y == 0).all())
+
+
 def test_layer_deterministic(gpu):
     w = W.variant(W.decode(), name="det", T=600, std_bias=2.0)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, 0, "bf16")
