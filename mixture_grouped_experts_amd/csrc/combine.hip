@@ -6,8 +6,12 @@
 // HBM-bound gather.  A wave takes one (token, 512-column block) item, so even a
 // few tokens spread over the whole chip; each lane owns 8 consecutive hidden
 // elements.  The token's slots are read in batches of 8 whose row loads are all
-// in flight together (the slot indices are wave-uniform, read through the scalar
-// cache), then accumulated in float32 in slot order (deterministic).
+// in flight together (lane j reads slot j's row index and gate; the contributing
+// slots are compacted with a ballot and handed to the whole wave with readlane),
+// then accumulated in float32 in slot order (deterministic).  The expert
+// rows are read once and y is written once, so both go with the non-temporal hint
+// (kept out of the caches' working sets: 287 -> 239 us on 8192 tokens x 8 slots x
+// 7680 columns).
 #include "moge_internal.hpp"
 
 namespace moge {
@@ -42,7 +46,9 @@ struct Raw8;
 template <>
 struct Raw8<uint16_t> {
   u32x4_t u;
-  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  }
   __device__ __forceinline__ void fma_into(float g, float* acc) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -134,8 +140,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int K, int d, c
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
     f32x4_t a = {acc[0], acc[1], acc[2], acc[3]}, b = {acc[4], acc[5], acc[6], acc[7]};
-    *reinterpret_cast<f32x4_t*>(y + t * d + c) = a;
-    *reinterpret_cast<f32x4_t*>(y + t * d + c + 4) = b;
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(y + t * d + c));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(y + t * d + c + 4));
   }
 }
 

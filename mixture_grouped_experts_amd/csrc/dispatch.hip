@@ -80,7 +80,6 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
   int* pbase = base + N;  // P(e): first local row of expert e (16-row aligned segments)
   __shared__ int scratch[4];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t b = blockIdx.x;
   const int64_t t0 = b * kTB;
 
