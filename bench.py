@@ -189,8 +189,8 @@ def cpu_baseline(w, seconds: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the multi-GPU expert-group sharding is a design, not code)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the expert-parallel "
+              f"sharding of the layer over several GPUs is described, not implemented", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration:
