@@ -298,6 +298,45 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   // epilogue (rows of dead blocks are never stored).  GEMM 1 writes the tiled h
   // (NPAD = F rounded up to 32 columns; its padding columns come out as zeros from
   // the zero rows of the packed weights); GEMM 2 writes row-major [row][NOUT].
+  if (!SWIGLU && !op.Y && (NOUT & 7) == 0) {
+    // GEMM 2 through LDS (the ring is idle now): each wave writes its 64 columns of up
+    // to kPassBlocks row blocks into its own 10 KiB of LDS as 128-byte rows (16-byte
+    // chunks XOR-swizzled by row), then reads back 16 bytes per lane, so each row's
+    // 128 bytes leave as whole cache lines instead of four 32-byte pieces.  Only this
+    // wave touches its region, so the ordering needed is the wave's own (its LDS
+    // operations complete in order; the waits keep the compiler from reordering).
+    constexpr int kPassBlocks = 5;
+    char* wl = lds + wave * (kPassBlocks * 16 * 128);
+#pragma unroll
+    for (int p0 = 0; p0 < NL; p0 += kPassBlocks) {
+      const int p1 = p0 + kPassBlocks < NL ? p0 + kPassBlocks : NL;
+#pragma unroll
+      for (int t = p0; t < p1; ++t) {
+        const int r = (t - p0) * 16 + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16(acc[t][q][0]) | ((uint32_t)f32_to_bf16(acc[t][q][1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(acc[t][q][2]) | ((uint32_t)f32_to_bf16(acc[t][q][3]) << 16);
+          const int ch = 2 * q + (kq >> 1);
+          *reinterpret_cast<uint2*>(wl + r * 128 + ((ch ^ (r & 7)) << 4) + (kq & 1) * 8) = pk;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(lgkm0_imm());
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < (p1 - p0) * 2; ++i) {
+        const int r = i * 8 + (lane >> 3), c8 = lane & 7;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + r * 128 + ((c8 ^ (r & 7)) << 4));
+        const int trow = (wm + WMG * (p0 + (r >> 4))) * 16 + (r & 15);
+        const int col = n0 + wn * 64 + c8 * 8;
+        if (trow < mrows && col < NOUT) *reinterpret_cast<u32x4_t*>(C + (row0 + trow) * NOUT + col) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(lgkm0_imm());
+      __builtin_amdgcn_wave_barrier();
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < NL; ++t) {
     const int trow = (wm + WMG * t) * 16 + (lane & 15);

@@ -78,6 +78,7 @@ __device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3
 // wave outstanding; the second form also waits for all of the wave's LDS reads.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+constexpr int lgkm0_imm() { return 15 | (7 << 4) | (3 << 14); }  // all of the wave's LDS operations done
 
 // LDS byte address of a __shared__ pointer (what M0 takes for a direct load).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
