@@ -337,6 +337,47 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
     }
     return;
   }
+  if (SWIGLU) {
+    // GEMM 1: a wave's 16 rows x 32 h columns of one row block are exactly one 1 KiB
+    // tile of the tiled layout.  Each lane puts its SwiGLU values into the wave's own
+    // LDS (16-byte chunks XOR-swizzled by row / 4) and reads back the 16 bytes at its
+    // position in the tile, so the block leaves as one contiguous 1 KiB store (rows
+    // past mrows masked) instead of two stores of 32-byte pieces.
+    char* wl = lds + wave * (TileShape<WMG>::kBlocks * 1024);
+    const int col0 = n0 + wn * 32;
+    if (col0 < NPAD) {
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        const int r = lane & 15;
+#pragma unroll
+        for (int qo = 0; qo < 2; ++qo) {
+          uint16_t hv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = acc[t][qo][i], uv = acc[t][2 + qo][i];
+            hv[i] = f32_to_bf16(gv / (1.f + expf(-gv)) * uv);
+          }
+          uint2 pk;
+          pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+          pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+          const int ch = 2 * qo + (kq >> 1);
+          *reinterpret_cast<uint2*>(wl + t * 1024 + r * 64 + ((ch ^ ((r >> 2) & 3)) << 4) + (kq & 1) * 8) = pk;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(lgkm0_imm());
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        const int r = lane >> 2, c = lane & 3;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + t * 1024 + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+        const int trow = (wm + WMG * t) * 16 + r;
+        if (trow < mrows) *reinterpret_cast<u32x4_t*>(C + tiled_index(row0 + trow, col0 + c * 8, NPAD)) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(lgkm0_imm());
+      __builtin_amdgcn_wave_barrier();
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < NL; ++t) {
     const int trow = (wm + WMG * t) * 16 + (lane & 15);
