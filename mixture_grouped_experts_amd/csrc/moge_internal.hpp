@@ -49,11 +49,13 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
 // binary32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
+// float -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (two values per
+// instruction where two conversions meet).  Checked on the GPU against the plain
+// integer rounding (add 0x7FFF plus the kept lsb, keep the top half) over every
+// exponent's ties and neighbours, denormals, overflow, infinities and 16 M random
+// patterns: identical for every finite value and infinity; NaNs come out quiet.  In
+// the GEMM epilogues the software form cost 7-8 vector instructions per value.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
