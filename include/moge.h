@@ -140,6 +140,18 @@ moge_status_t moge_pack_weights(int32_t dtype, int64_t E, int64_t rows, int64_t 
                                 hipStream_t stream);
 
 /*
+ * moge_round_bf16 -- y[i] = x[i] rounded to bf16 (round to nearest, ties to even;
+ * infinities kept; a NaN stays a NaN, made quiet), the rounding the library
+ * applies where the layer stores bf16 values: h before the down projection and
+ * the expert outputs.  For callers that prepare bf16 activations with the same
+ * rounding, and to check it.
+ *   x  [n] float32 device;  y [n] bf16 bit patterns (uint16) device, not
+ *      overlapping x;  n >= 0 (0: nothing is launched).
+ * Errors: MOGE_ERR_SHAPE (n < 0), MOGE_ERR_NULL (x or y NULL with n > 0).
+ */
+moge_status_t moge_round_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream);
+
+/*
  * moge_route -- router scores, global softmax, top-K' per group ([P1] section 1).
  *   x        [T][d] (dtype) or NULL; w_router [N][d] (dtype); bias [N] f32 or NULL.
  *   logits   [T][N] f32.  If x != NULL: scores are computed as x.w_router^T (+bias)

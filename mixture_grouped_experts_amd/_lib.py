@@ -38,7 +38,7 @@ EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_
            "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
            "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_expert_down_combine",
            "moge_set_gemm_tiles", "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_version",
-           "moge_last_error")
+           "moge_last_error", "moge_round_bf16")
 
 
 class Shape(ctypes.Structure):
@@ -75,6 +75,8 @@ _lib.moge_packed_weight_elems.argtypes = [_I64, _I64]
 _lib.moge_packed_weight_elems.restype = _I64
 _lib.moge_pack_weights.argtypes = [_I32, _I64, _I64, _I64, _P, _P, _P]
 _lib.moge_pack_weights.restype = ctypes.c_int
+_lib.moge_round_bf16.argtypes = [_P, _P, _I64, _P]
+_lib.moge_round_bf16.restype = ctypes.c_int
 _lib.moge_workspace_size.argtypes = [_SP, _I32]
 _lib.moge_workspace_size.restype = ctypes.c_size_t
 _lib.moge_route.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _P]
@@ -170,6 +172,15 @@ def pack_weights(dtype: int, w, out, stream=None) -> None:
     st = _lib.moge_pack_weights(dtype, E, rows, cols, _ptr(w, "w", et, E * rows * cols),
                                 _ptr(out, "out", et, E * packed_weight_elems(rows, cols)), _stream(stream))
     _check("moge_pack_weights", st)
+
+
+def round_bf16(x, y, stream=None) -> None:
+    """y = x (float32) rounded to bf16 as the library stores bf16 values; y holds the bit patterns
+    (torch.int16 or torch.bfloat16 viewed as int16) with x.numel() elements."""
+    n = x.numel()
+    yv = y.view(torch.int16) if y.dtype == torch.bfloat16 else y
+    st = _lib.moge_round_bf16(_ptr(x, "x", torch.float32, n), _ptr(yv, "y", torch.int16, n), n, _stream(stream))
+    _check("moge_round_bf16", st)
 
 
 def workspace_size(shape: Shape, stage: int = STAGE_DISPATCH) -> int:

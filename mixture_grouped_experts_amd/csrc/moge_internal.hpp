@@ -50,11 +50,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 
 // binary32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
 // float -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 (two values per
-// instruction where two conversions meet).  Checked on the GPU against the plain
-// integer rounding (add 0x7FFF plus the kept lsb, keep the top half) over every
-// exponent's ties and neighbours, denormals, overflow, infinities and 16 M random
-// patterns: identical for every finite value and infinity; NaNs come out quiet.  In
-// the GEMM epilogues the software form cost 7-8 vector instructions per value.
+// instruction where two conversions meet).  It equals the plain integer rounding (add
+// 0x7FFF plus the kept lsb, keep the top half) for every finite value and infinity;
+// NaNs come out quiet (moge_round_bf16 exposes it; its test checks every exponent's
+// ties and neighbours, denormals, overflow and a million random patterns).  In the
+// GEMM epilogues the integer form cost 7-8 vector instructions per value.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float wave_max(float v) {

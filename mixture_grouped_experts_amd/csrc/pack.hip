@@ -48,3 +48,25 @@ extern "C" moge_status_t moge_pack_weights(int32_t dtype, int64_t E, int64_t row
   const moge_status_t st = check_launch("pack_weights_kernel");
   return st == MOGE_OK ? ok() : st;
 }
+
+namespace moge {
+
+// float32 -> bf16 with the rounding of the expert GEMMs' outputs (f32_to_bf16).
+__global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y,
+                                                         int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) y[i] = f32_to_bf16(x[i]);
+}
+
+}  // namespace moge
+
+extern "C" moge_status_t moge_round_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream) {
+  if (n < 0) return fail(MOGE_ERR_SHAPE, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!x || !y) return fail(MOGE_ERR_NULL, "x and y are required");
+  int64_t grid = (n + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(round_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, y, n);
+  const moge_status_t st = check_launch("round_bf16_kernel");
+  return st == MOGE_OK ? ok() : st;
+}

@@ -86,6 +86,17 @@ def _call(fn, *args):
     return getattr(ctypes.CDLL(moge.LIB_PATH), fn)(*args)
 
 
+def test_round_bf16_argument_errors():
+    lib = ctypes.CDLL(moge.LIB_PATH)
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: every case returns before a launch
+    lib.moge_round_bf16.argtypes = [P, P, ctypes.c_int64, P]
+    assert lib.moge_round_bf16(fake, fake, -1, None) == 2      # MOGE_ERR_SHAPE
+    assert lib.moge_round_bf16(None, fake, 4, None) == 3       # MOGE_ERR_NULL
+    assert lib.moge_round_bf16(fake, None, 4, None) == 3
+    assert lib.moge_round_bf16(None, None, 0, None) == 0       # nothing to round
+
+
 def test_null_and_argument_errors_before_any_launch():
     lib = ctypes.CDLL(moge.LIB_PATH)
     s = S()
