@@ -256,7 +256,9 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[t][q][r] = 0.f;
 
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // nothing of the previous tile in flight
+  // (the previous tile's epilogue stores may still be in flight: the loads do not
+  // depend on them, and loads complete in order among themselves, so each wait
+  // below still guarantees its step; older stores only make it stricter)
   issue(0);
   issue(1);
   issue(2);
@@ -378,18 +380,36 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
     }
     return;
   }
+  // combine epilogue: the token and gate of each of this lane's rows.  The loads are
+  // unconditional (clamped indices) and their values used on every path, so none is
+  // still outstanding when the next tile's reduction loop starts.
+  int64_t ytoks[NL > 0 ? NL : 1];
+  float ygs[NL > 0 ? NL : 1];
+  if (!SWIGLU && op.Y) {
+    int32_t pv[NL > 0 ? NL : 1];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      const int trow = (wm + WMG * t) * 16 + (lane & 15);
+      pv[t] = op.perm[row0 + (trow < mrows ? trow : 0)];
+    }
+    float gv[NL > 0 ? NL : 1];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      const int trow = (wm + WMG * t) * 16 + (lane & 15);
+      // (a live row always has a token; never store out of range)
+      ytoks[t] = trow < mrows && pv[t] >= 0 && pv[t] < op.arows ? (int64_t)pv[t] : -1;
+      gv[t] = op.gate[(ytoks[t] >= 0 ? ytoks[t] : 0) * op.gstride + op.gslot];
+    }
+#pragma unroll
+    for (int t = 0; t < NL; ++t) ygs[t] = ytoks[t] >= 0 ? gv[t] : 0.f;
+  }
 #pragma unroll
   for (int t = 0; t < NL; ++t) {
     const int trow = (wm + WMG * t) * 16 + (lane & 15);
     if (trow < mrows) {
       const int64_t row = row0 + trow;
-      int64_t ytok = -1;
-      float yg = 0.f;
-      if (!SWIGLU && op.Y) {  // combine epilogue: the row's token and its gate
-        ytok = op.perm[row];
-        if (ytok >= 0 && ytok < op.arows) yg = op.gate[ytok * op.gstride + op.gslot];
-        else ytok = -1;       // (a live row always has a token; never store out of range)
-      }
+      const int64_t ytok = !SWIGLU && op.Y ? ytoks[t] : -1;
+      const float yg = !SWIGLU && op.Y ? ygs[t] : 0.f;
 #pragma unroll
       for (int qo = 0; qo < (SWIGLU ? 2 : 4); ++qo) {
         const int col = n0 + (SWIGLU ? wn * 32 : wn * 64) + qo * 16 + kq * 4;
