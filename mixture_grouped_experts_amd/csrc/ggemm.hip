@@ -142,12 +142,100 @@ struct GemmOperands {
 // the row-major x through perm (16 rows x 64 B per instruction), which saves
 // materialising x_perm at all.
 
+// First stage row of DMA instruction j of this wave (wave-uniform):
+//   320 x 256: waves 0-3 move token rows wave*64 .. +64 (4 instructions); waves
+//              4-7 weight rows (wave-4)*64 .. +64 and token rows 256 + (wave-4)*16;
+//   96 x 512:  every wave moves weight rows wave*64 .. +64; waves 0-5 also token
+//              rows wave*16 .. +16.
+// Each instruction moves one tile of 16 rows x 32 columns; lane l brings 16 bytes of
+// row lrow + l/4.
+template <int WMG>
+__device__ __forceinline__ int dma_stage_row(int wave, int j) {
+  constexpr int BM = TileShape<WMG>::BM;
+  const bool wtok = WMG == 2 && wave < 4;
+  const bool five = WMG == 2 ? wave >= 4 : wave < BM / kTileRows;
+  if (WMG == 2) return wtok ? wave * 64 + j * 16 : (j < 4 ? BM + (wave - 4) * 64 + j * 16 : 256 + (wave - 4) * 16);
+  return j < 4 ? BM + wave * 64 + j * 16 : (five ? wave * 16 : 0);
+}
+
+// The token row read by this lane in each of its DMA instructions: the local row for
+// the tiled A (bands past the live rows re-read the last live band, never stored), the
+// token itself for the gathered A (loaded from perm, all five loads together, indices
+// kept inside perm; -1 past it), the row for row-major A.
+template <int WMG>
+__device__ __forceinline__ void token_rows(const GemmOperands& op, int64_t mband0, int mrows, int32_t (&tok)[5]) {
+  constexpr int BM = TileShape<WMG>::BM;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int live_bands = (mrows + kTileRows - 1) / kTileRows;
+  int64_t trow[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int lrow = dma_stage_row<WMG>(wave, j);
+    int band = lrow < BM ? lrow / kTileRows : 0;
+    if (band >= live_bands) band = live_bands - 1;
+    trow[j] = (mband0 + band) * kTileRows + (lane >> 2);
+  }
+  if (op.amode == kAGather) {
+    int32_t t32[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) t32[j] = op.perm[trow[j] < op.prows ? trow[j] : op.prows - 1];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) tok[j] = trow[j] < op.prows ? t32[j] : -1;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) tok[j] = (int32_t)trow[j];
+  }
+}
+
+// Per-lane global sources of this wave's DMA instructions for step 0 of a tile.
+template <bool SWIGLU, int WMG>
+__device__ __forceinline__ void dma_sources(const GemmOperands& op, const uint16_t* __restrict__ wbase0,
+                                            const uint16_t* __restrict__ wbase1, int wbands, int nkf, int n0,
+                                            const int32_t (&tok)[5], const uint16_t* (&dsrc)[5]) {
+  constexpr int BM = TileShape<WMG>::BM, BW = TileShape<WMG>::BW;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int lrow = dma_stage_row<WMG>(wave, j);
+    const int srow = lrow + (lane >> 2);                 // stage row (token rows 0..BM-1, then weight rows)
+    const int chunk = (lane & 3) ^ swz(srow);            // 16-byte chunk of the tile row fetched by this lane
+    const int inner = (lane >> 2) * kTileCols + chunk * 8;
+    if (lrow < BM) {
+      if (op.amode == kATiled) {
+        dsrc[j] = op.A + (int64_t)(tok[j] >> 4) * nkf * kTileElems + inner;
+      } else {  // row-major x: this lane's row is one token's row, 64 bytes of it per step
+        const int64_t t = tok[j] < 0 || tok[j] >= op.arows ? 0 : tok[j];  // padding rows read token 0 (never stored)
+        dsrc[j] = op.A + t * op.KP + chunk * 8;
+      }
+    } else {
+      const int r = lrow - BM;  // GEMM 1: rows < BW/2 are gate rows, the rest the up rows of the same columns
+      int band = (SWIGLU ? n0 + (r & (BW / 2 - 1)) : n0 + r) / kTileRows;
+      if (band >= wbands) band = wbands - 1;
+      dsrc[j] = (SWIGLU && r >= BW / 2 ? wbase1 : wbase0) + (int64_t)band * nkf * kTileElems + inner;
+    }
+  }
+}
+
+// Where a tile's first three steps come from and where the next tile's go: with pre,
+// steps 0-2 were issued by the previous tile into stages 1-3 (step s in stage
+// (1 + s) % 4); with chain, this tile issues the next one's steps 0-2 into stages 1-3
+// right after its reduction loop, so they land during this tile's epilogue, which
+// then stages its output in stage 0 only.
+struct NextTile {
+  const uint16_t* wb0;
+  const uint16_t* wb1;
+  int64_t mband0;
+  int wbands, nkf, n0, mrows, unused0, unused1;  // (no padding bytes: copies stay in registers)
+};
+
 template <bool SWIGLU, int NL, int WMG>
 __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __restrict__ lds,
-                                             const uint16_t* __restrict__ A, int64_t mband0,
                                              const uint16_t* __restrict__ wbase0, const uint16_t* __restrict__ wbase1,
                                              int wbands, int nkf, int mrows, int64_t row0, int n0, int NOUT, int NPAD,
-                                             uint16_t* __restrict__ C) {
+                                             uint16_t* __restrict__ C, const int32_t (&tokc)[5], bool pre, bool chain,
+                                             const GemmOperands& nop, const NextTile& nx, int32_t (&tokn)[5]) {
   constexpr int BM = TileShape<WMG>::BM, BW = TileShape<WMG>::BW, NB = TileShape<WMG>::kBlocks;
   constexpr int kStageB = stage_bytes<WMG>();
   const int tid = threadIdx.x, lane = tid & 63;
@@ -155,79 +243,32 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   // the two waves on a SIMD (w and w + 4) take different token-row halves, so an odd
   // number of live row blocks still gives every SIMD the same MFMA count
   const int wm = WMG == 2 ? wave >> 2 : 0, wn = WMG == 2 ? wave & 3 : wave;
-  // DMA sources: instruction j moves the 16 stage rows at lrow[j] .. +16 (one tile of
-  // 16 rows x 32 columns); lane l brings 16 bytes of row lrow[j] + l/4.
-  //   320 x 256: waves 0-3 move token rows wave*64 .. +64 (4 instructions); waves
-  //              4-7 weight rows (wave-4)*64 .. +64 and token rows 256 + (wave-4)*16;
-  //   96 x 512:  every wave moves weight rows wave*64 .. +64; waves 0-5 also token
-  //              rows wave*16 .. +16.
-  // wtok: this wave's first four instructions are token rows; five: it issues five.
   const bool wtok = WMG == 2 && wave < 4;
   const bool five = WMG == 2 ? wave >= 4 : wave < BM / kTileRows;
-  const int live_bands = (mrows + kTileRows - 1) / kTileRows;
+  int lrow[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) lrow[j] = dma_stage_row<WMG>(wave, j);
   const uint16_t* dsrc[5];
-  int lrow[5];  // first stage row of each instruction (wave-uniform)
+  dma_sources<SWIGLU, WMG>(op, wbase0, wbase1, wbands, nkf, n0, tokc, dsrc);
   const int astep = op.amode == kATiled ? kTileElems : kTileCols;  // token-row elements per step
-  // local token row of this lane's 16 bytes in each instruction; bands past the live
-  // rows re-read the last live band (never stored)
-  int64_t trow[5];
-  int chunk[5];
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    if (WMG == 2) lrow[j] = wtok ? wave * 64 + j * 16 : (j < 4 ? BM + (wave - 4) * 64 + j * 16 : 256 + (wave - 4) * 16);
-    else lrow[j] = j < 4 ? BM + wave * 64 + j * 16 : (five ? wave * 16 : 0);
-    const int srow = lrow[j] + (lane >> 2);  // stage row (token rows 0..BM-1, then weight rows)
-    chunk[j] = (lane & 3) ^ swz(srow);       // 16-byte chunk of the 32-column tile row fetched by this lane
-    int band = lrow[j] < BM ? lrow[j] / kTileRows : 0;
-    if (band >= live_bands) band = live_bands - 1;
-    trow[j] = (mband0 + band) * kTileRows + (lane >> 2);
-  }
-  // gathered rows: the five tokens are loaded together (one wait), from indices kept
-  // inside perm (a band may run past the last of its entries)
-  int64_t tok[5];
-  if (op.amode == kAGather) {
-    int32_t t32[5];
-#pragma unroll
-    for (int j = 0; j < 5; ++j) t32[j] = op.perm[trow[j] < op.prows ? trow[j] : op.prows - 1];
-#pragma unroll
-    for (int j = 0; j < 5; ++j) tok[j] = trow[j] < op.prows ? (int64_t)t32[j] : -1;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 5; ++j) tok[j] = trow[j];
-  }
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const int inner = (lane >> 2) * kTileCols + chunk[j] * 8;
-    if (lrow[j] < BM) {
-      if (op.amode == kATiled) {
-        dsrc[j] = A + (trow[j] >> 4) * nkf * kTileElems + inner;
-      } else {  // row-major x: this lane's row is one token's row, 64 bytes of it per step
-        const int64_t t = tok[j] < 0 || tok[j] >= op.arows ? 0 : tok[j];  // padding rows read token 0 (never stored)
-        dsrc[j] = A + t * op.KP + chunk[j] * 8;
-      }
-    } else {
-      const int r = lrow[j] - BM;  // GEMM 1: rows < BW/2 are gate rows, the rest the up rows of the same columns
-      int band = (SWIGLU ? n0 + (r & (BW / 2 - 1)) : n0 + r) / kTileRows;
-      if (band >= wbands) band = wbands - 1;
-      dsrc[j] = (SWIGLU && r >= BW / 2 ? wbase1 : wbase0) + (int64_t)band * nkf * kTileElems + inner;
-    }
-  }
-  // Step ks into stage ks % 4 (steps past the last full step reload step 0); the
-  // waits are explicit (vmcnt_imm) and each is followed by a barrier before the
+  const int sbase = pre ? 1 : 0;
+  // Step ks into stage (sbase + ks) % 4 (steps past the last full step reload step 0);
+  // the waits are explicit (vmcnt_imm) and each is followed by a barrier before the
   // stage is read.
   const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](int ks) {
-    const int kq = ks < nkf ? ks : 0;
-    const int offa = kq * astep, offb = kq * kTileElems;
-    const uint32_t st = lds0 + (uint32_t)((ks % kStages) * kStageB);
+  auto issue_from = [&](const uint16_t* const (&src)[5], int offa, int offb, uint32_t st) {
     if (wtok) {  // four token-row instructions
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma_16x64(dsrc[j] + offa, st + (uint32_t)(lrow[j] * kRowB));
+      for (int j = 0; j < 4; ++j) dma_16x64(src[j] + offa, st + (uint32_t)(lrow[j] * kRowB));
     } else {     // four weight-row instructions and (five) one token-row instruction
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma_16x64_stream(dsrc[j] + offb, st + (uint32_t)(lrow[j] * kRowB));
-      if (WMG == 2 || five) dma_16x64(dsrc[4] + offa, st + (uint32_t)(lrow[4] * kRowB));
+      for (int j = 0; j < 4; ++j) dma_16x64_stream(src[j] + offb, st + (uint32_t)(lrow[j] * kRowB));
+      if (WMG == 2 || five) dma_16x64(src[4] + offa, st + (uint32_t)(lrow[4] * kRowB));
     }
+  };
+  auto issue = [&](int ks) {
+    const int kq = ks < nkf ? ks : 0;
+    issue_from(dsrc, kq * astep, kq * kTileElems, lds0 + (uint32_t)(((sbase + ks) & (kStages - 1)) * kStageB));
   };
   // Fragments of one 32-column step for v_mfma_f32_16x16x32_bf16: lane l holds 8
   // consecutive columns (16-byte chunk l/16) of row l%16 of a 16-row block, for the
@@ -259,17 +300,20 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   // (the previous tile's epilogue stores may still be in flight: the loads do not
   // depend on them, and loads complete in order among themselves, so each wait
   // below still guarantees its step; older stores only make it stricter)
-  issue(0);
-  issue(1);
-  issue(2);
-  // step 0 landed (this wave issues 4 or 5 loads per step)
+  if (!pre) {
+    issue(0);
+    issue(1);
+    issue(2);
+  }
+  // step 0 landed (this wave issues 4 or 5 loads per step; with pre, steps 0-2 and
+  // then the previous epilogue's stores are the operations in flight)
   if (five) __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
   __syncthreads();
   for (int ks = 0; ks < nkf; ++ks) {
     issue(ks + 3);
     if (NL) {
-      const char* st = lds + (ks % kStages) * kStageB;
+      const char* st = lds + ((sbase + ks) & (kStages - 1)) * kStageB;
       bf16x8_t bq[4], at[NB];
 #pragma unroll
       for (int q = 0; q < 4; ++q) bq[q] = rd(st, brow[q]);
@@ -297,6 +341,16 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // drain the trailing reloads before LDS is reused
   __syncthreads();
+  if (chain) {  // the next tile's steps 0-2 into stages 1-3, in flight during this epilogue
+    const uint16_t* ndsrc[5];
+    // GEMM 2's token rows are plain arithmetic, done here (its registers are at their
+    // limit in the loop); GEMM 1's were loaded by the caller a tile ahead
+    if constexpr (!SWIGLU) token_rows<WMG>(nop, nx.mband0, nx.mrows, tokn);
+    dma_sources<SWIGLU, WMG>(nop, nx.wb0, nx.wb1, nx.wbands, nx.nkf, nx.n0, tokn, ndsrc);
+    const int nastep = nop.amode == kATiled ? kTileElems : kTileCols;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) issue_from(ndsrc, j * nastep, j * kTileElems, lds0 + (uint32_t)((1 + j) * kStageB));
+  }
   // epilogue (rows of dead blocks are never stored).  GEMM 1 writes the tiled h
   // (NPAD = F rounded up to 32 columns; its padding columns come out as zeros from
   // the zero rows of the packed weights); GEMM 2 writes row-major [row][NOUT].
@@ -307,7 +361,7 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
     // 128 bytes leave as whole cache lines instead of four 32-byte pieces.  Only this
     // wave touches its region, so the ordering needed is the wave's own (its LDS
     // operations complete in order; the waits keep the compiler from reordering).
-    constexpr int kPassBlocks = 5;
+    constexpr int kPassBlocks = 5;  // 10 KiB per wave (GEMM 2 does not chain: the ring is free)
     char* wl = lds + wave * (kPassBlocks * 16 * 128);
 #pragma unroll
     for (int p0 = 0; p0 < NL; p0 += kPassBlocks) {
@@ -345,38 +399,44 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
     // LDS (16-byte chunks XOR-swizzled by row / 4) and reads back the 16 bytes at its
     // position in the tile, so the block leaves as one contiguous 1 KiB store (rows
     // past mrows masked) instead of two stores of 32-byte pieces.
-    char* wl = lds + wave * (TileShape<WMG>::kBlocks * 1024);
+    constexpr int kPassBlocks = 4;  // 4 KiB per wave: the 8 waves stay inside stage 0
+    char* wl = lds + wave * (kPassBlocks * 1024);
     const int col0 = n0 + wn * 32;
     if (col0 < NPAD) {
 #pragma unroll
-      for (int t = 0; t < NL; ++t) {
-        const int r = lane & 15;
+      for (int p0 = 0; p0 < NL; p0 += kPassBlocks) {
+        const int p1 = p0 + kPassBlocks < NL ? p0 + kPassBlocks : NL;
 #pragma unroll
-        for (int qo = 0; qo < 2; ++qo) {
-          uint16_t hv[4];
+        for (int t = p0; t < p1; ++t) {
+          const int r = lane & 15;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float gv = acc[t][qo][i], uv = acc[t][2 + qo][i];
-            hv[i] = f32_to_bf16(gv / (1.f + expf(-gv)) * uv);
+          for (int qo = 0; qo < 2; ++qo) {
+            uint16_t hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float gv = acc[t][qo][i], uv = acc[t][2 + qo][i];
+              hv[i] = f32_to_bf16(gv / (1.f + expf(-gv)) * uv);
+            }
+            uint2 pk;
+            pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+            pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+            const int ch = 2 * qo + (kq >> 1);
+            *reinterpret_cast<uint2*>(wl + (t - p0) * 1024 + r * 64 + ((ch ^ ((r >> 2) & 3)) << 4) + (kq & 1) * 8) = pk;
           }
-          uint2 pk;
-          pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-          pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-          const int ch = 2 * qo + (kq >> 1);
-          *reinterpret_cast<uint2*>(wl + t * 1024 + r * 64 + ((ch ^ ((r >> 2) & 3)) << 4) + (kq & 1) * 8) = pk;
         }
-      }
-      __builtin_amdgcn_s_waitcnt(lgkm0_imm());
-      __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(lgkm0_imm());
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int t = 0; t < NL; ++t) {
-        const int r = lane >> 2, c = lane & 3;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + t * 1024 + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
-        const int trow = (wm + WMG * t) * 16 + r;
-        if (trow < mrows) *reinterpret_cast<u32x4_t*>(C + tiled_index(row0 + trow, col0 + c * 8, NPAD)) = v;
+        for (int t = p0; t < p1; ++t) {
+          const int r = lane >> 2, c = lane & 3;
+          const u32x4_t v =
+              *reinterpret_cast<const u32x4_t*>(wl + (t - p0) * 1024 + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+          const int trow = (wm + WMG * t) * 16 + r;
+          if (trow < mrows) *reinterpret_cast<u32x4_t*>(C + tiled_index(row0 + trow, col0 + c * 8, NPAD)) = v;
+        }
+        __builtin_amdgcn_s_waitcnt(lgkm0_imm());
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_s_waitcnt(lgkm0_imm());
-      __builtin_amdgcn_wave_barrier();
     }
     return;
   }
@@ -534,9 +594,11 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
   const int per_xcd = P >> 3;
   const int slot = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
 
-  for (int tile = slot; tile < total; tile += P) {
-    // problem and tile index inside it
-    const bool dense = tile >= n0;
+  const int wm = WMG == 2 ? wave >> 2 : 0;
+  // a tile's wave-uniform description from its index in the list
+  auto decode = [&](int tile, bool& dense, int& mrows, int64_t& row0, int& ncol0, int& nl, int& nkf,
+                    const uint16_t*& wb0, const uint16_t*& wb1, int& wbands) {
+    dense = tile >= n0;
     const GemmOperands& op = dense ? p1 : p0;
     int ei = 0, q, erows, pb, trows;
     if (dense) {
@@ -566,25 +628,55 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
     const int gm0 = g * kGroupM;
     const int gm = (MT - gm0) < kGroupM ? (MT - gm0) : kGroupM;
     const int mt = gm0 + qi % gm, nt = qi / gm;
-    const int64_t row0 = (int64_t)pb + (int64_t)mt * trows;  // multiple of 16
-    const int mrows = (erows - mt * trows) < trows ? (erows - mt * trows) : trows;
-    const int ncol0 = nt * BNO;
+    row0 = (int64_t)pb + (int64_t)mt * trows;  // multiple of 16
+    mrows = (erows - mt * trows) < trows ? (erows - mt * trows) : trows;
+    ncol0 = nt * BNO;
     const int wrows = (int)round_up(op.NOUT, kWeightRowAlign);  // packed weight rows per expert
-    const uint16_t* wb0 = op.B0 + (int64_t)ei * wrows * op.KP;
-    const uint16_t* wb1 = SWIGLU ? op.B1 + (int64_t)ei * wrows * op.KP : wb0;
-    const int64_t mband0 = row0 / kTileRows;
-    const int wbands = wrows / kTileRows;
-    const int npad = (int)round_up(op.NOUT, kTileCols);
-    const int nkf = op.KP / kTileCols;
-
+    wb0 = op.B0 + (int64_t)ei * wrows * op.KP;
+    wb1 = SWIGLU ? op.B1 + (int64_t)ei * wrows * op.KP : wb0;
+    wbands = wrows / kTileRows;
+    nkf = op.KP / kTileCols;
     // live row blocks of this wave (wave-uniform): block wm + WMG t is live if it starts below mrows
-    const int wm = WMG == 2 ? wave >> 2 : 0;
     const int nrb = (mrows + 15) / 16;
-    const int nl = nrb > wm ? (nrb - wm + WMG - 1) / WMG : 0;
-#define MOGE_TILE(NLV)                                                                                          \
-  tile_compute<SWIGLU, NLV, WMG>(op, lds, op.A, mband0, wb0, wb1, wbands, nkf, mrows, row0, ncol0, op.NOUT, npad, \
-                                 op.C)
-    switch (nl) {
+    nl = nrb > wm ? (nrb - wm + WMG - 1) / WMG : 0;
+  };
+
+  if (slot >= total) return;
+  bool c_dense;
+  int c_mrows, c_ncol0, c_nl, c_nkf, c_wbands;
+  int64_t c_row0;
+  const uint16_t *c_wb0, *c_wb1;
+  decode(slot, c_dense, c_mrows, c_row0, c_ncol0, c_nl, c_nkf, c_wb0, c_wb1, c_wbands);
+  int32_t tokc[5], tokn[5];
+  if constexpr (SWIGLU) token_rows<WMG>(c_dense ? p1 : p0, c_row0 / kTileRows, c_mrows, tokc);
+  bool pre = false;  // this tile's steps 0-2 were issued by the previous one
+  for (int tile = slot; tile < total; tile += P) {
+    const bool more = tile + P < total;
+    bool n_dense = false;
+    int n_mrows = 1, n_ncol0 = 0, n_nl = 0, n_nkf = 0, n_wbands = 1;
+    int64_t n_row0 = 0;
+    const uint16_t *n_wb0 = c_wb0, *n_wb1 = c_wb1;
+    if (more) decode(tile + P, n_dense, n_mrows, n_row0, n_ncol0, n_nl, n_nkf, n_wb0, n_wb1, n_wbands);
+    if constexpr (SWIGLU) {  // the next tile's gathered tokens, a whole tile ahead of their use
+      if (more) token_rows<WMG>(n_dense ? p1 : p0, n_row0 / kTileRows, n_mrows, tokn);
+      else {
+#pragma unroll
+        for (int j = 0; j < 5; ++j) tokn[j] = tokc[j];
+      }
+    } else {
+      token_rows<WMG>(c_dense ? p1 : p0, c_row0 / kTileRows, c_mrows, tokc);
+    }
+    // GEMM 1 chains; GEMM 2 (64-step tiles at 2048 columns) keeps its epilogue in two
+    // passes over the whole ring instead, which measured faster than five in one stage
+    const bool chain = SWIGLU && more && c_nkf >= 3 && n_nkf >= 3;
+    const GemmOperands& op = c_dense ? p1 : p0;
+    const GemmOperands& nop = n_dense ? p1 : p0;
+    const NextTile nx{n_wb0, n_wb1, n_row0 / kTileRows, n_wbands, n_nkf, n_ncol0, n_mrows, 0, 0};
+    const int npad = (int)round_up(op.NOUT, kTileCols);
+#define MOGE_TILE(NLV)                                                                                               \
+  tile_compute<SWIGLU, NLV, WMG>(op, lds, c_wb0, c_wb1, c_wbands, c_nkf, c_mrows, c_row0, c_ncol0, op.NOUT, npad, op.C, \
+                                 tokc, pre, chain, nop, nx, tokn)
+    switch (c_nl) {
       case 10: if constexpr (TileShape<WMG>::kBlocks >= 10) MOGE_TILE(10); break;
       case 9: if constexpr (TileShape<WMG>::kBlocks >= 9) MOGE_TILE(9); break;
       case 8: if constexpr (TileShape<WMG>::kBlocks >= 8) MOGE_TILE(8); break;
@@ -599,6 +691,13 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
     }
 #undef MOGE_TILE
     __syncthreads();  // LDS stages are reused by the next tile
+    pre = chain;
+    c_dense = n_dense; c_mrows = n_mrows; c_row0 = n_row0; c_ncol0 = n_ncol0; c_nl = n_nl; c_nkf = n_nkf;
+    c_wb0 = n_wb0; c_wb1 = n_wb1; c_wbands = n_wbands;
+    if constexpr (SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < 5; ++j) tokc[j] = tokn[j];
+    }
   }
 }
 
