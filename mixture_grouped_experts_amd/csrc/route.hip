@@ -234,6 +234,12 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   const int64_t t0 = (int64_t)(blockIdx.x / PARTS) * TM;
   const int e0 = (int)(blockIdx.x % PARTS) * NP;  // first expert of this workgroup
   const int nkf = d / 32;                        // full steps; a ragged tail follows the loop
+  // token tiles start at different steps (and wrap around), so the workgroups do not all
+  // read the same column range of their rows at once: each tile walks 64-byte pieces of
+  // rows 8 KiB apart, and in a plain streaming probe of that pattern the staggered start
+  // reads 9% faster (router -11% on 65536 tokens x 4096).  The order of the float32
+  // accumulation over k then depends on the tile; scores stay within the tolerance.
+  const int krot = nkf > 0 ? (int)(((t0 / TM) * 37) % nkf) : 0;
   const bool many = (NI % WV == 0) || wave < (NI % WV);  // this wave issues CH loads per step, else CL
 
   // load j of this wave moves stage rows 16 i .. 16 i + 15 with i = wave + WV j
@@ -258,7 +264,10 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
     const uint32_t st = lds0 + (uint32_t)((ks % S) * STAGE);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      if (wave + WV * j < NI) dma_16x64(src[j] + ks * 32, st + (uint32_t)(16 * (wave + WV * j) * 64));
+      if (wave + WV * j < NI) {
+        const int kk = ks + krot < nkf ? ks + krot : ks + krot - nkf;
+        dma_16x64(src[j] + kk * 32, st + (uint32_t)(16 * (wave + WV * j) * 64));
+      }
   };
   // at most `steps` steps of this wave's loads still in flight (and, with lgkm, no LDS reads)
   auto wait_steps = [&](int steps_left_ok, bool lgkm) {
