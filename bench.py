@@ -150,9 +150,9 @@ def cpu_baseline(w, seconds: float):
     import numpy as np
 
     import oracle
-    from tests import moge_harness as H
+    from synth.inputs import HostInputs, sample_tokens
 
-    hi = H.HostInputs(w)
+    hi = HostInputs(w)
     wr, bias = hi.w_router(), hi.bias()
     threads = oracle.threads()
 
@@ -172,14 +172,14 @@ def cpu_baseline(w, seconds: float):
         return time.perf_counter() - t0
 
     # size the sample to about `seconds` of oracle time: a small probe, then one correction
-    probe = H.sample_tokens(w.T, 8, seed=7)[:8]
+    probe = sample_tokens(w.T, 8, seed=7)[:8]
     dt = run(probe)
     n = int(max(2, min(w.T, 4096, seconds / max(dt / len(probe), 1e-9))))
-    tokens = H.sample_tokens(w.T, n, seed=11)[:n]
+    tokens = sample_tokens(w.T, n, seed=11)[:n]
     dt = run(tokens)
     if dt < 0.6 * seconds and n < min(w.T, 4096):
         n = int(min(w.T, 4096, n * seconds / max(dt, 1e-9)))
-        tokens = H.sample_tokens(w.T, n, seed=11)[:n]
+        tokens = sample_tokens(w.T, n, seed=11)[:n]
         dt = run(tokens)
     return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(tokens)} of {w.T} tokens (seeded sample), full layer per token in binary64; "
@@ -203,7 +203,7 @@ def main():
     import mixture_grouped_experts_amd as moge
     from mixture_grouped_experts_amd.layer import MoGELayer
     from synth import workloads as W
-    from tests import moge_harness as H
+    from synth.inputs import device_inputs
 
     w = {"ultra": W.ultra, "group0": W.group0, "decode": W.decode, "routing": W.routing, "tiny": W.tiny,
          "pro": W.pro}[
@@ -214,10 +214,10 @@ def main():
         w = W.variant(w, T=args.tokens, e_lo=w.e_lo, e_hi=w.e_hi,
                       name=re.sub(r"_T\d+_", f"_T{args.tokens}_", w.name))
     torch.cuda.set_device(0)
-    dv = H.device_inputs(w)
+    dv = device_inputs(w)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi,
-                      gather={"auto": None, "gather": True, "copy": False}[args.rows])
-    moge.set_gemm_tiles({"auto": moge.TILES_AUTO, "tall": moge.TILES_TALL, "wide": moge.TILES_WIDE}[args.tiles])
+                      gather={"auto": None, "gather": True, "copy": False}[args.rows],
+                      tiles={"auto": moge.TILES_AUTO, "tall": moge.TILES_TALL, "wide": moge.TILES_WIDE}[args.tiles])
     if w.F:
         # expert weights are packed once, at load time (outside the timed steps)
         (pg, pu, pd), ps = layer.pack_expert_weights(dv.w_gate, dv.w_up, dv.w_down, dv.shared)

@@ -19,8 +19,9 @@
  *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     never allocates or frees device memory and keeps no per-call state (its
- *     one process-wide setting is the tile-shape knob, moge_set_gemm_tiles).
+ *     never allocates or frees device memory and keeps no state between calls
+ *     (every setting, such as the expert GEMMs' tile shape, travels with the
+ *     call in moge_shape_t).
  *   - Tensors are contiguous.  x, logits, idx, gate, inv, the expert outputs
  *     and y are row-major; the operands of the expert GEMMs use the tiled
  *     layout described at moge_tiled_elems.  Weights come in the
@@ -58,7 +59,8 @@ typedef enum {
   MOGE_ERR_WORKSPACE = 4,  /* workspace missing or smaller than moge_workspace_size() */
   MOGE_ERR_DTYPE = 5,      /* unknown dtype */
   MOGE_ERR_HIP = 6,        /* a HIP launch failed (message has the HIP error) */
-  MOGE_ERR_CAPACITY = 7    /* rows_cap is below the row bound of the call */
+  MOGE_ERR_CAPACITY = 7,   /* rows_cap is below the row bound of the call */
+  MOGE_ERR_NONFINITE = 8   /* moge_check_finite found a NaN or an infinity */
 } moge_status_t;
 
 typedef enum { MOGE_BF16 = 0, MOGE_F32 = 1 } moge_dtype_t;
@@ -69,14 +71,27 @@ typedef enum { MOGE_BF16 = 0, MOGE_F32 = 1 } moge_dtype_t;
 typedef enum { MOGE_ROUTE_GROUPED = 0, MOGE_ROUTE_GLOBAL = 1 } moge_route_mode_t;
 
 /* Workspace stages for moge_workspace_size(). */
-typedef enum { MOGE_STAGE_DISPATCH = 1 } moge_stage_t;
+typedef enum { MOGE_STAGE_DISPATCH = 1, MOGE_STAGE_CHECK = 2 } moge_stage_t;
+
+/* Tile shape of the bf16 expert GEMMs (moge_shape_t.tiles).  Every output is
+ * bit-identical under all of them (same reduction order per output element).
+ *   MOGE_TILES_AUTO  the library's choice from the shape (the default, 0): its
+ *                    table of tile shapes keyed by the rows per expert, which
+ *                    plays the part of the grouped matmul's tiling cache and its
+ *                    switch of mode by workload ([P1] section 3, SwiftGMM);
+ *   MOGE_TILES_TALL  320 token rows x 256 weight rows;
+ *   MOGE_TILES_WIDE  96 token rows x 512 weight rows (few rows per expert). */
+#define MOGE_TILES_AUTO 0
+#define MOGE_TILES_TALL 1
+#define MOGE_TILES_WIDE 2
 
 /*
  * Layer shape.  Rules checked by moge_validate():
  *   T >= 1 tokens; d >= 8 hidden, d % 8 == 0; 1 <= M <= N experts, N % M == 0;
- *   1 <= k_per_group (K') <= N/M; K = M*K' slots per token;
+ *   1 <= k_per_group (K') <= N/M; K = M*K' slots per token (so K <= N);
  *   F expert width: F == 0 (routing only) or F >= 8 with F % 8 == 0;
- *   T*K < 2^31;  N <= 256 (both dtypes);  dtype in moge_dtype_t.
+ *   T*K < 2^31;  N <= 256 (both dtypes);  dtype in moge_dtype_t;
+ *   tiles: MOGE_TILES_AUTO, _TALL or _WIDE (a zero-initialised struct: AUTO).
  * Groups are contiguous blocks of expert ids: group(e) = e / (N/M).
  */
 typedef struct {
@@ -87,6 +102,7 @@ typedef struct {
   int32_t k_per_group;
   int32_t F;
   int32_t dtype;
+  int32_t tiles;
 } moge_shape_t;
 
 /* Host-only shape check (no device call; usable without a GPU). */
@@ -161,8 +177,12 @@ moge_status_t moge_round_bf16(const float* x, uint16_t* y, int64_t n, hipStream_
  *   gate     [T][K] f32 out: the chosen experts' probabilities under the softmax
  *            over all N scores (not renormalised over the chosen experts).
  * Slot order: GROUPED -> slot = g*K' + rank inside group g; GLOBAL -> slot = rank.
- * rank orders experts by score, higher first, equal scores -> lower expert id.
- * Scores must be finite.
+ * rank orders experts by score, higher first, equal scores -> lower expert id
+ * (-0 and +0 are equal).
+ * Scores are meant to be finite (moge_check_finite tests them).  A NaN score
+ * ranks as -inf (below every finite score; ties by the lower id as above), so
+ * the choice keeps exactly K' distinct experts of every group whatever the
+ * scores; a token with a NaN or infinite score may get NaN gates.
  */
 moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, const void* x, const void* w_router,
                          const float* bias, float* logits, int32_t* idx, float* gate, hipStream_t stream);
@@ -200,7 +220,11 @@ moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32
 
 /*
  * moge_grouped_ffn -- the SwiGLU expert applied to every expert's row segment
- * (a grouped GEMM pair).
+ * (a grouped GEMM pair).  [P1] section 1: each token's rows go to the experts it
+ * chose, whose groups sit on separate devices; section 3: the grouped matmul
+ * (GroupMatmul, SwiftGMM) that multiplies every expert's rows by that expert's
+ * weights is the dominant kernel of inference.  The expert form itself (SwiGLU,
+ * no biases) is not on the pages; it is the form stated at the top of this file.
  *   x_perm   tiled, rows_cap rows x d columns: local rows P(e) .. P(e)+counts[e]-1
  *            belong to expert e (counts[e] = offsets[e+1] - offsets[e]).
  *   offsets  [N+1] int32 device (from moge_dispatch).
@@ -298,24 +322,10 @@ moge_status_t moge_expert_down_combine(const moge_shape_t* shape, const void* h,
                                        const int32_t* perm, const float* gate, float* y, hipStream_t stream);
 
 /*
- * moge_set_gemm_tiles -- the tile shape of the bf16 expert GEMMs for the calls that
- * follow, process-wide (a tuning and testing knob; the default needs no call).
- *   MOGE_TILES_AUTO  320 x 256 tiles, or 96 x 512 when the routed experts average
- *                    at most 64 rows (T * M * k_per_group <= 64 * N): few rows per
- *                    expert (decode), where the wide tiles keep twice the weight
- *                    bytes in flight per CU -- the grouped matmul's switch to a
- *                    matrix-vector-like mode by workload ([P1] section 3, SwiftGMM).
- *   MOGE_TILES_TALL  always 320 x 256;  MOGE_TILES_WIDE  always 96 x 512.
- * Every output is bit-identical under all three (same reduction order).
- * Errors: MOGE_ERR_ARG for any other value.
- */
-#define MOGE_TILES_AUTO 0
-#define MOGE_TILES_TALL 1
-#define MOGE_TILES_WIDE 2
-moge_status_t moge_set_gemm_tiles(int32_t tiles);
-
-/*
  * moge_combine -- gate-weighted sum of the expert outputs back in token order.
+ * [P1] section 1: the weights are the chosen experts' probabilities under the
+ * softmax over all N experts, taken before the per-group choice, so they are not
+ * renormalised; [P4]: the always-on shared expert is added to every token.
  *   y[t] = sum over slots s (in slot order) with inv[t][s] >= 0 of
  *          gate[t][s] * o[inv[t][s]]   (+ shared_out[t] when not NULL), in float32.
  *   o [rows_cap][d] (dtype), inv/gate [T][K], shared_out [T][d] (dtype) or NULL,
@@ -347,6 +357,24 @@ moge_status_t moge_imbalance(const moge_shape_t* shape, const int32_t* counts, i
  */
 moge_status_t moge_imbalance_batches(const moge_shape_t* shape, const int32_t* idx, int64_t tokens_per_batch,
                                      int32_t* group_load, int32_t* is_raw, hipStream_t stream);
+
+/*
+ * moge_check_finite -- a checking call: tests n values for NaN and infinities
+ * and WAITS for the result (it synchronises `stream`), for callers that want
+ * the router scores (moge_route's logits) or any other input checked before
+ * trusting a result.  The pages define no outcome for non-finite scores, so the
+ * layer's own calls do not test for them.
+ *   dtype  MOGE_F32 (a: float32) or MOGE_BF16 (a: bf16 bit patterns).
+ *   a      [n] device;  n >= 0.
+ *   ws     device workspace of moge_workspace_size(any valid shape,
+ *          MOGE_STAGE_CHECK) bytes.
+ * Returns MOGE_OK if every value is finite, MOGE_ERR_NONFINITE otherwise (the
+ * message gives the count and the first index), MOGE_ERR_HIP if the stream
+ * fails, MOGE_ERR_DTYPE / MOGE_ERR_SHAPE / MOGE_ERR_NULL / MOGE_ERR_WORKSPACE
+ * for bad arguments.  Not for use while `stream` is being captured into a graph.
+ */
+moge_status_t moge_check_finite(int32_t dtype, const void* a, int64_t n, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /* Library version string and the calling thread's last error message. */
 const char* moge_version(void);

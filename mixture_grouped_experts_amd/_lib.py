@@ -23,12 +23,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK = 0
 STATUS = {0: "MOGE_OK", 1: "MOGE_ERR_ARG", 2: "MOGE_ERR_SHAPE", 3: "MOGE_ERR_NULL", 4: "MOGE_ERR_WORKSPACE",
-          5: "MOGE_ERR_DTYPE", 6: "MOGE_ERR_HIP", 7: "MOGE_ERR_CAPACITY"}
+          5: "MOGE_ERR_DTYPE", 6: "MOGE_ERR_HIP", 7: "MOGE_ERR_CAPACITY", 8: "MOGE_ERR_NONFINITE"}
 BF16 = 0
 F32 = 1
 ROUTE_GROUPED = 0
 ROUTE_GLOBAL = 1
 STAGE_DISPATCH = 1
+STAGE_CHECK = 2
 TILES_AUTO = 0
 TILES_TALL = 1
 TILES_WIDE = 2
@@ -37,13 +38,16 @@ EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_
            "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_grouped_ffn",
            "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
            "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_expert_down_combine",
-           "moge_set_gemm_tiles", "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_version",
+           "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_check_finite", "moge_version",
            "moge_last_error", "moge_round_bf16")
 
 
 class Shape(ctypes.Structure):
+    """moge_shape_t; ``tiles`` (default TILES_AUTO) picks the expert GEMMs' tile shape for the calls
+    made with this shape."""
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("N", ctypes.c_int32), ("M", ctypes.c_int32),
-                ("k_per_group", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("k_per_group", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("tiles", ctypes.c_int32)]
 
     @property
     def K(self) -> int:
@@ -51,7 +55,7 @@ class Shape(ctypes.Structure):
 
     def __repr__(self):
         return (f"Shape(T={self.T}, d={self.d}, N={self.N}, M={self.M}, k_per_group={self.k_per_group}, "
-                f"F={self.F}, dtype={'bf16' if self.dtype == BF16 else 'f32'})")
+                f"F={self.F}, dtype={'bf16' if self.dtype == BF16 else 'f32'}, tiles={self.tiles})")
 
 
 class MogeError(RuntimeError):
@@ -98,8 +102,8 @@ _lib.moge_expert_gate_up_gather.argtypes = [_SP, _P, _P, _P, _I32, _I32, _I64, _
 _lib.moge_expert_gate_up_gather.restype = ctypes.c_int
 _lib.moge_expert_down_combine.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P]
 _lib.moge_expert_down_combine.restype = ctypes.c_int
-_lib.moge_set_gemm_tiles.argtypes = [_I32]
-_lib.moge_set_gemm_tiles.restype = ctypes.c_int
+_lib.moge_check_finite.argtypes = [_I32, _P, _I64, _P, ctypes.c_size_t, _P]
+_lib.moge_check_finite.restype = ctypes.c_int
 _lib.moge_combine.argtypes = [_SP, _P, _P, _P, _I64, _P, _P, _P]
 _lib.moge_combine.restype = ctypes.c_int
 _lib.moge_imbalance.argtypes = [_SP, _P, _P, _P, _P, _P]
@@ -293,9 +297,19 @@ def expert_gate_up_gather(shape: Shape, x, perm, offsets, e_lo: int, e_hi: int, 
     _check("moge_expert_gate_up_gather", st)
 
 
-def set_gemm_tiles(tiles: int) -> None:
-    """Process-wide tile shape of the bf16 expert GEMMs: TILES_AUTO (default), TILES_TALL or TILES_WIDE."""
-    _check("moge_set_gemm_tiles", _lib.moge_set_gemm_tiles(tiles))
+def check_finite(a, ws, stream=None) -> None:
+    """Raises MogeError (MOGE_ERR_NONFINITE) if the float32 or bf16 tensor `a` holds a NaN or an
+    infinity.  Synchronises `stream`.  ws: workspace_size(shape, STAGE_CHECK) bytes."""
+    if a.dtype == torch.float32:
+        dt = F32
+    elif a.dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise TypeError(f"a must be float32 or bfloat16, got {a.dtype}")
+    n = a.numel()
+    st = _lib.moge_check_finite(dt, _ptr(a, "a", None, n), n, _ptr(ws, "ws", None, None),
+                                ws.numel() * ws.element_size(), _stream(stream))
+    _check("moge_check_finite", st)
 
 
 def expert_down_combine(shape: Shape, h, offsets, e_lo: int, e_hi: int, rows_cap: int, w_down, perm, gate, y,

@@ -329,8 +329,7 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   if (x && !inv) return fail(MOGE_ERR_NULL, "row copies need inv and perm");
   if (x_tiled && !x) return fail(MOGE_ERR_NULL, "x_tiled needs x");
   if (e_lo < 0 || e_hi > s.N || e_lo >= e_hi) return fail(MOGE_ERR_ARG, "need 0 <= e_lo < e_hi <= N");
-  const int K = s.M * s.k_per_group;
-  if (K > 64) return fail(MOGE_ERR_SHAPE, "dispatch supports K = M*k_per_group <= 64");
+  const int K = s.M * s.k_per_group;  // <= N <= 256 (moge_validate)
   const int64_t bound = rows_bound(s, mode, e_lo, e_hi);
   if (inv && rows_cap < bound)
     return fail(MOGE_ERR_CAPACITY, "rows_cap is below moge_rows_bound() for this expert range");
@@ -338,8 +337,14 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   if (!ws || ws_bytes < need) return fail(MOGE_ERR_WORKSPACE, "dispatch workspace missing or too small");
 
   if ((int64_t)s.T * K <= kSmallSlots) {  // one workgroup does counts, offsets and the permutation
+    // 8 N + 4 (T (K + 1) + 3 N + 1) bytes: with T K <= 8192 and N <= 256 at most
+    // 8 * 256 + 4 * (2 * 8192 + 769) = 70.7 KiB (T = 8192, K = 1), above the 64 KiB default
     const size_t slds = sizeof(uint64_t) * (size_t)s.N +
-                        sizeof(int) * ((size_t)s.T * (K + 1) + (size_t)s.N * 3 + 1);  // <= 51 KiB
+                        sizeof(int) * ((size_t)s.T * (K + 1) + (size_t)s.N * 3 + 1);
+    if (slds > 64 * 1024) {
+      st = raise_dynamic_lds(reinterpret_cast<const void*>(dispatch_small_kernel), slds, "dispatch_small_kernel");
+      if (st != MOGE_OK) return st;
+    }
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallThreads), slds, stream, (int64_t)s.T, K, s.N, idx,
                        e_lo, e_hi, rows_cap, counts, offsets, inv, perm);
     st = check_launch("dispatch_small_kernel");

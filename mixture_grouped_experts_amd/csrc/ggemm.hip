@@ -47,8 +47,6 @@
 // shapes only).
 #include <math.h>
 
-#include <atomic>
-
 #include "moge_internal.hpp"
 
 namespace moge {
@@ -653,9 +651,11 @@ __global__ __launch_bounds__(kThreads) void ggemm_bf16_kernel(GemmOperands p0, c
     // GEMM 1's first reduction step is staggered by expert: the workgroups then do not all
     // stream the same column range of their weight bands at once (gate/up -2 to -3%), while
     // all tiles of one expert still start together and share its token rows in L2.  The
-    // order of the float32 sums then depends on the expert only, the same for both tile
-    // shapes, whose outputs stay bit-identical.  (GEMM 2 measured 0-2% slower with it.)
-    krot = SWIGLU ? (int)(((int64_t)(dense ? E : ei) * 37) % nkf) : 0;
+    // offset is keyed on the absolute expert id (and 0 for the dense shared-expert problem),
+    // so the order of an output's float32 sums depends on that expert alone: the same under
+    // both tile shapes, for any expert range of the call, and for the shared expert fused
+    // into the routed launch or run on its own.  (GEMM 2 measured 0-2% slower with it.)
+    krot = SWIGLU && !dense ? (int)(((int64_t)(e_lo + ei) * 37) % nkf) : 0;
     // live row blocks of this wave (wave-uniform): block wm + WMG t is live if it starts below mrows
     const int nrb = (mrows + 15) / 16;
     nl = nrb > wm ? (nrb - wm + WMG - 1) / WMG : 0;
@@ -814,14 +814,11 @@ static moge_status_t launch_ggemm_shape(const GemmOperands& p0, const int32_t* o
   return check_launch(SWIGLU ? "ggemm_bf16_kernel<gate_up>" : "ggemm_bf16_kernel<down>");
 }
 
-static std::atomic<int> g_tiles{MOGE_TILES_AUTO};
-
 // The tile shape: the 96 x 512 tiles when the routed experts average at most 64 rows
-// (T K / N, exact per group under MoGE routing), else 320 x 256; or as set by
-// moge_set_gemm_tiles.
+// (T K / N, exact per group under MoGE routing), else 320 x 256; or as the call's
+// shape.tiles asks.
 static bool wide_tiles(const moge_shape_t& s) {
-  const int t = g_tiles.load(std::memory_order_relaxed);
-  if (t != MOGE_TILES_AUTO) return t == MOGE_TILES_WIDE;
+  if (s.tiles != MOGE_TILES_AUTO) return s.tiles == MOGE_TILES_WIDE;
   return (int64_t)s.T * s.M * s.k_per_group <= (int64_t)64 * s.N;
 }
 
@@ -998,11 +995,4 @@ extern "C" moge_status_t moge_expert_down_combine(const moge_shape_t* shape, con
   const GemmOperands none{};
   st = launch_ggemm<false>(s, p, offsets, e_lo, e_hi - e_lo, rows_cap, none, 0, stream);
   return st == MOGE_OK ? ok() : st;
-}
-
-extern "C" moge_status_t moge_set_gemm_tiles(int32_t tiles) {
-  if (tiles != MOGE_TILES_AUTO && tiles != MOGE_TILES_TALL && tiles != MOGE_TILES_WIDE)
-    return fail(MOGE_ERR_ARG, "tiles must be MOGE_TILES_AUTO, MOGE_TILES_TALL or MOGE_TILES_WIDE");
-  g_tiles.store(tiles, std::memory_order_relaxed);
-  return ok();
 }

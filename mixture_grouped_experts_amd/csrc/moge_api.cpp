@@ -43,6 +43,8 @@ moge_status_t validate_shape(const moge_shape_t* s) {
     return fail(MOGE_ERR_SHAPE, "F must be 0 (routing only) or a positive multiple of 8");
   const int64_t K = (int64_t)s->M * s->k_per_group;
   if ((int64_t)s->T * K >= (int64_t(1) << 31)) return fail(MOGE_ERR_SHAPE, "T*K must be < 2^31");
+  if (s->tiles != MOGE_TILES_AUTO && s->tiles != MOGE_TILES_TALL && s->tiles != MOGE_TILES_WIDE)
+    return fail(MOGE_ERR_ARG, "tiles must be MOGE_TILES_AUTO, MOGE_TILES_TALL or MOGE_TILES_WIDE");
   return MOGE_OK;
 }
 
@@ -109,6 +111,7 @@ extern "C" size_t moge_workspace_size(const moge_shape_t* shape, int32_t stage) 
     const int64_t nb = dispatch_blocks(shape->T);
     return (size_t)(2 * (int64_t)shape->N * nb) * sizeof(int32_t);
   }
+  if (stage == MOGE_STAGE_CHECK) return check_workspace_bytes();
   return (size_t)-1;
 }
 

@@ -36,6 +36,10 @@ __host__ __device__ __forceinline__ int64_t tiled_index(int64_t r, int64_t c, in
   return ((r >> 4) * (cp >> 5) + (c >> 5)) * kTileElems + (r & 15) * kTileCols + (c & 31);
 }
 
+// moge_check_finite: partial results per workgroup (count, first index) in its workspace.
+constexpr int kCheckBlocks = 1024;
+inline size_t check_workspace_bytes() { return (size_t)kCheckBlocks * 2 * sizeof(int64_t) + 2 * sizeof(int64_t); }
+
 // Dispatch geometry (shared by moge_workspace_size and the dispatch kernels).
 constexpr int kDispatchTokens = 64;   // tokens per dispatch workgroup (one per lane)
 inline int64_t dispatch_blocks(int64_t T) { return (T + kDispatchTokens - 1) / kDispatchTokens; }

@@ -32,6 +32,12 @@
 
 namespace moge {
 
+// The order the choice sorts by: the score itself, except that a NaN ranks as -inf
+// (ties, -inf ones included, go to the lower expert id).  The pages define the choice
+// on finite scores only; with this key every group still yields exactly k distinct
+// experts of its own, whatever the scores (moge_check_finite reports non-finite ones).
+__device__ __forceinline__ float order_key(float v) { return v == v ? v : -INFINITY; }
+
 // Softmax over the token's N scores (LDS row `l`) and the per-group choice.
 // One full wave per token; lane owns experts lane, lane+64, lane+128, lane+192.
 // Narrow groups (G <= 64): rank(e) = #{e' in group(e) : l[e'] > l[e] or
@@ -44,12 +50,13 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int N,
   const int lane = threadIdx.x & 63;
   const int G = N / n_groups;
   const int K = n_groups * k;
-  float v[4], ex[4];
+  float v[4], ex[4], kv[4];
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
     v[j] = e < N ? l[e] : -INFINITY;
+    kv[j] = order_key(v[j]);
     m = fmaxf(m, v[j]);
   }
   m = wave_max(m);
@@ -70,8 +77,8 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int N,
         const int base = g * G;
         int rank = 0;
         for (int e2 = base; e2 < base + G; ++e2) {
-          const float w = l[e2];
-          rank += (w > v[j]) || (w == v[j] && e2 < e);
+          const float w = order_key(l[e2]);
+          rank += (w > kv[j]) || (w == kv[j] && e2 < e);
         }
         if (rank < k) {
           idx[t * K + g * k + rank] = e;
@@ -89,8 +96,8 @@ __device__ __forceinline__ void select_token(const float* __restrict__ l, int N,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = lane + 64 * j;
-        if (e < N && e / G == g && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
-          bv = v[j];
+        if (e < N && e / G == g && !((taken >> j) & 1u) && (kv[j] > bv || (kv[j] == bv && e < bi))) {
+          bv = kv[j];
           bi = e;
         }
       }
@@ -149,7 +156,7 @@ __device__ __forceinline__ void select_tile(const float* __restrict__ lt, int ld
         float bv = -INFINITY;
         int bi = -1;
         for (int i = 0; i < n; ++i) {
-          const float x = v[i];
+          const float x = order_key(v[i]);
           const bool after = x < pv || (x == pv && i > pi);  // not yet taken
           if (after && (bi < 0 || x > bv)) {
             bv = x;
@@ -206,9 +213,10 @@ __device__ __forceinline__ void select_tile_g(const float* __restrict__ lt, int 
         int bi = -1;
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-          const bool after = s[i] < pv || (s[i] == pv && i > pi);  // not yet taken
-          if (after && (bi < 0 || s[i] > bv)) {
-            bv = s[i];
+          const float x = order_key(s[i]);
+          const bool after = x < pv || (x == pv && i > pi);  // not yet taken
+          if (after && (bi < 0 || x > bv)) {
+            bv = x;
             bi = i;
           }
         }
@@ -649,16 +657,18 @@ __global__ __launch_bounds__(256) void route_select_lane_kernel(int64_t T, int N
   const int G = N / n_groups, K = n_groups * k;
   float bv[KMAX];
   int bi[KMAX];
+  // Entries start as empty places (bi = -1) that any expert fills; experts arrive in
+  // increasing id order, so a later equal key never displaces an earlier expert.
   auto insert = [&](float v, int e) {
     // position of v: below every entry >= v; entries below it move down one place
 #pragma unroll
     for (int j = KMAX - 1; j > 0; --j) {
-      const bool up = v > bv[j - 1];  // v lands above j - 1: entry j - 1 moves to j
-      const bool here = v > bv[j];
+      const bool up = v > bv[j - 1] || bi[j - 1] < 0;  // v lands above j - 1: entry j - 1 moves to j
+      const bool here = v > bv[j] || bi[j] < 0;
       bv[j] = up ? bv[j - 1] : (here ? v : bv[j]);
       bi[j] = up ? bi[j - 1] : (here ? e : bi[j]);
     }
-    if (v > bv[0]) {
+    if (v > bv[0] || bi[0] < 0) {
       bv[0] = v;
       bi[0] = e;
     }
@@ -673,11 +683,11 @@ __global__ __launch_bounds__(256) void route_select_lane_kernel(int64_t T, int N
     for (e8 = g * G; e8 + 8 <= ge; e8 += 8) {
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = row[e8 + j];
+      for (int j = 0; j < 8; ++j) v[j] = order_key(row[e8 + j]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) insert(v[j], e8 + j);
     }
-    for (; e8 < ge; ++e8) insert(row[e8], e8);
+    for (; e8 < ge; ++e8) insert(order_key(row[e8]), e8);
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       if (r < k) {

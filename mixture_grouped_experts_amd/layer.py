@@ -39,10 +39,10 @@ from . import _lib as L
 class MoGELayer:
     def __init__(self, T: int, d: int, N: int, M: int, Kp: int, F: int, F_shared: int = 0, dtype: str = "bf16",
                  e_lo: int = 0, e_hi: int | None = None, device="cuda", comparator: bool = True,
-                 gather: bool | None = None):
+                 gather: bool | None = None, tiles: int = L.TILES_AUTO):
         self.dtype_code = L.BF16 if dtype == "bf16" else L.F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.shape = L.Shape(T, d, N, M, Kp, F, self.dtype_code)
+        self.shape = L.Shape(T, d, N, M, Kp, F, self.dtype_code, tiles)
         st = L.validate(self.shape)
         if st != 0:
             raise L.MogeError("moge_validate", st, L.last_error())
@@ -99,7 +99,7 @@ class MoGELayer:
             self.o = None if self.fuse_combine else torch.empty(R, d, dtype=self.tdtype, device=dev)
             self.y = torch.empty(T, d, **f32)
         if F_shared:
-            self.sshape = L.Shape(T, d, 1, 1, 1, F_shared, self.dtype_code)
+            self.sshape = L.Shape(T, d, 1, 1, 1, F_shared, self.dtype_code, tiles)
             self.soffsets = torch.tensor([0, T], **i32)
             self.x_tiled = None if self.gather else torch.empty(L.tiled_elems(T, d), dtype=self.tdtype, device=dev)
             self.sh = torch.empty(L.tiled_elems(T, F_shared), dtype=self.tdtype, device=dev)
@@ -213,6 +213,14 @@ class MoGELayer:
                 comparator(main)
             mk("global_comparator")
         return None if self.routing_only else self.y
+
+    def check_scores(self, stream=None) -> None:
+        """Raises MogeError (MOGE_ERR_NONFINITE) if the router scores of the last forward hold a NaN
+        or an infinity.  Waits for the stream."""
+        if not hasattr(self, "check_ws"):
+            self.check_ws = torch.empty(L.workspace_size(self.shape, L.STAGE_CHECK), dtype=torch.uint8,
+                                        device=self.logits.device)
+        L.check_finite(self.logits, self.check_ws, stream)
 
     def capture(self, x, w_router, bias, w_gate=None, w_up=None, w_down=None, shared=None, warmup: int = 1):
         """Records one ``forward`` on these tensors into a HIP graph and returns it; ``g.replay()``

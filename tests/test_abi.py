@@ -31,14 +31,16 @@ def test_version():
     assert "gfx950" in moge.version()
 
 
-def S(T=64, d=128, N=8, M=4, Kp=1, F=64, dt=moge.BF16):
-    return moge.Shape(T, d, N, M, Kp, F, dt)
+def S(T=64, d=128, N=8, M=4, Kp=1, F=64, dt=moge.BF16, tiles=moge.TILES_AUTO):
+    return moge.Shape(T, d, N, M, Kp, F, dt, tiles)
 
 
 @pytest.mark.parametrize("shape,code", [
     (S(), 0), (S(dt=moge.F32), 0), (S(F=0), 0), (S(M=1, Kp=8), 0), (S(N=256, M=8, Kp=32), 0),
     (S(T=0), 2), (S(d=100), 2), (S(d=0), 2), (S(M=3), 2), (S(M=16), 2), (S(Kp=0), 2), (S(Kp=3), 2),
     (S(F=12), 2), (S(F=-8), 2), (S(N=512, M=8), 2), (S(dt=7), 5), (S(T=2 ** 28, M=8, N=64, Kp=1), 2),
+    (S(tiles=moge.TILES_TALL), 0), (S(tiles=moge.TILES_WIDE), 0), (S(tiles=3), 1), (S(tiles=-1), 1),
+    (S(N=256, M=8, Kp=32), 0), (S(N=256, M=1, Kp=256), 0),                  # K = N: every expert chosen
 ])
 def test_validate(shape, code):
     assert moge.validate(shape) == code
@@ -59,6 +61,8 @@ def test_rows_bound_and_workspace():
     assert moge.workspace_size(S(T=65536, N=64)) == 2 * 64 * 1024 * 4   # blocks of 64 tokens
     assert moge.workspace_size(S(T=1, N=8)) == 2 * 8 * 1 * 4
     assert moge.workspace_size(S(T=0)) == 2 ** 64 - 1
+    assert moge.workspace_size(S(), moge.STAGE_CHECK) == 1024 * 16 + 16
+    assert moge.workspace_size(S(), 9) == 2 ** 64 - 1
 
 
 def test_tiled_sizes():
@@ -128,10 +132,16 @@ def test_null_and_argument_errors_before_any_launch():
     assert lib.moge_dispatch(sp, 0, fake, fake, 0, 8, cap, fake, fake, None, None, fake, None, fake, ws, None) == 3
     # x_tiled without x
     assert lib.moge_dispatch(sp, 0, fake, None, 0, 8, cap, fake, fake, fake, fake, None, fake, fake, ws, None) == 3
-    big = S(N=128, M=2, Kp=64)                                                            # K = 128 > 64
-    assert lib.moge_dispatch(ctypes.byref(big), 0, fake, fake, 0, 128, 64 * 128 + 15 * 128, fake, fake, fake,
-                             fake, fake, None, fake, 1 << 20, None) == 2
+    # every shape moge_validate accepts (K = M K' <= N <= 256) passes dispatch's own checks: here
+    # K = 256 with an undersized rows_cap is refused for the capacity, not for K
+    big = S(N=256, M=8, Kp=32)
+    assert moge.validate(big) == 0
+    assert lib.moge_dispatch(ctypes.byref(big), 0, fake, fake, 0, 256, 64 * 256 + 15 * 256 - 1, fake, fake, fake,
+                             fake, fake, None, fake, 1 << 20, None) == 7
     lib.moge_grouped_ffn.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64] + [P] * 6
+    # a bad tile shape is refused by every call that takes the shape
+    bad_tiles = ctypes.byref(S(tiles=9))
+    assert lib.moge_grouped_ffn(bad_tiles, fake, fake, 0, 8, 64, fake, fake, fake, fake, fake, None) == 1
     assert lib.moge_grouped_ffn(ctypes.byref(S(F=0)), fake, fake, 0, 8, 64, fake, fake, fake, fake, fake, None) == 2
     assert lib.moge_grouped_ffn(sp, fake, fake, 0, 8, 64, fake, None, fake, fake, fake, None) == 3
     assert lib.moge_grouped_ffn(sp, fake, fake, -1, 8, 64, fake, fake, fake, fake, fake, None) == 1
@@ -163,9 +173,6 @@ def test_null_and_argument_errors_before_any_launch():
     assert dc(grp, fake, fake, 2, 4, 64, fake, fake, None, fake, None) == 3              # no gate
     assert dc(grp, fake, fake, 2, 4, 64, fake, None, fake, fake, None) == 3              # no perm
     assert dc(grp, fake, fake, 2, 4, 0, fake, fake, fake, fake, None) == 7               # rows_cap
-    lib.moge_set_gemm_tiles.argtypes = [ctypes.c_int32]
-    assert lib.moge_set_gemm_tiles(3) == 1 and lib.moge_set_gemm_tiles(-1) == 1
-    assert lib.moge_set_gemm_tiles(0) == 0                                               # back to the default
     lib.moge_combine.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P]
     assert lib.moge_combine(sp, fake, fake, None, 64, None, fake, None) == 3
     assert lib.moge_combine(sp, fake, fake, fake, 0, None, fake, None) == 7
@@ -176,3 +183,19 @@ def test_null_and_argument_errors_before_any_launch():
     lib.moge_imbalance.argtypes = [P] * 6
     assert lib.moge_imbalance(sp, fake, fake, None, fake, None) == 3
     assert lib.moge_imbalance(ctypes.byref(S(M=3)), fake, fake, fake, fake, None) == 2
+
+
+def test_check_finite_argument_errors():
+    lib = ctypes.CDLL(moge.LIB_PATH)
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: every case returns before a launch
+    lib.moge_check_finite.argtypes = [ctypes.c_int32, P, ctypes.c_int64, P, ctypes.c_size_t, P]
+    ws = moge.workspace_size(S(), moge.STAGE_CHECK)
+    assert lib.moge_check_finite(7, fake, 4, fake, ws, None) == 5           # MOGE_ERR_DTYPE
+    assert lib.moge_check_finite(moge.F32, fake, -1, fake, ws, None) == 2   # MOGE_ERR_SHAPE
+    assert lib.moge_check_finite(moge.F32, None, 4, fake, ws, None) == 3    # MOGE_ERR_NULL
+    assert lib.moge_check_finite(moge.BF16, fake, 4, fake, ws - 1, None) == 4  # MOGE_ERR_WORKSPACE
+    assert lib.moge_check_finite(moge.BF16, fake, 4, None, ws, None) == 4
+    assert lib.moge_check_finite(moge.F32, None, 0, None, 0, None) == 0     # nothing to check
+    from mixture_grouped_experts_amd import _lib
+    assert _lib.STATUS[8] == "MOGE_ERR_NONFINITE"

@@ -105,3 +105,16 @@ def test_dispatch_rejects_small_capacity(gpu):
                       torch.zeros(100, 4, **dev), torch.zeros(cap, **dev),
                       torch.zeros(moge.tiled_elems(cap, 64), dtype=torch.bfloat16, device="cuda"),
                       torch.empty(moge.workspace_size(s), dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("T,d,N,M,Kp", [
+    (8192, 64, 256, 1, 1),    # M = 1 (MoGE is the global top-K), one workgroup: 70.6 KiB of LDS
+    (8192, 64, 1, 1, 1),      # one expert takes every token
+    (32, 64, 256, 8, 32),     # K' = N/M: every expert chosen, K = 256, one workgroup
+    (40, 64, 256, 8, 32),     # K = 256 over several 64-token blocks
+    (20, 64, 256, 1, 256),    # one group of all 256 experts, every one chosen
+])
+def test_dispatch_edge_slot_counts(gpu, T, d, N, M, Kp):
+    idx = _idx(T, N, M, Kp, seed=T * 7 + Kp)
+    x, counts, offsets, inv, perm, xp = _run(T, d, N, M, Kp, idx, 0, N)
+    _check_rows(idx, x, counts, offsets, inv, perm, xp, 0, N)

@@ -131,9 +131,14 @@ def test_grouped_ffn_expert_range_and_shared_form(gpu):
     assert ok, (err, bound)
 
 
-def test_routed_and_shared_in_one_launch_bitexact(gpu):
+@pytest.mark.parametrize("w", [
+    W.variant(MID, name="fused_shared_d256", F_shared=136, std_shared_down=0.02, T=333),
+    # d = 520: 17 reduction steps, so the gate/up GEMM's per-expert starting step is not 0 for the
+    # shared expert's position in the list either (16 * 37 mod 17 = 14)
+    W.variant(MID, name="fused_shared_d520", d=520, F_shared=136, std_shared_down=0.02, T=333),
+], ids=lambda w: w.name)
+def test_routed_and_shared_in_one_launch_bitexact(gpu, w):
     # the fused launches compute every element exactly as the separate calls do
-    w = W.variant(MID, F_shared=136, std_shared_down=0.02, T=333)
     dv = H.device_inputs(w)
     hi = H.HostInputs(w)
     idx, _, _ = oracle.route(H.oracle_logits_all(hi), w.M, w.Kp, "grouped")
@@ -168,6 +173,28 @@ def test_routed_and_shared_in_one_launch_bitexact(gpu):
     assert torch.equal(H.untile_rows(h1, cap, w.F)[live], H.untile_rows(h2, cap, w.F)[live])
     assert torch.equal(o1[live], o2[live])
     assert torch.equal(hs1, hs2) and torch.equal(so1, so2)
+    # an expert's outputs do not depend on the expert range of the call: experts [5, 13) alone
+    lo, hi_ = 5, 13
+    cap3 = moge.rows_bound(s, moge.ROUTE_GROUPED, lo, hi_)
+    c3, of3 = torch.empty(w.N, **i32), torch.empty(w.N + 1, **i32)
+    inv3, perm3, xp3 = torch.empty(w.T, w.K, **i32), torch.empty(cap3, **i32), torch.empty(moge.tiled_elems(cap3, w.d), **bf)
+    moge.dispatch(s, moge.ROUTE_GROUPED, torch.from_numpy(idx).cuda(), dv.x, lo, hi_, cap3, c3, of3, inv3, perm3,
+                  xp3, ws)
+    h3 = torch.zeros(moge.tiled_elems(cap3, w.F), **bf)
+    o3 = torch.zeros(cap3, w.d, **bf)
+    sl = slice(lo * moge.packed_weight_elems(w.F, w.d), hi_ * moge.packed_weight_elems(w.F, w.d))
+    sld = slice(lo * moge.packed_weight_elems(w.d, w.F), hi_ * moge.packed_weight_elems(w.d, w.F))
+    moge.grouped_ffn(s, xp3, of3, lo, hi_, cap3, pg[sl], pu[sl], pd[sld], h3, o3)
+    torch.cuda.synchronize()
+    cn = counts.cpu().numpy()
+    P3 = H.segment_bases(cn, lo, hi_)
+    H1 = H.untile_rows(h1, cap, w.F)
+    H3 = H.untile_rows(h3, cap3, w.F)
+    for e in range(lo, hi_):
+        n = int(cn[e])
+        a0, b0 = int(P[e]), int(P3[e - lo])
+        assert torch.equal(H1[a0:a0 + n], H3[b0:b0 + n]), e
+        assert torch.equal(o1[a0:a0 + n], o3[b0:b0 + n]), e
 
 
 @pytest.mark.parametrize("w", [
@@ -326,9 +353,9 @@ def test_tile_shapes_bitexact(gpu, w):
     g = torch.from_numpy(gate.astype(np.float32)).cuda()
     fused = w.Kp == 1 and not Fs and w.e_hi - w.e_lo == w.N // w.M and w.e_lo % (w.N // w.M) == 0
     outs = []
-    try:
-        for tiles in (moge.TILES_TALL, moge.TILES_WIDE):
-            moge.set_gemm_tiles(tiles)
+    for tiles in (moge.TILES_TALL, moge.TILES_WIDE):
+        s.tiles = tiles
+        if True:
             h = torch.zeros(moge.tiled_elems(cap, w.F), **bf)
             hs = torch.zeros(moge.tiled_elems(w.T, Fs), **bf) if Fs else None
             o = torch.zeros(cap, w.d, **bf)
@@ -343,8 +370,6 @@ def test_tile_shapes_bitexact(gpu, w):
                 moge.expert_down_combine(s, h, offsets, w.e_lo, w.e_hi, cap, pd, perm, g, y)
             torch.cuda.synchronize()
             outs.append((h, o, hs, so, y))
-    finally:
-        moge.set_gemm_tiles(moge.TILES_AUTO)
     for a, b in zip(*outs):
         if a is not None:
             assert H.same_bits(a, b)

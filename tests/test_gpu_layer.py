@@ -175,3 +175,21 @@ def test_abi_errors_on_gpu(gpu):
     with pytest.raises(moge.MogeError, match="ARG"):
         moge.route(s, 0, None, None, torch.zeros(8, device="cuda"), torch.zeros(64, 8, device="cuda"),
                    torch.zeros(64, 4, dtype=torch.int32, device="cuda"), torch.zeros(64, 4, device="cuda"))
+
+
+def test_layer_every_expert_chosen(gpu):
+    # K' = N/M at 256 experts: the dense softmax mixture of all experts (K = 256 slots per token)
+    w = W.variant(W.decode(), name="dense_N256_M8_K32", T=40, d=256, N=256, M=8, Kp=32, F=64, std_bias=1.0)
+    layer, y = check_layer(w)
+    assert (layer.counts.cpu().numpy() == w.T).all()
+    # the gates of a token are its whole softmax: they sum to 1
+    assert np.allclose(layer.gate.sum(1).cpu().numpy(), 1.0, atol=1e-5)
+
+
+def test_layer_check_scores(gpu):
+    w = W.variant(W.decode(), name="check_T64", T=64, d=256, N=16, M=4, Kp=1, F=64)
+    layer, _ = check_layer(w)
+    layer.check_scores()                         # finite scores pass
+    layer.logits[3, 5] = float("nan")
+    with pytest.raises(moge.MogeError, match="NONFINITE"):
+        layer.check_scores()

@@ -125,3 +125,109 @@ def test_route_from_x_shapes(gpu, N, M, Kp, d, store):
     ridx, _, rgap = oracle.route(lg_ref, M, Kp, "grouped")
     _, _, hard = H.compare_routing(w, idx, ridx, rgap)
     assert hard.size == 0
+
+
+def _int_operands(T, d, N, seed, f32=False, zero_rows=()):
+    """x in {-2..2}, router rows in {-1, 0, 1}, an integer bias with -0 and +0: every score is an
+    exact integer (|score| <= 2 d + 3) whatever the order of the float32 sums, so experts tie
+    exactly and often.  Returns device tensors and the oracle's host copies (same values)."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randint(-2, 3, (T, d), generator=g).float()
+    x[list(zero_rows)] = 0.0                                    # these tokens score the bias alone
+    wr = torch.randint(-1, 2, (N, d), generator=g).float()
+    bias = torch.randint(-3, 4, (N,), generator=g).float()
+    bias[(bias == 0) & (torch.arange(N) % 2 == 1)] = -0.0      # half the zero biases are -0
+    dt = torch.float32 if f32 else torch.bfloat16
+    xd, wd = x.to(dt).cuda(), wr.to(dt).cuda()
+
+    def host(t):
+        return t.numpy() if f32 else t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return xd, wd, bias.cuda(), host(x), host(wr), bias.numpy()
+
+
+# (T, d, N, M, Kp, dtype, store): each fused router epilogue -- the split-K kernel for few tokens
+# (N <= 64 and <= 128), the streaming kernel (N = 64, 128; N = 256 as one 256-wide tile or, with
+# the scores stored, two halves and the lane-per-token choice), the generic and the unrolled
+# lane-parallel choice, the wave-per-token choice, the float32 kernel
+TIE_CASES = [(300, 128, 64, 8, 1, "bf16", True), (300, 128, 64, 8, 2, "bf16", False),
+             (32832, 128, 64, 8, 1, "bf16", True), (32832, 64, 64, 8, 2, "bf16", False),
+             (300, 128, 128, 4, 2, "bf16", True), (32832, 64, 128, 4, 2, "bf16", False),
+             (520, 128, 256, 8, 1, "bf16", True), (520, 128, 256, 8, 1, "bf16", False),
+             (300, 96, 16, 4, 1, "bf16", True), (64, 128, 8, 4, 1, "f32", True)]
+
+
+@pytest.mark.parametrize("T,d,N,M,Kp,dtype,store", TIE_CASES)
+def test_route_from_x_exact_ties(gpu, T, d, N, M, Kp, dtype, store):
+    # integer scores are computed exactly on both sides, so the choice -- including every tie,
+    # broken by the lower expert id, and -0 == +0 -- must match the oracle bit for bit
+    print(f"[route ties from x] T={T} d={d} N={N} M={M} K'={Kp} {dtype} store={store}", flush=True)
+    xd, wd, bd, xh, wh, bh = _int_operands(T, d, N, seed=T + N + Kp, f32=dtype == "f32", zero_rows=(0, 1, T - 1))
+    w = W.variant(W.routing(), T=T, d=d, N=N, M=M, Kp=Kp, dtype=dtype)
+    lg_ref = oracle.logits(xh, wh, bh)
+    for mode, omode in ((moge.ROUTE_GROUPED, "grouped"), (moge.ROUTE_GLOBAL, "global")):
+        _, idx, gate, lg = _route_dev(w, x=xd, wr=wd, bias=bd, mode=mode, store_logits=store)
+        if store:
+            assert np.array_equal(lg, lg_ref)
+        ridx, rgate, _ = oracle.route(lg_ref, M, Kp, omode)
+        assert (idx == ridx).all(), f"{omode}: {(idx != ridx).any(1).sum()} tokens differ"
+        assert (np.abs(gate - rgate) <= 1e-5 * rgate + 1e-8).all()
+
+
+NAN_CASES = [(200, 64, 8, 1, moge.ROUTE_GROUPED), (200, 64, 8, 2, moge.ROUTE_GLOBAL),
+             (130, 256, 8, 8, moge.ROUTE_GLOBAL), (100, 16, 4, 2, moge.ROUTE_GROUPED)]
+
+
+@pytest.mark.parametrize("T,N,M,Kp,mode", NAN_CASES)
+def test_route_nan_scores_keep_the_groups_full(gpu, T, N, M, Kp, mode):
+    # NaN is outside the method; the library ranks it as -inf, so every group still gets exactly K'
+    # distinct experts of its own, the same ones the oracle picks with NaN read as -inf
+    rng = np.random.default_rng(T + N)
+    lg = rng.standard_normal((T, N)).astype(np.float32)
+    lg[rng.random((T, N)) < 0.1] = np.nan
+    lg[3] = np.nan                                              # a token with no number at all
+    lg[5, :N // 2] = -np.inf
+    w = W.variant(W.routing(), T=T, N=N, M=M, Kp=Kp)
+    _, idx, _, _ = _route_dev(w, lg_np=lg, mode=mode)
+    omode = "grouped" if mode == moge.ROUTE_GROUPED else "global"
+    ridx, _, _ = oracle.route(np.where(np.isnan(lg), -np.inf, lg).astype(np.float32), M, Kp, omode)
+    assert (idx == ridx).all()
+    k, G, ng = (Kp, N // M, M) if mode == moge.ROUTE_GROUPED else (M * Kp, N, 1)
+    for g in range(ng):                         # exactly k distinct experts of group g in its slots
+        sl = idx[:, g * k:(g + 1) * k]
+        assert ((sl >= g * G) & (sl < (g + 1) * G)).all()
+        assert all(len(set(r)) == k for r in sl.tolist())
+
+
+def test_route_nan_token_from_x(gpu):
+    # a NaN in a token's row makes all its scores NaN inside the fused epilogue: it still takes
+    # the first K' experts of every group (ties by the lower id); the other tokens are unaffected
+    T, d, N, M, Kp = 300, 128, 64, 8, 2
+    xd, wd, bd, xh, wh, bh = _int_operands(T, d, N, seed=11)
+    xd[7, 3] = float("nan")
+    w = W.variant(W.routing(), T=T, d=d, N=N, M=M, Kp=Kp)
+    _, idx, _, _ = _route_dev(w, x=xd, wr=wd, bias=bd)
+    ridx, _, _ = oracle.route(oracle.logits(xh, wh, bh), M, Kp, "grouped")
+    keep = np.arange(T) != 7
+    assert (idx[keep] == ridx[keep]).all()
+    assert (idx[7] == np.repeat(np.arange(M) * (N // M), Kp) + np.tile(np.arange(Kp), M)).all()
+
+
+def test_check_finite(gpu):
+    ws = torch.empty(moge.workspace_size(moge.Shape(1, 8, 1, 1, 1, 0, moge.F32), moge.STAGE_CHECK),
+                     dtype=torch.uint8, device="cuda")
+    a = torch.randn(1_000_003, device="cuda")
+    moge.check_finite(a, ws)
+    for bad, where in ((float("nan"), 999_999), (float("inf"), 5), (float("-inf"), 1_000_002)):
+        b = a.clone()
+        b[where] = bad
+        b[where + 1 if where + 1 < b.numel() else 0] = bad
+        with pytest.raises(moge.MogeError, match="NONFINITE") as ei:
+            moge.check_finite(b, ws)
+        first = min(where, where + 1 if where + 1 < b.numel() else 0)
+        assert f"2 of {b.numel()} values" in str(ei.value) and f"index {first}" in str(ei.value)
+    h = torch.randn(4099, device="cuda").to(torch.bfloat16)
+    moge.check_finite(h, ws)
+    h[4098] = float("inf")
+    with pytest.raises(moge.MogeError, match="NONFINITE"):
+        moge.check_finite(h, ws)
+    moge.check_finite(torch.empty(0, device="cuda"), ws)
