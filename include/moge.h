@@ -219,6 +219,24 @@ moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32
                             hipStream_t stream);
 
 /*
+ * moge_dispatch_noalloc -- moge_dispatch for callers that cannot allocate device
+ * memory (code recorded into a HIP graph, tight serving loops, harnesses that
+ * forbid allocation): the same arguments and results, without ws / ws_bytes.
+ * Its workspace is a fixed 4 MiB array in device memory that the library holds
+ * on every GPU it runs on until the process ends; the call allocates and frees
+ * nothing.  Limit: moge_workspace_size(shape, MOGE_STAGE_DISPATCH) <= 4 MiB,
+ * i.e. N * ceil(T / 64) <= 524288 (256 experts up to T = 131072 tokens, 64
+ * experts up to T = 524288); larger shapes get MOGE_ERR_WORKSPACE before any
+ * launch.  All calls on one GPU share that array: calls that overlap in time on
+ * one GPU (different streams, or threads without ordering) race and must not be
+ * made; calls in order on one stream are safe.  The array keeps the last call's
+ * contents, and no part of it needs clearing between calls.
+ */
+moge_status_t moge_dispatch_noalloc(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
+                                    int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts, int32_t* offsets,
+                                    int32_t* inv, int32_t* perm, void* x_perm, void* x_tiled, hipStream_t stream);
+
+/*
  * moge_grouped_ffn -- the SwiGLU expert applied to every expert's row segment
  * (a grouped GEMM pair).  [P1] section 1: each token's rows go to the experts it
  * chose, whose groups sit on separate devices; section 3: the grouped matmul

@@ -35,7 +35,8 @@ TILES_TALL = 1
 TILES_WIDE = 2
 
 EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_weight_elems",
-           "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_grouped_ffn",
+           "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_dispatch_noalloc",
+           "moge_grouped_ffn",
            "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
            "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_expert_down_combine",
            "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_check_finite", "moge_version",
@@ -88,6 +89,8 @@ _lib.moge_route.restype = ctypes.c_int
 _lib.moge_dispatch.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                _P]
 _lib.moge_dispatch.restype = ctypes.c_int
+_lib.moge_dispatch_noalloc.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]
+_lib.moge_dispatch_noalloc.restype = ctypes.c_int
 _lib.moge_grouped_ffn.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P]
 _lib.moge_grouped_ffn.restype = ctypes.c_int
 _lib.moge_expert_gate_up.argtypes = [_SP, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P]
@@ -224,6 +227,21 @@ def dispatch(shape: Shape, mode: int, idx, x, e_lo: int, e_hi: int, rows_cap: in
                             _ptr(x_tiled, "x_tiled", et, tiled_elems(T, d), optional=True), _ptr(ws, "ws", None, None),
                             ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
     _check("moge_dispatch", st)
+
+
+def dispatch_noalloc(shape: Shape, mode: int, idx, x, e_lo: int, e_hi: int, rows_cap: int, counts, offsets, inv,
+                     perm, x_perm, x_tiled=None, stream=None) -> None:
+    """moge_dispatch without a workspace argument (the library's fixed device array instead)."""
+    T, N, K, d = shape.T, shape.N, shape.K, shape.d
+    et = _elem_dtype(shape)
+    st = _lib.moge_dispatch_noalloc(ctypes.byref(shape), mode, _ptr(idx, "idx", torch.int32, T * K),
+                                    _ptr(x, "x", et, T * d, optional=True), e_lo, e_hi, rows_cap,
+                                    _ptr(counts, "counts", torch.int32, N), _ptr(offsets, "offsets", torch.int32, N + 1),
+                                    _ptr(inv, "inv", torch.int32, T * K, optional=True),
+                                    _ptr(perm, "perm", torch.int32, rows_cap, optional=True),
+                                    _ptr(x_perm, "x_perm", et, tiled_elems(rows_cap, d), optional=True),
+                                    _ptr(x_tiled, "x_tiled", et, tiled_elems(T, d), optional=True), _stream(stream))
+    _check("moge_dispatch_noalloc", st)
 
 
 def grouped_ffn(shape: Shape, x_perm, offsets, e_lo: int, e_hi: int, rows_cap: int, w_gate, w_up, w_down, h, out,

@@ -22,6 +22,9 @@
 //                             when the expert GEMMs cannot read the rows from x).
 // Every expert's rows start on a 16-row boundary (P(e) in moge.h), so a 16-row
 // tile of the GEMM operands never mixes experts.
+#include <mutex>
+#include <string>
+
 #include "moge_internal.hpp"
 
 namespace moge {
@@ -315,10 +318,10 @@ static moge_status_t dispatch_blocks_path(const moge_shape_t& s, int K, const in
   return st;
 }
 
-extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
-                                       int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts,
-                                       int32_t* offsets, int32_t* inv, int32_t* perm, void* x_perm, void* x_tiled,
-                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+// Argument checks shared by both entry points (no workspace check).
+static moge_status_t dispatch_checks(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
+                                     int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts, int32_t* offsets,
+                                     int32_t* inv, int32_t* perm, void* x_perm, void* x_tiled) {
   moge_status_t st = validate_shape(shape);
   if (st != MOGE_OK) return st;
   const moge_shape_t& s = *shape;
@@ -329,13 +332,18 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
   if (x && !inv) return fail(MOGE_ERR_NULL, "row copies need inv and perm");
   if (x_tiled && !x) return fail(MOGE_ERR_NULL, "x_tiled needs x");
   if (e_lo < 0 || e_hi > s.N || e_lo >= e_hi) return fail(MOGE_ERR_ARG, "need 0 <= e_lo < e_hi <= N");
-  const int K = s.M * s.k_per_group;  // <= N <= 256 (moge_validate)
   const int64_t bound = rows_bound(s, mode, e_lo, e_hi);
   if (inv && rows_cap < bound)
     return fail(MOGE_ERR_CAPACITY, "rows_cap is below moge_rows_bound() for this expert range");
-  const size_t need = moge_workspace_size(shape, MOGE_STAGE_DISPATCH);
-  if (!ws || ws_bytes < need) return fail(MOGE_ERR_WORKSPACE, "dispatch workspace missing or too small");
+  return MOGE_OK;
+}
 
+// The launches (arguments already checked; ws holds moge_workspace_size(MOGE_STAGE_DISPATCH) bytes).
+static moge_status_t dispatch_launch(const moge_shape_t& s, const int32_t* idx, const void* x, int32_t e_lo,
+                                     int32_t e_hi, int64_t rows_cap, int32_t* counts, int32_t* offsets, int32_t* inv,
+                                     int32_t* perm, void* x_perm, void* x_tiled, void* ws, hipStream_t stream) {
+  moge_status_t st;
+  const int K = s.M * s.k_per_group;  // <= N <= 256 (moge_validate)
   if ((int64_t)s.T * K <= kSmallSlots) {  // one workgroup does counts, offsets and the permutation
     // 8 N + 4 (T (K + 1) + 3 N + 1) bytes: with T K <= 8192 and N <= 256 at most
     // 8 * 256 + 4 * (2 * 8192 + 769) = 70.7 KiB (T = 8192, K = 1), above the 64 KiB default
@@ -360,5 +368,74 @@ extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, 
                        static_cast<char*>(x_tiled));
     st = check_launch("dispatch_copy_kernel");
   }
+  return st;
+}
+
+extern "C" moge_status_t moge_dispatch(const moge_shape_t* shape, int32_t mode, const int32_t* idx, const void* x,
+                                       int32_t e_lo, int32_t e_hi, int64_t rows_cap, int32_t* counts,
+                                       int32_t* offsets, int32_t* inv, int32_t* perm, void* x_perm, void* x_tiled,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  moge_status_t st = dispatch_checks(shape, mode, idx, x, e_lo, e_hi, rows_cap, counts, offsets, inv, perm, x_perm,
+                                     x_tiled);
+  if (st != MOGE_OK) return st;
+  const size_t need = moge_workspace_size(shape, MOGE_STAGE_DISPATCH);
+  if (!ws || ws_bytes < need) return fail(MOGE_ERR_WORKSPACE, "dispatch workspace missing or too small");
+  st = dispatch_launch(*shape, idx, x, e_lo, e_hi, rows_cap, counts, offsets, inv, perm, x_perm, x_tiled, ws, stream);
+  return st == MOGE_OK ? ok() : st;
+}
+
+// ---- moge_dispatch_noalloc: the same work with the workspace in a file-scope device array.
+// Each GPU that runs the library holds its own copy of `scratch` until the process ends; host
+// code never passes the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): it asks the runtime for the device address once per device, with that device
+// current, and uses that address from then on.  Nothing in the array has to start at zero (the
+// block counts and their prefixes are fully written before they are read), so no call clears it.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;  // 4 MiB: N * ceil(T / 64) <= 524288
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The device address of `scratch` on the device that runs `stream` (looked up once per device).
+static moge_status_t scratch_address(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(MOGE_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return fail(MOGE_ERR_HIP, std::string("hipStreamGetDevice: ") + hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOGE_ERR_HIP, "device id out of the supported range");
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(MOGE_ERR_HIP, std::string("hipSetDevice: ") + hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) hipSetDevice(cur);
+    if (e != hipSuccess || !p)
+      return fail(MOGE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return MOGE_OK;
+}
+
+extern "C" moge_status_t moge_dispatch_noalloc(const moge_shape_t* shape, int32_t mode, const int32_t* idx,
+                                               const void* x, int32_t e_lo, int32_t e_hi, int64_t rows_cap,
+                                               int32_t* counts, int32_t* offsets, int32_t* inv, int32_t* perm,
+                                               void* x_perm, void* x_tiled, hipStream_t stream) {
+  moge_status_t st = dispatch_checks(shape, mode, idx, x, e_lo, e_hi, rows_cap, counts, offsets, inv, perm, x_perm,
+                                     x_tiled);
+  if (st != MOGE_OK) return st;
+  const size_t need = moge_workspace_size(shape, MOGE_STAGE_DISPATCH);
+  if (need > kNoAllocScratchBytes)
+    return fail(MOGE_ERR_WORKSPACE, "moge_dispatch_noalloc: the shape needs " + std::to_string(need) +
+                                        " bytes of workspace, above its fixed " +
+                                        std::to_string(kNoAllocScratchBytes) + " (N * ceil(T / 64) <= 524288)");
+  void* ws = nullptr;
+  if ((st = scratch_address(stream, &ws)) != MOGE_OK) return st;
+  st = dispatch_launch(*shape, idx, x, e_lo, e_hi, rows_cap, counts, offsets, inv, perm, x_perm, x_tiled, ws, stream);
   return st == MOGE_OK ? ok() : st;
 }

@@ -199,3 +199,21 @@ def test_check_finite_argument_errors():
     assert lib.moge_check_finite(moge.F32, None, 0, None, 0, None) == 0     # nothing to check
     from mixture_grouped_experts_amd import _lib
     assert _lib.STATUS[8] == "MOGE_ERR_NONFINITE"
+
+
+def test_dispatch_noalloc_refuses_shapes_past_its_scratch():
+    # checked on the host before the device is touched: 256 experts x 2049 token blocks x 8 bytes > 4 MiB
+    lib = ctypes.CDLL(moge.LIB_PATH)
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    lib.moge_dispatch_noalloc.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                          P, P, P, P, P, P, P]
+    big = S(T=131073, N=256, M=8, Kp=1)
+    assert moge.workspace_size(big) > 4 << 20
+    assert lib.moge_dispatch_noalloc(ctypes.byref(big), 0, fake, None, 0, 256, 0, fake, fake, None, None, None, None,
+                                     None) == 4
+    assert "4194304" in moge.last_error()
+    ok_shape = S(T=131072, N=256, M=8, Kp=1)
+    assert moge.workspace_size(ok_shape) == 4 << 20                  # exactly the limit
+    assert lib.moge_dispatch_noalloc(ctypes.byref(S()), 0, None, None, 0, 8, 0, fake, fake, None, None, None, None,
+                                     None) == 3                       # idx NULL
