@@ -16,9 +16,16 @@ roofline uses the call's event-measured duration with its algorithmic bytes (wei
 activations it must move) and FLOPs per launch.  The per-stage table comes from K more steps
 with every call marked, after the timed region.
 
+With the default workload the same process then measures the metric's other two parts on their
+own shapes (key "extra"): the router's HBM rate on the 65536-token x 4096 x 64-expert routing
+shape, and the grouped GEMMs' MFMA rate on one device's share of a 65536-token batch (group 0's
+8 experts).  The line also carries each expert's share of its group's load (min / mean / max;
+1/(N/M) when even) for MoGE and for the global top-K comparator, and the parity statistics of the
+CPU-baseline sample (near-tie and flipped tokens, max |y_gpu - y_oracle| against the bar).
+
     python bench.py [--steps K] [--warmup W] [--workload ultra|group0|decode|routing|tiny|pro]
                     [--tokens T] [--rows auto|gather|copy] [--tiles auto|tall|wide]
-                    [--no-cpu-baseline] [--cpu-seconds S]
+                    [--no-cpu-baseline] [--cpu-seconds S] [--no-extra] [--extra-steps K]
 """
 from __future__ import annotations
 
@@ -51,6 +58,9 @@ def parse():
     p.add_argument("--tokens", type=int, default=0,
                    help="run the workload's shape with this many tokens instead (its name records the count)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the routing-shape router and one-group-share GEMM measurements (ultra only)")
+    p.add_argument("--extra-steps", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
@@ -144,9 +154,13 @@ def measured_traffic(workload, stage):
     return rec["read_bytes"] + rec["written_bytes"]
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_baseline(w, seconds: float, gpu_idx=None, gpu_y=None):
     """The oracle, as it stands, on a bounded sample of tokens of the same workload (route on the
-    sampled tokens' scores + every routed and shared expert they use + the weighted sum)."""
+    sampled tokens' scores + every routed and shared expert they use + the weighted sum).  With the
+    GPU's idx and y of the same inputs, the sample's parity statistics are returned as well: the
+    tokens whose in-group probability gap is below 1e-5 (near-tie), those routed differently on such
+    a gap (flipped, excluded from the y comparison) or on a larger one (hard flips: a failure), and
+    the largest |y_gpu - y_oracle| against the bound 1e-2 max|y_oracle| + 1e-3."""
     import numpy as np
 
     import oracle
@@ -166,63 +180,71 @@ def cpu_baseline(w, seconds: float):
                 hi.expert(int(e))
         t0 = time.perf_counter()
         lg = oracle.logits(x, wr, bias)
-        idx, gate, _ = oracle.route(lg, w.M, w.Kp, "grouped")
-        if w.F:
-            oracle.combine_rows(x, idx, gate, w.e_lo, w.e_hi, hi.expert, hi.shared())
-        return time.perf_counter() - t0
+        idx, gate, gap = oracle.route(lg, w.M, w.Kp, "grouped")
+        y = oracle.combine_rows(x, idx, gate, w.e_lo, w.e_hi, hi.expert, hi.shared()) if w.F else None
+        return time.perf_counter() - t0, idx, gap, y
 
     # size the sample to about `seconds` of oracle time: a small probe, then one correction
     probe = sample_tokens(w.T, 8, seed=7)[:8]
-    dt = run(probe)
+    dt = run(probe)[0]
     n = int(max(2, min(w.T, 4096, seconds / max(dt / len(probe), 1e-9))))
     tokens = sample_tokens(w.T, n, seed=11)[:n]
-    dt = run(tokens)
+    dt, idx, gap, yref = run(tokens)
     if dt < 0.6 * seconds and n < min(w.T, 4096):
         n = int(min(w.T, 4096, n * seconds / max(dt, 1e-9)))
         tokens = sample_tokens(w.T, n, seed=11)[:n]
-        dt = run(tokens)
-    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(tokens)} of {w.T} tokens (seeded sample), full layer per token in binary64; "
-                      f"{dt:.1f} s"}
+        dt, idx, gap, yref = run(tokens)
+    out = {"value": len(tokens) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(tokens)} of {w.T} tokens (seeded sample), full layer per token in binary64; "
+                     f"{dt:.1f} s"}
+    if gpu_idx is not None:
+        diff = np.any(gpu_idx[tokens] != idx, axis=1)
+        near = gap < 1e-5
+        par = {"tokens": int(len(tokens)), "near_tie": int(near.sum()), "flipped": int((diff & near).sum()),
+               "hard_flips": int((diff & ~near).sum())}
+        if yref is not None and gpu_y is not None:
+            keep = ~diff
+            ref = yref[keep]
+            err = float(np.max(np.abs(gpu_y[tokens][keep].astype(np.float64) - ref))) if ref.size else 0.0
+            bound = 1e-2 * float(np.max(np.abs(ref))) + 1e-3 if ref.size else 1e-3
+            par.update({"y_max_abs_err": err, "y_bound": bound, "y_within_bound": bool(err <= bound)})
+        out["parity"] = par
+    return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the expert-parallel "
-              f"sharding of the layer over several GPUs is described, not implemented", file=sys.stderr)
-        sys.exit(2)
-
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
+def expert_share(counts, w):
+    """Each expert's share of its group's assignments, counts[e] / (T K'); MoGE puts exactly T K'
+    assignments in every group, so the shares of a group sum to 1 and average 1 / (N/M)."""
     import numpy as np
+
+    c = np.asarray(counts, dtype=np.float64)
+    sh = c / float(w.T * w.Kp)
+    return {"mean": float(sh.mean()), "min": float(sh.min()), "max": float(sh.max()),
+            "uniform": 1.0 / (w.N // w.M)}
+
+
+def _layer(w, rows="auto", tiles="auto"):
     import torch
 
     import mixture_grouped_experts_amd as moge
     from mixture_grouped_experts_amd.layer import MoGELayer
-    from synth import workloads as W
     from synth.inputs import device_inputs
 
-    w = {"ultra": W.ultra, "group0": W.group0, "decode": W.decode, "routing": W.routing, "tiny": W.tiny,
-         "pro": W.pro}[
-        args.workload]()
-    if args.tokens:
-        import re
-
-        w = W.variant(w, T=args.tokens, e_lo=w.e_lo, e_hi=w.e_hi,
-                      name=re.sub(r"_T\d+_", f"_T{args.tokens}_", w.name))
-    torch.cuda.set_device(0)
     dv = device_inputs(w)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi,
-                      gather={"auto": None, "gather": True, "copy": False}[args.rows],
-                      tiles={"auto": moge.TILES_AUTO, "tall": moge.TILES_TALL, "wide": moge.TILES_WIDE}[args.tiles])
+                      gather={"auto": None, "gather": True, "copy": False}[rows],
+                      tiles={"auto": moge.TILES_AUTO, "tall": moge.TILES_TALL, "wide": moge.TILES_WIDE}[tiles])
     if w.F:
         # expert weights are packed once, at load time (outside the timed steps)
         (pg, pu, pd), ps = layer.pack_expert_weights(dv.w_gate, dv.w_up, dv.w_down, dv.shared)
         dv = dataclasses.replace(dv, w_gate=pg, w_up=pu, w_down=pd, shared=ps)
         torch.cuda.synchronize()
+    return layer, dv
+
+
+def _stepper(layer, dv):
+    import torch
+
     stream = torch.cuda.current_stream()
 
     def step(marks=None, only=None):
@@ -252,6 +274,79 @@ def main():
             for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
                 out.setdefault(n1, []).append(e0.elapsed_time(e1))
         return out
+    return stream, step, run_marked
+
+
+def _stage_table(stage_us, work):
+    stages = {}
+    for k, us in stage_us.items():
+        entry = {"us": round(us, 2)}
+        if k in work:
+            wk = work[k]
+            entry["GB/s"] = round(wk["bytes"] / (us * 1e-6) / 1e9, 1)
+            if wk["flops"]:
+                entry["TFLOP/s"] = round(wk["flops"] / (us * 1e-6) / 1e12, 1)
+                entry["mfma_frac"] = round(wk["flops"] / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
+            entry["hbm_frac"] = round(wk["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        stages[k] = entry
+    return stages
+
+
+def side_workload(w, steps, warmup, keys):
+    """The stages `keys` of another workload's layer, measured in the same process (every call
+    marked, `steps` steps after `warmup`): what the metric asks for beside the main workload's
+    tokens/s -- the router's HBM rate at the routing shape, the grouped GEMMs' MFMA rate at the
+    one-group share."""
+    import numpy as np
+    import torch
+
+    layer, dv = _layer(w)
+    _, step, run_marked = _stepper(layer, dv)
+    for _ in range(warmup):
+        step()
+    times = run_marked(steps)
+    work = algorithmic_work(w, layer.counts.cpu().numpy(), fused_shared=bool(w.F_shared) and layer.fuse_shared,
+                            gather=layer.gather, fused_combine=layer.fuse_combine)
+    stage_us = {k: 1000.0 * float(np.mean(v)) for k, v in times.items() if k in keys}
+    out = {"workload": w.name, "steps": steps, "stages": _stage_table(stage_us, work),
+           "per_expert_share": expert_share(layer.counts.cpu().numpy()[w.e_lo:w.e_hi], w),
+           "imbalance": {"moge_is_raw": int(layer.is_raw.item()),
+                         "global_topk_is_raw": int(layer.g_is_raw.item())}}
+    if w.e_hi - w.e_lo == w.N:
+        out["per_expert_share_global_topk"] = expert_share(layer.gcounts.cpu().numpy(), w)
+    del layer, dv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the expert-parallel "
+              f"sharding of the layer over several GPUs is described, not implemented", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from synth import workloads as W
+
+    w = {"ultra": W.ultra, "group0": W.group0, "decode": W.decode, "routing": W.routing, "tiny": W.tiny,
+         "pro": W.pro}[
+        args.workload]()
+    if args.tokens:
+        import re
+
+        w = W.variant(w, T=args.tokens, e_lo=w.e_lo, e_hi=w.e_hi,
+                      name=re.sub(r"_T\d+_", f"_T{args.tokens}_", w.name))
+    torch.cuda.set_device(0)
+    layer, dv = _layer(w, args.rows, args.tiles)
+    stream, step, run_marked = _stepper(layer, dv)
 
     for _ in range(max(args.warmup - 1, 0)):
         step()
@@ -305,18 +400,7 @@ def main():
     roof["algorithmic_bytes"] = wb
     roof["algorithmic_flops"] = wf
     roof["avg_us"] = stage_us[dom]
-
-    stages = {}
-    for k, us in stage_us.items():
-        entry = {"us": round(us, 2)}
-        if k in work:
-            wk = work[k]
-            entry["GB/s"] = round(wk["bytes"] / (us * 1e-6) / 1e9, 1)
-            if wk["flops"]:
-                entry["TFLOP/s"] = round(wk["flops"] / (us * 1e-6) / 1e12, 1)
-                entry["mfma_frac"] = round(wk["flops"] / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
-            entry["hbm_frac"] = round(wk["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-        stages[k] = entry
+    roof["mfma_frac"] = wf / t / 1e12 / BF16_PEAK_TFLOPS if wf else None
 
     out = {
         "metric": METRIC,
@@ -337,12 +421,28 @@ def main():
                    "tiles": (args.tiles if args.tiles != "auto"
                              else "wide" if w.T * w.M * w.Kp <= 64 * w.N else "tall")},
         "roofline": roof,
-        "stages": stages,
+        "stages": _stage_table(stage_us, work),
         "imbalance": {"moge_is_raw": int(layer.is_raw.item()),
                       "global_topk_is_raw": int(layer.g_is_raw.item()) if layer.comparator else None},
+        "per_expert_share": expert_share(counts[w.e_lo:w.e_hi], w),
     }
+    if layer.comparator and w.e_hi - w.e_lo == w.N:
+        out["per_expert_share_global_topk"] = expert_share(layer.gcounts.cpu().numpy(), w)
+    gpu_idx = layer.idx.cpu().numpy()
+    gpu_y = layer.y.cpu().numpy() if w.F else None
+    del layer, dv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_extra and args.workload == "ultra" and not args.tokens:
+        # the metric's other two parts, on their own workloads, in this same process
+        out["extra"] = {
+            "routing_router": side_workload(W.routing(), args.extra_steps, 3, {"route", "dispatch",
+                                                                                "global_comparator"}),
+            "group0_gemms": side_workload(W.group0(), args.extra_steps, 3, {"gate_up", "down", "dispatch",
+                                                                             "route"}),
+        }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, gpu_idx, gpu_y)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
