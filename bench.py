@@ -95,7 +95,8 @@ def algorithmic_work(w, counts, fused_shared=False, gather=False, fused_combine=
     R = int(rng.sum())
     active = int((rng > 0).sum())
     work = {}
-    work["route"] = dict(bytes=T * d * b + N * d * b + T * N * 4 + T * K * 8, flops=2 * T * d * N)
+    # both routers' choices (MoGE and the global comparator) from one pass over x; no scores stored
+    work["route"] = dict(bytes=T * d * b + N * d * b + 2 * T * K * 8, flops=2 * T * d * N)
     work["dispatch"] = dict(bytes=T * K * 4 * 3 + (T * d * b + R * d * b if F and not gather else 0), flops=0)
     if F:
         a_bytes = T * d * b if gather else R * d * b

@@ -71,7 +71,7 @@ typedef enum { MOGE_BF16 = 0, MOGE_F32 = 1 } moge_dtype_t;
 typedef enum { MOGE_ROUTE_GROUPED = 0, MOGE_ROUTE_GLOBAL = 1 } moge_route_mode_t;
 
 /* Workspace stages for moge_workspace_size(). */
-typedef enum { MOGE_STAGE_DISPATCH = 1, MOGE_STAGE_CHECK = 2 } moge_stage_t;
+typedef enum { MOGE_STAGE_DISPATCH = 1, MOGE_STAGE_CHECK = 2, MOGE_STAGE_ROUTE = 3 } moge_stage_t;
 
 /* Tile shape of the bf16 expert GEMMs (moge_shape_t.tiles).  Every output is
  * bit-identical under all of them (same reduction order per output element).
@@ -176,6 +176,9 @@ moge_status_t moge_round_bf16(const float* x, uint16_t* y, int64_t n, hipStream_
  *   idx      [T][K] int32 out: chosen expert ids.
  *   gate     [T][K] f32 out: the chosen experts' probabilities under the softmax
  *            over all N scores (not renormalised over the chosen experts).
+ *   ws       device workspace of moge_workspace_size(shape, MOGE_STAGE_ROUTE)
+ *            bytes (0 -- NULL allowed -- except for bf16 scores from x with
+ *            N > 128, where it holds partial sums of a split reduction).
  * Slot order: GROUPED -> slot = g*K' + rank inside group g; GLOBAL -> slot = rank.
  * rank orders experts by score, higher first, equal scores -> lower expert id
  * (-0 and +0 are equal).
@@ -185,7 +188,21 @@ moge_status_t moge_round_bf16(const float* x, uint16_t* y, int64_t n, hipStream_
  * scores; a token with a NaN or infinite score may get NaN gates.
  */
 moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, const void* x, const void* w_router,
-                         const float* bias, float* logits, int32_t* idx, float* gate, hipStream_t stream);
+                         const float* bias, float* logits, int32_t* idx, float* gate, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * moge_route_pair -- both routers on the same scores in one pass: the MoGE choice
+ * (idx, gate: MOGE_ROUTE_GROUPED) and the conventional global top-K with K = M*K'
+ * (gidx, ggate: MOGE_ROUTE_GLOBAL) that [P1] section 1 compares it with.  Each
+ * result equals moge_route's for that mode; the scores are computed (or read) once
+ * and need not be stored for the second router.  Arguments as moge_route; all four
+ * outputs are required.
+ */
+moge_status_t moge_route_pair(const moge_shape_t* shape, const void* x, const void* w_router, const float* bias,
+                              float* logits, int32_t* idx, float* gate, int32_t* gidx, float* ggate, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
 
 /*
  * moge_dispatch -- per-expert counts and the token permutation (dropless: every

@@ -30,12 +30,14 @@ ROUTE_GROUPED = 0
 ROUTE_GLOBAL = 1
 STAGE_DISPATCH = 1
 STAGE_CHECK = 2
+STAGE_ROUTE = 3
 TILES_AUTO = 0
 TILES_TALL = 1
 TILES_WIDE = 2
 
 EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_weight_elems",
-           "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_dispatch", "moge_dispatch_noalloc",
+           "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_route_pair", "moge_dispatch",
+           "moge_dispatch_noalloc",
            "moge_grouped_ffn",
            "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
            "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_expert_down_combine",
@@ -84,8 +86,10 @@ _lib.moge_round_bf16.argtypes = [_P, _P, _I64, _P]
 _lib.moge_round_bf16.restype = ctypes.c_int
 _lib.moge_workspace_size.argtypes = [_SP, _I32]
 _lib.moge_workspace_size.restype = ctypes.c_size_t
-_lib.moge_route.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _P]
+_lib.moge_route.argtypes = [_SP, _I32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.moge_route.restype = ctypes.c_int
+_lib.moge_route_pair.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.moge_route_pair.restype = ctypes.c_int
 _lib.moge_dispatch.argtypes = [_SP, _I32, _P, _P, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                _P]
 _lib.moge_dispatch.restype = ctypes.c_int
@@ -202,16 +206,37 @@ def last_error() -> str:
     return _lib.moge_last_error().decode()
 
 
-def route(shape: Shape, mode: int, x, w_router, bias, logits, idx, gate, stream=None) -> None:
+def _ws(ws):
+    return (_ptr(ws, "ws", None, None), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+
+
+def route(shape: Shape, mode: int, x, w_router, bias, logits, idx, gate, ws=None, stream=None) -> None:
+    """ws: workspace_size(shape, STAGE_ROUTE) bytes (None when that is 0)."""
     T, N, K, d = shape.T, shape.N, shape.K, shape.d
     et = _elem_dtype(shape)
+    wsp, wsb = _ws(ws)
     st = _lib.moge_route(ctypes.byref(shape), mode, _ptr(x, "x", et, T * d, optional=True),
                          _ptr(w_router, "w_router", et, N * d, optional=x is None),
                          _ptr(bias, "bias", torch.float32, N, optional=True),
                          _ptr(logits, "logits", torch.float32, T * N, optional=x is not None),
-                         _ptr(idx, "idx", torch.int32, T * K), _ptr(gate, "gate", torch.float32, T * K),
+                         _ptr(idx, "idx", torch.int32, T * K), _ptr(gate, "gate", torch.float32, T * K), wsp, wsb,
                          _stream(stream))
     _check("moge_route", st)
+
+
+def route_pair(shape: Shape, x, w_router, bias, logits, idx, gate, gidx, ggate, ws=None, stream=None) -> None:
+    """Both routers on the same scores: MoGE into idx/gate, the global top-K into gidx/ggate."""
+    T, N, K, d = shape.T, shape.N, shape.K, shape.d
+    et = _elem_dtype(shape)
+    wsp, wsb = _ws(ws)
+    st = _lib.moge_route_pair(ctypes.byref(shape), _ptr(x, "x", et, T * d, optional=True),
+                              _ptr(w_router, "w_router", et, N * d, optional=x is None),
+                              _ptr(bias, "bias", torch.float32, N, optional=True),
+                              _ptr(logits, "logits", torch.float32, T * N, optional=x is not None),
+                              _ptr(idx, "idx", torch.int32, T * K), _ptr(gate, "gate", torch.float32, T * K),
+                              _ptr(gidx, "gidx", torch.int32, T * K), _ptr(ggate, "ggate", torch.float32, T * K),
+                              wsp, wsb, _stream(stream))
+    _check("moge_route_pair", st)
 
 
 def dispatch(shape: Shape, mode: int, idx, x, e_lo: int, e_hi: int, rows_cap: int, counts, offsets, inv, perm,

@@ -112,6 +112,7 @@ extern "C" size_t moge_workspace_size(const moge_shape_t* shape, int32_t stage) 
     return (size_t)(2 * (int64_t)shape->N * nb) * sizeof(int32_t);
   }
   if (stage == MOGE_STAGE_CHECK) return check_workspace_bytes();
+  if (stage == MOGE_STAGE_ROUTE) return route_workspace_bytes(*shape);
   return (size_t)-1;
 }
 

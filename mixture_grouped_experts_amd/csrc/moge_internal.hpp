@@ -40,6 +40,9 @@ __host__ __device__ __forceinline__ int64_t tiled_index(int64_t r, int64_t c, in
 constexpr int kCheckBlocks = 1024;
 inline size_t check_workspace_bytes() { return (size_t)kCheckBlocks * 2 * sizeof(int64_t) + 2 * sizeof(int64_t); }
 
+// Bytes of workspace moge_route needs for the shape when it computes the scores from x.
+size_t route_workspace_bytes(const moge_shape_t& s);
+
 // Dispatch geometry (shared by moge_workspace_size and the dispatch kernels).
 constexpr int kDispatchTokens = 64;   // tokens per dispatch workgroup (one per lane)
 inline int64_t dispatch_blocks(int64_t T) { return (T + kDispatchTokens - 1) / kDispatchTokens; }

@@ -1,5 +1,6 @@
-// moge_route: router scores -> softmax over all N experts -> top-K' inside each
-// of the M expert groups (MoGE), or top-K over all experts (conventional router).
+// moge_route / moge_route_pair: router scores -> softmax over all N experts -> top-K'
+// inside each of the M expert groups (MoGE), and/or top-K over all experts (the
+// conventional router the pages compare MoGE with), from one pass over x.
 //
 // Method: Pangu Pro MoE, lsdiaocha.cn summary, section 1 (architecture): the N
 // experts are split evenly into M groups, one per device; a token's scores go
@@ -7,26 +8,28 @@
 // group are kept, which puts exactly K' of the token's assignments on each device.
 //
 // gfx950 design
-//   * bf16 scores: x [T][d] is streamed from HBM once.  A workgroup of 4 waves owns
-//     TM tokens x NP experts (128 x 64, 64 x 128 or 32 x 256 by N), TM*NP = 8192;
-//     each wave owns a 32-token x 64-expert block and accumulates it with
-//     v_mfma_f32_32x32x16_bf16 (float32 accumulate).  Token rows and router rows go
-//     from global memory straight into a 6- to 8-stage LDS ring with direct-to-LDS
-//     loads, several 32-element steps ahead, so each workgroup keeps tens of KiB of
-//     x in flight without staging registers; the router slab of a step is shared by
-//     the workgroup's waves.  Few tokens (fewer 128-token tiles than CUs, N <= 128):
-//     a split-K kernel whose operands go straight from global memory into MFMA
-//     registers.
-//   * Epilogue in the same kernel: the TM x N score tile goes to LDS, the optional
-//     score store is coalesced, and the choice runs lane-parallel (one lane per
-//     token and group) or, for wide groups, one wave per token.
-//   * N > 128 with the scores stored: the experts are split in two halves over the
-//     XCDs (each XCD's L2 keeps its half of the router matrix), the kernel only
-//     writes scores, and the choice is a second pass.
-//   * The choice from stored scores (that pass, the global comparator, caller
-//     scores) runs one lane per token with a sorted register list per group.
+//   * bf16 scores, N <= 128: x [T][d] is streamed from HBM once.  A workgroup of 4
+//     waves owns TM tokens x NP experts (128 x 64 or 64 x 128), each wave a 32-token x
+//     64-expert block accumulated with v_mfma_f32_32x32x16_bf16 (float32).  Token rows
+//     and router rows go from global memory straight into a 6-stage LDS ring with
+//     direct-to-LDS loads, several 32-element steps ahead.  Few tokens (fewer 128-token
+//     tiles than CUs): a split-K kernel whose operands go straight into registers.
+//   * bf16 scores, 128 < N <= 256: split over the hidden dimension.  Workgroup b takes
+//     slice b % S of the reduction (S = 1..4, so that the token tiles times S fill the
+//     chip) of a 128-token x 256-expert tile; workgroup b runs on XCD b % 8, so an XCD
+//     only ever reads its slices of the router matrix, which stay in its L2, and x is
+//     read from HBM exactly once.  Slice partial sums go to the workspace; a second
+//     kernel adds them in slice order (deterministic), adds the bias and chooses.
+//   * The choice (one epilogue for every kernel): the score tile sits in LDS; lane
+//     (token, group) keeps its group's best experts in a sorted register list; the
+//     token's softmax max and sum are butterflies over its lanes; MoGE takes the first
+//     K' of every list, the global top-K merges the lists head by head -- both routers
+//     from the same tile, so the comparator needs no stored scores.  Shapes past the
+//     lists' limits use one lane per (token, group) rank rounds or one wave per token.
 //   * float32 shapes use a vector-ALU scores kernel with the same epilogue.
 #include <math.h>
+
+#include <type_traits>
 
 #include "moge_internal.hpp"
 
@@ -236,21 +239,320 @@ __host__ __device__ __forceinline__ bool lane_parallel_choice(int N, int n_group
   return n_groups <= 64 && (k + 2) * (N / n_groups) <= 256;
 }
 
-// Writes the LDS score tile [rows][ld] to logits_out (if any) and runs the choice.
-// (all threads of the block call it)
-__device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
-                                              int N, int n_groups, int k, float* __restrict__ logits_out,
-                                              int32_t* __restrict__ idx, float* __restrict__ gate) {
-  // The scores go out with the non-temporal hint: every tile writes them at the same
-  // time at the end of the kernel, and streamed past the L2 they no longer wait there
-  // for the kernel's final write-back (the route kernel at 65536 tokens x 4096 x 64
-  // experts was 4% faster).
-  if (logits_out) {
-    for (int i = threadIdx.x; i < rows * N; i += blockDim.x) {
-      const int r = i / N, c = i - r * N;
-      if (t0 + r < T) __builtin_nontemporal_store(lt[r * ld + c], logits_out + (t0 + r) * N + c);
+
+// Butterfly partner of a lane at distance `off` (1, 2, 4, ...) inside its group of 2 off lanes,
+// for the lane-parallel choices' reductions over a token's lanes.  Up to 16 lanes the partner
+// comes through DPP (quad permutations, then the half-row and row mirrors: the pairing differs
+// from lane ^ off but, applied in this order, every lane ends with its group's result), beyond
+// that through the cross-lane permute.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int partner_i(int v, int off) {
+  switch (off) {
+    case 1: return dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    case 2: return dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    case 4: return dpp_mov<0x141>(v);  // row_half_mirror
+    case 8: return dpp_mov<0x140>(v);  // row_mirror
+    default: return __shfl_xor(v, off, 64);
+  }
+}
+__device__ __forceinline__ float partner_f(float v, int off) {
+  return __builtin_bit_cast(float, partner_i(__builtin_bit_cast(int, v), off));
+}
+
+// Length of the sorted per-group list that choose_lanes keeps (a power of two <= 32), or 0
+// when the lanes cannot take the shape: the MoGE choice needs the k best of a group, the
+// global top-K (K = M k) at most min(G, K) of one group.
+__host__ __device__ __forceinline__ int lane_list_len(int N, int M, int k, bool global) {
+  const int G = N / M;
+  const int need = global ? (G < M * k ? G : M * k) : k;
+  if (M > 64 || need > 32 || G * need > 8192) return 0;
+  int L = 1;
+  while (L < need) L <<= 1;
+  return L;
+}
+
+// Both routers from one LDS score tile [rows][ld].  Lane (tl, g) of a wave owns group g
+// of token tl: a token's Mp lanes (M rounded up to a power of two) are adjacent, so a
+// wave pass covers 64 / Mp tokens.  The lane keeps the KMAX best experts of its group,
+// best first (score descending, expert id ascending; a branch-free insertion network
+// over the scores in id order: a later equal score never displaces an earlier one, and
+// empty places take any expert).  The token's softmax maximum and denominator over all
+// N scores are butterflies over its lanes.
+//   MoGE  (idx != NULL):  slot g*k + r <- the group's r-th best, r < k;
+//   global (gidx != NULL): K = M*k rounds; each takes the best head among the token's
+//         lists (higher score, then lower id: ids grow with the group) and pops it, so
+//         slot r gets the expert of global rank r.  Round r's result is kept by lane
+//         r mod Mp, so the gates are computed once per slot and a token's slots leave
+//         as one contiguous store.
+// Gates are the softmax probabilities over all N experts, e^(l - max) / sum, with the
+// hardware exp2 and reciprocal (a few float32 ulps).
+template <int KMAX, int MPC>  // MPC: the lanes per token when known at compile time, else 0
+__device__ __forceinline__ void choose_lanes(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
+                                             int N, int M, int k, int32_t* __restrict__ idx,
+                                             float* __restrict__ gate, int32_t* __restrict__ gidx,
+                                             float* __restrict__ ggate) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int G = N / M, K = M * k;
+  int Mp = 1;
+  while (Mp < M) Mp <<= 1;
+  if constexpr (MPC > 0) Mp = MPC;
+  const int tpp = 64 / Mp;  // tokens per wave pass
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int g = lane & (Mp - 1), tl = lane / Mp;
+  for (int r0 = wave * tpp; r0 < rows; r0 += nw * tpp) {  // wave-uniform
+    const int r = r0 + tl;
+    const bool tok = r < rows && t0 + r < T;
+    const bool own = tok && g < M;
+    const float* v = lt + (int64_t)(own ? r : 0) * ld + (own ? g * G : 0);
+    const int n = own ? G : 0;
+    float m = -INFINITY;
+    for (int i = 0; i < n; ++i) m = fmaxf(m, v[i]);
+    for (int off = 1; off < Mp; off <<= 1) m = fmaxf(m, partner_f(m, off));
+    const float ml = m * kLog2e;
+    float z = 0.f;
+    for (int i = 0; i < n; ++i) z += __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], kLog2e, -ml));
+    for (int off = 1; off < Mp; off <<= 1) z += partner_f(z, off);
+    const float rz = __builtin_amdgcn_rcpf(z);
+    auto prob = [&](float l) { return __builtin_amdgcn_exp2f(__builtin_fmaf(l, kLog2e, -ml)) * rz; };
+    float bv[KMAX];
+    int bi[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      bv[j] = -INFINITY;
+      bi[j] = -1;
+    }
+    for (int i = 0; i < n; ++i) {
+      const float x = order_key(v[i]);
+      const int e = g * G + i;
+#pragma unroll
+      for (int j = KMAX - 1; j > 0; --j) {
+        const bool up = x > bv[j - 1] || bi[j - 1] < 0;  // x lands above j - 1: entry j - 1 moves to j
+        const bool here = x > bv[j] || bi[j] < 0;
+        bv[j] = up ? bv[j - 1] : (here ? x : bv[j]);
+        bi[j] = up ? bi[j - 1] : (here ? e : bi[j]);
+      }
+      if (x > bv[0] || bi[0] < 0) {
+        bv[0] = x;
+        bi[0] = e;
+      }
+    }
+    const int64_t t = t0 + r;
+    if (idx && own) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          idx[t * K + g * k + j] = bi[j];
+          gate[t * K + g * k + j] = prob(bv[j]);
+        }
+      }
+    }
+    if (gidx) {
+      // round rk = j * Mp + q takes the best head among the token's lists (a lane whose head is
+      // taken shifts its list up) and lane q keeps the result
+      float rv[KMAX];  // K / Mp <= k <= KMAX rounds per lane
+      int ri[KMAX];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        rv[j] = -INFINITY;
+        ri[j] = 0;
+      }
+      auto round = [&](float& wv, int& wi) {
+        wv = bv[0];
+        wi = own && bi[0] >= 0 ? bi[0] : 0x7FFFFFFF;  // no entry: loses every tie against a real one
+        if (!own) wv = -INFINITY;
+        for (int off = 1; off < Mp; off <<= 1) {
+          const float ov = partner_f(wv, off);
+          const int oi = partner_i(wi, off);
+          const bool take = ov > wv || (ov == wv && oi < wi);
+          wv = take ? ov : wv;
+          wi = take ? oi : wi;
+        }
+        const bool pop = own && bi[0] == wi;
+#pragma unroll
+        for (int j = 0; j < KMAX - 1; ++j) {
+          bv[j] = pop ? bv[j + 1] : bv[j];
+          bi[j] = pop ? bi[j + 1] : bi[j];
+        }
+        bv[KMAX - 1] = pop ? -INFINITY : bv[KMAX - 1];
+        bi[KMAX - 1] = pop ? -1 : bi[KMAX - 1];
+      };
+      if constexpr (MPC > 0) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+#pragma unroll
+          for (int q = 0; q < MPC; ++q) {
+            if (j * MPC + q < K) {
+              float wv;
+              int wi;
+              round(wv, wi);
+              if (g == q) {
+                rv[j] = wv;
+                ri[j] = wi;
+              }
+            }
+          }
+        }
+      } else {
+        for (int rk = 0; rk < K; ++rk) {  // K is the same for the whole wave
+          float wv;
+          int wi;
+          round(wv, wi);
+          const int slot = rk / Mp;
+          if (g == (rk & (Mp - 1))) {
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+              if (j == slot) {
+                rv[j] = wv;
+                ri[j] = wi;
+              }
+            }
+          }
+        }
+      }
+      if (tok) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          const int rk = j * Mp + g;
+          if (rk < K) {
+            gidx[t * K + rk] = ri[j];
+            ggate[t * K + rk] = prob(rv[j]);
+          }
+        }
+      }
     }
   }
+}
+
+// Groups of exactly 8 experts, at most 8 groups (64 experts in 8 groups: the Pangu Pro shape).  Lane (tl, g)
+// holds its group's 8 scores in registers and sorts them completely with a 19-comparator
+// network (Knuth's for 8 inputs), comparing (score descending, expert id ascending): ids are
+// distinct, so the order is total and the sorted list unique.  The MoGE choice is its first
+// k entries; the global top-K merges the token's sorted lists head by head as choose_lanes
+// does, a lane shifting its list up when its head is taken.  Same results as choose_lanes.
+constexpr int kListG8 = 64;  // the host's code for this form
+template <int MP>  // lanes per token: M rounded up to a power of two
+__device__ __forceinline__ void choose_g8(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
+                                          int M, int k, int32_t* __restrict__ idx, float* __restrict__ gate,
+                                          int32_t* __restrict__ gidx, float* __restrict__ ggate) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int tpp = 64 / MP;  // tokens per wave pass
+  const int K = M * k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int g = lane & (MP - 1), tl = lane / MP;
+  for (int r0 = wave * tpp; r0 < rows; r0 += nw * tpp) {  // wave-uniform
+    const int r = r0 + tl;
+    const bool tok = r < rows && t0 + r < T;
+    const bool own = tok && g < M;
+    const float* v = lt + (int64_t)(own ? r : 0) * ld + (own ? g * 8 : 0);
+    float key[8];
+    int id[8];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = own ? v[i] : -INFINITY;
+      m = fmaxf(m, x);
+      key[i] = x;
+    }
+#pragma unroll
+    for (int off = 1; off < MP; off <<= 1) m = fmaxf(m, partner_f(m, off));
+    const float ml = m * kLog2e;
+    float z = 0.f;
+    if (own) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z += __builtin_amdgcn_exp2f(__builtin_fmaf(key[i], kLog2e, -ml));
+    }
+#pragma unroll
+    for (int off = 1; off < MP; off <<= 1) z += partner_f(z, off);
+    const float rz = __builtin_amdgcn_rcpf(z);
+    auto prob = [&](float l) { return __builtin_amdgcn_exp2f(__builtin_fmaf(l, kLog2e, -ml)) * rz; };
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      key[i] = order_key(key[i]);
+      id[i] = own ? g * 8 + i : 0x7FFFFFFF;
+    }
+    auto ce = [&](int a, int b) {  // a before b: higher score, then lower id
+      const bool keep = key[a] > key[b] || (key[a] == key[b] && id[a] < id[b]);
+      const float ka = key[a], kb = key[b];
+      const int ia = id[a], ib = id[b];
+      key[a] = keep ? ka : kb;
+      key[b] = keep ? kb : ka;
+      id[a] = keep ? ia : ib;
+      id[b] = keep ? ib : ia;
+    };
+    ce(0, 2); ce(1, 3); ce(4, 6); ce(5, 7);
+    ce(0, 4); ce(1, 5); ce(2, 6); ce(3, 7);
+    ce(0, 1); ce(2, 3); ce(4, 5); ce(6, 7);
+    ce(2, 4); ce(3, 5);
+    ce(1, 4); ce(3, 6);
+    ce(1, 2); ce(3, 4); ce(5, 6);
+    const int64_t t = t0 + r;
+    if (idx && own) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < k) {
+          idx[t * K + g * k + j] = id[j];
+          gate[t * K + g * k + j] = prob(key[j]);
+        }
+      }
+    }
+    if (gidx) {
+      // round rk = j * MP + q takes the best head among the token's lists; lane q keeps it
+      float rv[8];
+      int ri[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        rv[j] = -INFINITY;
+        ri[j] = 0;
+#pragma unroll
+        for (int q = 0; q < MP; ++q) {
+          if (j * MP + q < K) {  // K = M k <= 8 MP: at most 8 rounds per lane
+            float wv = key[0];
+            int wi = id[0];  // an exhausted or foreign lane offers (-inf, INT_MAX): it loses every tie
+#pragma unroll
+            for (int off = 1; off < MP; off <<= 1) {
+              const float ov = partner_f(wv, off);
+              const int oi = partner_i(wi, off);
+              const bool take = ov > wv || (ov == wv && oi < wi);
+              wv = take ? ov : wv;
+              wi = take ? oi : wi;
+            }
+            const bool pop = id[0] == wi;  // this lane's head was taken: the list moves up
+#pragma unroll
+            for (int i = 0; i < 7; ++i) {
+              key[i] = pop ? key[i + 1] : key[i];
+              id[i] = pop ? id[i + 1] : id[i];
+            }
+            key[7] = pop ? -INFINITY : key[7];
+            id[7] = pop ? 0x7FFFFFFF : id[7];
+            if (g == q) {
+              rv[j] = wv;
+              ri[j] = wi;
+            }
+          }
+        }
+      }
+      if (tok) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int rk = j * MP + g;
+          if (rk < K) {
+            gidx[t * K + rk] = ri[j];
+            ggate[t * K + rk] = prob(rv[j]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// The choices of the older per-mode forms, for shapes past the lists' limits: lane-parallel
+// rank rounds per (token, group) or one wave per token.
+__device__ __forceinline__ void choose_fallback(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
+                                                int N, int n_groups, int k, int32_t* __restrict__ idx,
+                                                float* __restrict__ gate) {
   if (lane_parallel_choice(N, n_groups, k)) {
     if (N == 8 * n_groups) select_tile_g<8>(lt, ld, rows, t0, T, n_groups, k, idx, gate);
     else select_tile(lt, ld, rows, t0, T, N, n_groups, k, idx, gate);
@@ -263,31 +565,73 @@ __device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int 
   }
 }
 
+// Writes the LDS score tile [rows][ld] to logits_out (if any) and makes the choices: MoGE
+// into idx/gate when idx is set, the global top-K into gidx/ggate when gidx is set.  KL is
+// lane_list_len of the call (the host picks the kernel instance): the lists' length, or 0
+// for the fallback forms.  (all threads of the block call it)
+template <int KL>
+__device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
+                                              int N, int M, int k, float* __restrict__ logits_out,
+                                              int32_t* __restrict__ idx, float* __restrict__ gate,
+                                              int32_t* __restrict__ gidx, float* __restrict__ ggate) {
+  // The scores go out with the non-temporal hint: every tile writes them at the same
+  // time at the end of the kernel, and streamed past the L2 they no longer wait there
+  // for the kernel's final write-back (the route kernel at 65536 tokens x 4096 x 64
+  // experts was 4% faster).
+  if (logits_out) {
+    for (int i = threadIdx.x; i < rows * N; i += blockDim.x) {
+      const int r = i / N, c = i - r * N;
+      if (t0 + r < T) __builtin_nontemporal_store(lt[r * ld + c], logits_out + (t0 + r) * N + c);
+    }
+  }
+  if constexpr (KL == kListG8) {
+    if (M <= 1) choose_g8<1>(lt, ld, rows, t0, T, M, k, idx, gate, gidx, ggate);
+    else if (M <= 2) choose_g8<2>(lt, ld, rows, t0, T, M, k, idx, gate, gidx, ggate);
+    else if (M <= 4) choose_g8<4>(lt, ld, rows, t0, T, M, k, idx, gate, gidx, ggate);
+    else choose_g8<8>(lt, ld, rows, t0, T, M, k, idx, gate, gidx, ggate);
+  } else if constexpr (KL > 0) {
+    if (M == 8) choose_lanes<KL, 8>(lt, ld, rows, t0, T, N, M, k, idx, gate, gidx, ggate);
+    else choose_lanes<KL, 0>(lt, ld, rows, t0, T, N, M, k, idx, gate, gidx, ggate);
+  } else {
+    if (idx) choose_fallback(lt, ld, rows, t0, T, N, M, k, idx, gate);
+    if (gidx) choose_fallback(lt, ld, rows, t0, T, N, 1, M * k, gidx, ggate);
+  }
+}
+
+// Calls f(std::integral_constant<int, KL>{}) with KL = the list length the host picked
+// (one kernel instance per length).
+template <typename Fn>
+static moge_status_t with_list_len(int kl, Fn&& f) {
+  switch (kl) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    case 16: return f(std::integral_constant<int, 16>{});
+    case 32: return f(std::integral_constant<int, 32>{});
+    case kListG8: return f(std::integral_constant<int, kListG8>{});
+    default: return f(std::integral_constant<int, 0>{});
+  }
+}
+
 // ----------------------------------------------------------------------------
-// bf16 scores, many tokens.  A workgroup of 4 waves owns TM tokens x NP experts
-// (NP = N rounded up to 64, 128 or 256 and TM = 8192 / NP, so every wave owns one
+// bf16 scores, many tokens, N <= 128.  A workgroup of 4 waves owns TM tokens x NP experts
+// (NP = N rounded up to 64 or 128 and TM = 8192 / NP, so every wave owns one
 // 32-token x 64-expert block: two 32x32 accumulators).  The token rows and the
 // router rows of each 32-element step go from global memory straight into an
 // S-stage LDS ring (global_load_lds_dwordx4, 16 rows of 64 bytes per instruction,
 // XOR-swizzled rows), S - 1 steps ahead, so x streams from HBM with several steps
 // of loads in flight per workgroup and no staging registers; x is read exactly
 // once.  One barrier per step.  The epilogue keeps the TM x NP score tile in LDS
-// for the softmax and the per-group choice.
-//
-// PARTS > 1 (N > 128, scores stored): the experts are split in PARTS slices of NP;
-// workgroup b computes slice b % PARTS of token tile b / PARTS and only writes its
-// scores, and a second pass (route_select_kernel) makes the choice.  Workgroup b
-// runs on XCD b % 8, so each XCD needs only its slice of the router matrix (1-2 MB
-// at N = 256, d = 7680), which then stays in that XCD's 4 MB L2 instead of being
-// fetched from the last-level cache by every workgroup, and the tile can take more
-// tokens, so more of each step's loads are token rows streaming from HBM.
-template <int TM, int NP, int S, int WV, int PARTS>
+// for the softmax and the choices.
+template <int TM, int NP, int S, int WV, int KL>
 __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, int N, int n_groups, int k,
                                                         const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ w,
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ logits_out, int32_t* __restrict__ idx,
-                                                        float* __restrict__ gate) {
+                                                        float* __restrict__ gate, int32_t* __restrict__ gidx,
+                                                        float* __restrict__ ggate) {
   constexpr int ROWS = TM + NP;      // stage rows of 64 bytes: tokens, then experts
   constexpr int NI = ROWS / 16;      // load instructions per step
   constexpr int NJ = (NI + WV - 1) / WV;  // per wave, at most
@@ -300,8 +644,7 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tb = wave % TB, es = wave / TB;
-  const int64_t t0 = (int64_t)(blockIdx.x / PARTS) * TM;
-  const int e0 = (int)(blockIdx.x % PARTS) * NP;  // first expert of this workgroup
+  const int64_t t0 = (int64_t)blockIdx.x * TM;
   const int nkf = d / 32;                        // full steps; a ragged tail follows the loop
   // token tiles start at different steps (and wrap around), so the workgroups do not all
   // read the same column range of their rows at once: each tile walks 64-byte pieces of
@@ -322,7 +665,7 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
       if (t > T - 1) t = T - 1;
       src[j] = x + t * d + c * 8;
     } else {
-      int e = e0 + srow - TM;
+      int e = srow - TM;
       if (e > N - 1) e = N - 1;
       src[j] = w + (int64_t)e * d + c * 8;
     }
@@ -415,19 +758,6 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
     __syncthreads();
   }
 
-  if (PARTS > 1) {  // scores of this slice only, straight to logits (the choice is a second pass)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int col = e0 + es * 64 + cb * 32 + (lane & 31);
-      const float b = (bias && col < N) ? bias[col] : 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = t0 + tb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (col < N && row < T) logits_out[row * N + col] = acc[cb][r] + b;
-      }
-    }
-    return;
-  }
   // scores -> LDS tile [TM][NP + 1] (odd row stride); padded experts get -inf
   constexpr int LD = NP + 1;
   float* lt = reinterpret_cast<float*>(lds);
@@ -442,24 +772,233 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
     }
   }
   __syncthreads();
-  tile_epilogue(lt, LD, TM, t0, T, N, n_groups, k, logits_out, idx, gate);
+  tile_epilogue<KL>(lt, LD, TM, t0, T, N, n_groups, k, logits_out, idx, gate, gidx, ggate);
 }
 
-template <int TM, int NP, int S, int WV, int PARTS = 1>
-static moge_status_t launch_route_dma(const moge_shape_t& s, int n_groups, int k, const void* x, const void* w,
-                                      const float* bias, float* logits, int32_t* idx, float* gate,
+template <int TM, int NP, int S, int WV>
+static moge_status_t launch_route_dma(const moge_shape_t& s, int kl, const void* x, const void* w, const float* bias,
+                                      float* logits, int32_t* idx, float* gate, int32_t* gidx, float* ggate,
                                       hipStream_t stream) {
-  constexpr size_t ring = (size_t)S * (TM + NP) * 64;
-  constexpr size_t tile = (size_t)TM * (NP + 1) * 4;
-  constexpr size_t lds = ring > tile ? ring : tile;
-  const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV, PARTS>);
-  moge_status_t st = raise_dynamic_lds(kern, lds, "route_dma_kernel");
-  if (st != MOGE_OK) return st;
-  const int64_t grid = ((int64_t)s.T + TM - 1) / TM * PARTS;
-  hipLaunchKernelGGL((route_dma_kernel<TM, NP, S, WV, PARTS>), dim3((unsigned)grid), dim3(64 * WV), lds, stream,
-                     (int64_t)s.T, s.d, s.N, n_groups, k, static_cast<const uint16_t*>(x),
-                     static_cast<const uint16_t*>(w), bias, logits, idx, gate);
-  return check_launch("route_dma_kernel");
+  return with_list_len(kl, [&](auto klc) {
+    constexpr int KL = decltype(klc)::value;
+    constexpr size_t ring = (size_t)S * (TM + NP) * 64;
+    constexpr size_t tile = (size_t)TM * (NP + 1) * 4;
+    constexpr size_t lds = ring > tile ? ring : tile;
+    const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV, KL>);
+    moge_status_t st = raise_dynamic_lds(kern, lds, "route_dma_kernel");
+    if (st != MOGE_OK) return st;
+    const int64_t grid = ((int64_t)s.T + TM - 1) / TM;
+    hipLaunchKernelGGL((route_dma_kernel<TM, NP, S, WV, KL>), dim3((unsigned)grid), dim3(64 * WV), lds, stream,
+                       (int64_t)s.T, s.d, s.N, s.M, s.k_per_group, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(w), bias, logits, idx, gate, gidx, ggate);
+    return check_launch("route_dma_kernel");
+  });
+}
+
+// ----------------------------------------------------------------------------
+// bf16 scores, 128 < N <= 256: split over the hidden dimension.  Workgroup b computes
+// slice b % S of the reduction (its steps k0 .. k1 - 1 of d / 32) for the 128-token x
+// 256-expert tile b / S, and stores the float32 partial sums to part[slice][t][e].
+// 8 waves; wave w owns tokens (w / 4) * 64 .. + 64 and experts (w % 4) * 64 .. + 64 as
+// 2 x 2 accumulators of 32 x 32 (v_mfma_f32_32x32x16_bf16).  Each step's 128 token rows
+// and 256 router rows (64 bytes of each) go straight into a 6-stage LDS ring (24 loads of
+// 16 rows per step, 3 per wave), 5 steps ahead, one barrier per step.  Workgroup b runs on
+// XCD b % 8 and S divides 8 (or is 1), so an XCD reads only its own slices of the router
+// matrix (at most 983 KB of a 256 x 7680 matrix), which stay in its L2, while x streams
+// from HBM once.  The last slice also takes the ragged tail of d (d % 32 columns).
+constexpr int kPartTM = 128, kPartNP = 256, kPartStages = 6;
+__global__ __launch_bounds__(512) void route_part_kernel(int64_t T, int d, int N, int S,
+                                                         const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ w,
+                                                         float* __restrict__ part) {
+  constexpr int TM = kPartTM, NP = kPartNP, SG = kPartStages;
+  constexpr int ROWS = TM + NP;       // 384 stage rows of 64 bytes
+  constexpr int STAGE = ROWS * 64;    // 24 KiB
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 2, wc = wave & 3;
+  const int slice = (int)(blockIdx.x % S);
+  const int64_t t0 = (int64_t)(blockIdx.x / S) * TM;
+  const int nkf = d / 32;
+  const int k0 = (int)((int64_t)nkf * slice / S), k1 = (int)((int64_t)nkf * (slice + 1) / S);
+  const int nks = k1 - k0;
+  // token tiles start their slice at staggered steps (as the one-pass kernel does)
+  const int krot = nks > 0 ? (int)(((t0 / TM) * 37) % nks) : 0;
+  // load j of this wave moves stage rows 16 i .. 16 i + 15, i = wave + 8 j: j = 0 token
+  // rows, j = 1, 2 router rows
+  const uint16_t* src[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int srow = 16 * (wave + 8 * j) + (lane >> 2);
+    const int c = (lane & 3) ^ lds_swz(srow);
+    if (srow < TM) {
+      int64_t t = t0 + srow;
+      if (t > T - 1) t = T - 1;
+      src[j] = x + t * d + c * 8;
+    } else {
+      int e = srow - TM;
+      if (e > N - 1) e = N - 1;
+      src[j] = w + (int64_t)e * d + c * 8;
+    }
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int ks) {
+    if (ks >= nks) return;
+    const uint32_t st = lds0 + (uint32_t)((ks % SG) * STAGE);
+    const int kr = ks + krot < nks ? ks + krot : ks + krot - nks;
+    const int kk = k0 + kr;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dma_16x64(src[j] + kk * 32, st + (uint32_t)(16 * (wave + 8 * j) * 64));
+  };
+  const int kc = lane >> 5;
+  int arow[2], brow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    arow[i] = wr * 64 + i * 32 + (lane & 31);
+    brow[i] = TM + wc * 64 + i * 32 + (lane & 31);
+  }
+  auto frag = [&](int stage, int kk, bf16x8_t (&a)[2], bf16x8_t (&b)[2]) {
+    const char* st = lds + stage * STAGE;
+    const int c = kk * 2 + kc;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      a[i] = __builtin_bit_cast(bf16x8_t,
+                                *reinterpret_cast<const u32x4_t*>(st + arow[i] * 64 + ((c ^ lds_swz(arow[i])) << 4)));
+      b[i] = __builtin_bit_cast(bf16x8_t,
+                                *reinterpret_cast<const u32x4_t*>(st + brow[i] * 64 + ((c ^ lds_swz(brow[i])) << 4)));
+    }
+  };
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mfma = [&](const bf16x8_t (&a)[2], const bf16x8_t (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+#pragma unroll
+  for (int s = 0; s < SG - 1; ++s) issue(s);
+  // steps 0 and 1 landed (3 loads per step per wave; at most SG - 3 later steps in flight):
+  // the first iteration reads step 0 and, ahead, the first half of step 1
+  if (nks >= SG - 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm((SG - 3) * 3));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  bf16x8_t a0[2], b0[2], a1[2], b1[2];
+  if (nks > 0) frag(0, 0, a0, b0);
+  for (int ks = 0; ks < nks; ++ks) {
+    issue(ks + SG - 1);  // into stage (ks - 1) % SG, last read before the previous barrier
+    frag(ks % SG, 1, a1, b1);
+    mfma(a0, b0);
+    frag((ks + 1) % SG, 0, a0, b0);  // read-ahead (unused after the last step)
+    mfma(a1, b1);
+    // step ks + 2 landed (once the tail issues no more, everything is waited for)
+    if (ks + SG - 1 < nks) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((SG - 3) * 3));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+    __syncthreads();
+  }
+  if (slice == S - 1 && (d % 32)) {
+    // ragged tail: one step through registers, columns at or past d are zero
+    const int kt = nkf * 32;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int srow = 16 * (wave + 8 * j) + (lane >> 2);
+      const int c = (lane & 3) ^ lds_swz(srow);
+      const u32x4_t v = (kt + c * 8 < d) ? *reinterpret_cast<const u32x4_t*>(src[j] + kt) : zero;
+      *reinterpret_cast<u32x4_t*>(lds + 16 * (wave + 8 * j) * 64 + lane * 16) = v;
+    }
+    __syncthreads();
+    frag(0, 0, a0, b0);
+    frag(0, 1, a1, b1);
+    mfma(a0, b0);
+    mfma(a1, b1);
+  }
+  float* dst = part + (int64_t)slice * T * N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wc * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = t0 + wr * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (col < N && row < T) dst[row * N + col] = acc[i][j][r];
+      }
+    }
+}
+
+// Slices per token tile for the split kernel: enough that the token tiles times the slices
+// fill the 256 CUs, at most 4, and a divisor of 8 so each XCD holds whole slices.
+__host__ __forceinline__ int route_slices(int64_t T) {
+  const int64_t tiles = (T + kPartTM - 1) / kPartTM;
+  int S = 1;
+  while (S < 4 && tiles * S < 256) S <<= 1;
+  return S;
+}
+
+// The split kernel's partial sums -> scores -> the choices.  32 tokens per workgroup:
+// the S slices of each score are added in slice order (bit-identical results run to run),
+// plus the bias, into an LDS tile [32][N + 1]; then the common epilogue.
+constexpr int kReduceTokens = 32;
+template <int KL>
+__global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int M, int k, int S,
+                                                           const float* __restrict__ part,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ logits_out, int32_t* __restrict__ idx,
+                                                           float* __restrict__ gate, int32_t* __restrict__ gidx,
+                                                           float* __restrict__ ggate) {
+  __shared__ float lt[kReduceTokens * (kMaxExperts + 1)];
+  const int ld = N + 1;
+  const int64_t t0 = (int64_t)blockIdx.x * kReduceTokens;
+  const int64_t nrows = (T - t0) < kReduceTokens ? (T - t0) : kReduceTokens;
+  const int total = (int)nrows * N;
+  const int64_t plane = T * N;
+  const float* src = part + t0 * N;  // the tile's rows are contiguous in every slice
+  if ((N & 3) == 0) {
+    // 16-byte loads, the four slices of 4 chunks all issued before any is added
+    for (int i0 = threadIdx.x * 4; i0 < total; i0 += 256 * 4 * 4) {
+      f32x4_t v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 1024;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          if (i < total && p < S) v[u][p] = *reinterpret_cast<const f32x4_t*>(src + p * plane + i);
+          else v[u][p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 1024;
+        if (i < total) {
+          const int r = i / N, c = i - r * N;  // c % 4 == 0: the 4 values share a row
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float a = v[u][0][q];
+#pragma unroll
+            for (int p = 1; p < 4; ++p)
+              if (p < S) a += v[u][p][q];
+            lt[r * ld + c + q] = a + (bias ? bias[c + q] : 0.f);
+          }
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < total; i += 256) {
+      float a = src[i];
+      for (int p = 1; p < S; ++p) a += src[p * plane + i];
+      const int r = i / N, c = i - r * N;
+      lt[r * ld + c] = a + (bias ? bias[c] : 0.f);
+    }
+  }
+  __syncthreads();
+  tile_epilogue<KL>(lt, ld, (int)nrows, t0, T, N, M, k, logits_out, idx, gate, gidx, ggate);
 }
 
 // ----------------------------------------------------------------------------
@@ -468,13 +1007,15 @@ static moge_status_t launch_route_dma(const moge_shape_t& s, int n_groups, int k
 // small batch still spreads over many waves.  Operands are read straight from
 // global memory in MFMA layout; the partial sums meet in LDS and are added in a
 // fixed order (deterministic).
-template <int WC>
+template <int WC, int KL>
 __global__ __launch_bounds__(256) void route_mfma_splitk_kernel(int64_t T, int d, int N, int n_groups, int k,
                                                                 const uint16_t* __restrict__ x,
                                                                 const uint16_t* __restrict__ w,
                                                                 const float* __restrict__ bias,
                                                                 float* __restrict__ logits_out,
-                                                                int32_t* __restrict__ idx, float* __restrict__ gate) {
+                                                                int32_t* __restrict__ idx, float* __restrict__ gate,
+                                                                int32_t* __restrict__ gidx,
+                                                                float* __restrict__ ggate) {
   constexpr int KS = 4 / WC;
   constexpr int NP = 64 * WC;
   constexpr int TM = 32;
@@ -535,18 +1076,20 @@ __global__ __launch_bounds__(256) void route_mfma_splitk_kernel(int64_t T, int d
     part[i] = col < N ? v + (bias ? bias[col] : 0.f) : -INFINITY;
   }
   __syncthreads();
-  tile_epilogue(part, NP, TM, t0, T, N, n_groups, k, logits_out, idx, gate);
+  tile_epilogue<KL>(part, NP, TM, t0, T, N, n_groups, k, logits_out, idx, gate, gidx, ggate);
 }
 
 // ----------------------------------------------------------------------------
 // float32 scores on the vector ALUs (small shapes).  16 tokens per workgroup.
 constexpr int kF32Tokens = 16;
+template <int KL>
 __global__ __launch_bounds__(256) void route_f32_kernel(int64_t T, int d, int N, int n_groups, int k,
                                                         const float* __restrict__ x, const float* __restrict__ w,
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ logits_out, int32_t* __restrict__ idx,
-                                                        float* __restrict__ gate) {
-  __shared__ float lt[kF32Tokens * kMaxExperts];
+                                                        float* __restrict__ gate, int32_t* __restrict__ gidx,
+                                                        float* __restrict__ ggate) {
+  __shared__ float lt[kF32Tokens * (kMaxExperts + 1)];
   const int64_t t0 = (int64_t)blockIdx.x * kF32Tokens;
   for (int i = threadIdx.x; i < kF32Tokens * N; i += blockDim.x) {
     const int r = i / N, e = i - r * N;
@@ -557,61 +1100,25 @@ __global__ __launch_bounds__(256) void route_f32_kernel(int64_t T, int d, int N,
     float acc = 0.f;
     for (int c = 0; c < d; ++c) acc = fmaf(xr[c], wr[c], acc);
     if (bias) acc += bias[e];
-    lt[r * N + e] = acc;
+    lt[r * (N + 1) + e] = acc;
   }
   __syncthreads();
-  tile_epilogue(lt, N, kF32Tokens, t0, T, N, n_groups, k, logits_out, idx, gate);
+  tile_epilogue<KL>(lt, N + 1, kF32Tokens, t0, T, N, n_groups, k, logits_out, idx, gate, gidx, ggate);
 }
 
 // ----------------------------------------------------------------------------
-// Caller-supplied scores.  Lane-parallel choice: 64 tokens per workgroup, staged in
-// LDS with an odd row stride.  Wide groups: one token per wave, 4 per workgroup
-// (the choice is a chain of wave-wide reductions; many resident waves hide it).
+// Caller-supplied scores: 64 tokens per workgroup, their rows staged in LDS (16-byte
+// loads when N % 4 == 0; odd row stride), then the common epilogue.
 constexpr int kSelTokens = 64;
-constexpr int kSelTokensWide = 4;
-template <bool LANES>
-__global__ __launch_bounds__(256) void route_select_kernel(int64_t T, int N, int n_groups, int k,
+template <int KL>
+__global__ __launch_bounds__(256) void route_select_kernel(int64_t T, int N, int M, int k,
                                                            const float* __restrict__ logits,
-                                                           int32_t* __restrict__ idx, float* __restrict__ gate) {
-  extern __shared__ float lt[];
-  if (LANES) {  // [kSelTokens][N + 1]
-    const int ld = N + 1;
-    const int64_t t0 = (int64_t)blockIdx.x * kSelTokens;
-    for (int i = threadIdx.x; i < kSelTokens * N; i += blockDim.x) {
-      const int r = i / N, c = i - r * N;
-      lt[r * ld + c] = (t0 + r < T) ? logits[(t0 + r) * N + c] : 0.f;
-    }
-    __syncthreads();
-    select_tile(lt, ld, kSelTokens, t0, T, N, n_groups, k, idx, gate);
-  } else {      // [kSelTokensWide][N]
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kSelTokensWide + wave;
-    if (t >= T) return;  // wave-uniform; no barrier below
-    float* row = lt + wave * N;
-    for (int e = lane; e < N; e += 64) row[e] = logits[t * N + e];
-    __builtin_amdgcn_wave_barrier();  // the row is written and read by this wave only (LDS is in order per wave)
-    select_token(row, N, n_groups, k, t, idx, gate);
-  }
-}
-
-// ----------------------------------------------------------------------------
-// Caller-supplied scores, k <= 32 per group: one lane per token, 64 tokens per
-// workgroup.  All four waves stage the 64 score rows in LDS (16-byte loads; odd row
-// stride, so the row reads are conflict-free); then wave 0 chooses, each lane
-// walking its own row: the maximum, the
-// softmax denominator, and for every group a sorted register list of the KMAX best
-// of that group (score desc, expert asc: a later equal score never displaces an
-// earlier one), kept by a branch-free insertion network.  No cross-lane reduction
-// at all, so a wave chooses for 64 tokens at once.
-constexpr int kLaneTokens = 64;
-template <int KMAX>
-__global__ __launch_bounds__(256) void route_select_lane_kernel(int64_t T, int N, int n_groups, int k,
-                                                               const float* __restrict__ logits,
-                                                               int32_t* __restrict__ idx, float* __restrict__ gate) {
-  extern __shared__ float lt[];  // [kLaneTokens][N + 1]
+                                                           int32_t* __restrict__ idx, float* __restrict__ gate,
+                                                           int32_t* __restrict__ gidx, float* __restrict__ ggate) {
+  extern __shared__ float lt[];  // [kSelTokens][N + 1]
   const int ld = N + 1;
-  const int64_t t0 = (int64_t)blockIdx.x * kLaneTokens;
-  const int64_t nrows = (T - t0) < kLaneTokens ? (T - t0) : kLaneTokens;
+  const int64_t t0 = (int64_t)blockIdx.x * kSelTokens;
+  const int64_t nrows = (T - t0) < kSelTokens ? (T - t0) : kSelTokens;
   const float* src = logits + t0 * N;  // the tile's rows are contiguous
   const int total = (int)nrows * N;
   if ((N & 3) == 0) {  // 16-byte loads (rows start on 16-byte boundaries)
@@ -630,165 +1137,123 @@ __global__ __launch_bounds__(256) void route_select_lane_kernel(int64_t T, int N
     }
   }
   __syncthreads();
-  if (threadIdx.x >= 64) return;  // wave 0 chooses
-  const int lane = threadIdx.x;
-  const int64_t t = t0 + lane;
-  if (t >= T) return;
-  const float* row = lt + lane * ld;
-  // pass 1: the maximum; pass 2: the denominator (8 interleaved partial sums, then a tree)
-  float mp[8] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY, -INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  int e8 = 0;
-  for (; e8 + 8 <= N; e8 += 8)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) mp[j] = fmaxf(mp[j], row[e8 + j]);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (e8 + j < N) mp[j] = fmaxf(mp[j], row[e8 + j]);
-  const float m = fmaxf(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])), fmaxf(fmaxf(mp[4], mp[5]), fmaxf(mp[6], mp[7])));
-  float zp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (e8 = 0; e8 + 8 <= N; e8 += 8)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) zp[j] += expf(row[e8 + j] - m);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (e8 + j < N) zp[j] += expf(row[e8 + j] - m);
-  const float z = ((zp[0] + zp[1]) + (zp[2] + zp[3])) + ((zp[4] + zp[5]) + (zp[6] + zp[7]));
-  // pass 3, per group: its KMAX best, in expert order (8 scores read ahead at a time)
-  const int G = N / n_groups, K = n_groups * k;
-  float bv[KMAX];
-  int bi[KMAX];
-  // Entries start as empty places (bi = -1) that any expert fills; experts arrive in
-  // increasing id order, so a later equal key never displaces an earlier expert.
-  auto insert = [&](float v, int e) {
-    // position of v: below every entry >= v; entries below it move down one place
-#pragma unroll
-    for (int j = KMAX - 1; j > 0; --j) {
-      const bool up = v > bv[j - 1] || bi[j - 1] < 0;  // v lands above j - 1: entry j - 1 moves to j
-      const bool here = v > bv[j] || bi[j] < 0;
-      bv[j] = up ? bv[j - 1] : (here ? v : bv[j]);
-      bi[j] = up ? bi[j - 1] : (here ? e : bi[j]);
-    }
-    if (v > bv[0] || bi[0] < 0) {
-      bv[0] = v;
-      bi[0] = e;
-    }
-  };
-  for (int g = 0; g < n_groups; ++g) {
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      bv[j] = -INFINITY;
-      bi[j] = -1;
-    }
-    const int ge = (g + 1) * G;
-    for (e8 = g * G; e8 + 8 <= ge; e8 += 8) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = order_key(row[e8 + j]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) insert(v[j], e8 + j);
-    }
-    for (; e8 < ge; ++e8) insert(order_key(row[e8]), e8);
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      if (r < k) {
-        idx[t * K + g * k + r] = bi[r];
-        gate[t * K + g * k + r] = expf(bv[r] - m) / z;
-      }
-    }
-  }
+  tile_epilogue<KL>(lt, ld, (int)nrows, t0, T, N, M, k, nullptr, idx, gate, gidx, ggate);
 }
 
 }  // namespace moge
 
 using namespace moge;
 
-extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, const void* x, const void* w_router,
-                                    const float* bias, float* logits, int32_t* idx, float* gate,
-                                    hipStream_t stream) {
+// Bytes of workspace the scores need: the split kernel's partial sums for bf16 shapes with
+// more than 128 experts (x given), else none.
+size_t moge::route_workspace_bytes(const moge_shape_t& s) {
+  if (s.dtype != MOGE_BF16 || s.N <= 128) return 0;
+  return (size_t)route_slices(s.T) * (size_t)s.T * (size_t)s.N * sizeof(float);
+}
+
+// Scores (from x, or the caller's) and the choices: MoGE into idx/gate when idx is set, the
+// global top-K into gidx/ggate when gidx is set.
+static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const void* w_router, const float* bias,
+                                float* logits, int32_t* idx, float* gate, int32_t* gidx, float* ggate, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
   moge_status_t st = validate_shape(shape);
   if (st != MOGE_OK) return st;
   const moge_shape_t& s = *shape;
-  if (mode != MOGE_ROUTE_GROUPED && mode != MOGE_ROUTE_GLOBAL) return fail(MOGE_ERR_ARG, "unknown route mode");
-  if (!idx || !gate) return fail(MOGE_ERR_NULL, "idx and gate are required");
   if (!x && !logits) return fail(MOGE_ERR_NULL, "either x (with w_router) or input logits is required");
   if (x && !w_router) return fail(MOGE_ERR_NULL, "w_router is required when x is given");
   if (!x && bias) return fail(MOGE_ERR_ARG, "bias must be NULL when logits are supplied (they include it)");
-  const int n_groups = mode == MOGE_ROUTE_GROUPED ? s.M : 1;
-  const int k = mode == MOGE_ROUTE_GROUPED ? s.k_per_group : s.M * s.k_per_group;
+  const size_t need = x ? route_workspace_bytes(s) : 0;
+  if (need && (!ws || ws_bytes < need)) return fail(MOGE_ERR_WORKSPACE, "route workspace missing or too small");
 
-  // the choice from stored scores (caller scores, or the split scores pass below)
-  auto select = [&]() -> moge_status_t {
-    if (k <= 32) {  // one lane per token
-      const int64_t grid = ((int64_t)s.T + kLaneTokens - 1) / kLaneTokens;
-      const size_t lds = sizeof(float) * kLaneTokens * (size_t)(s.N + 1);
-#define MOGE_SEL(KM)                                                                                              \
-  do {                                                                                                            \
-    if (lds > 64 * 1024) {                                                                                        \
-      st = raise_dynamic_lds(reinterpret_cast<const void*>(route_select_lane_kernel<KM>), lds,                     \
-                             "route_select_lane_kernel");                                                         \
-      if (st != MOGE_OK) return st;                                                                               \
-    }                                                                                                             \
-    hipLaunchKernelGGL(route_select_lane_kernel<KM>, dim3((unsigned)grid), dim3(256), lds, stream, (int64_t)s.T, \
-                       s.N, n_groups, k, logits, idx, gate);                                                      \
-  } while (0)
-      if (k <= 1) MOGE_SEL(1);
-      else if (k <= 2) MOGE_SEL(2);
-      else if (k <= 4) MOGE_SEL(4);
-      else if (k <= 8) MOGE_SEL(8);
-      else if (k <= 16) MOGE_SEL(16);
-      else MOGE_SEL(32);
-#undef MOGE_SEL
-      return check_launch("route_select_lane_kernel");
-    }
-    if (lane_parallel_choice(s.N, n_groups, k)) {
+  const int kl = (s.N == 8 * s.M && s.M <= 8) ? kListG8 : lane_list_len(s.N, s.M, s.k_per_group, gidx != nullptr);
+  if (!x) {
+    st = with_list_len(kl, [&](auto klc) {
+      constexpr int KL = decltype(klc)::value;
       const int64_t grid = ((int64_t)s.T + kSelTokens - 1) / kSelTokens;
       const size_t lds = sizeof(float) * kSelTokens * (size_t)(s.N + 1);
       if (lds > 64 * 1024) {
-        st = raise_dynamic_lds(reinterpret_cast<const void*>(route_select_kernel<true>), lds, "route_select_kernel");
-        if (st != MOGE_OK) return st;
+        moge_status_t r = raise_dynamic_lds(reinterpret_cast<const void*>(route_select_kernel<KL>), lds,
+                                            "route_select_kernel");
+        if (r != MOGE_OK) return r;
       }
-      hipLaunchKernelGGL(route_select_kernel<true>, dim3((unsigned)grid), dim3(256), lds, stream, (int64_t)s.T, s.N,
-                         n_groups, k, logits, idx, gate);
-    } else {
-      const int64_t grid = ((int64_t)s.T + kSelTokensWide - 1) / kSelTokensWide;
-      hipLaunchKernelGGL(route_select_kernel<false>, dim3((unsigned)grid), dim3(256),
-                         sizeof(float) * kSelTokensWide * (size_t)s.N, stream, (int64_t)s.T, s.N, n_groups, k, logits,
-                         idx, gate);
-    }
-    return check_launch("route_select_kernel");
-  };
-
-  if (!x) {
-    st = select();
+      hipLaunchKernelGGL(route_select_kernel<KL>, dim3((unsigned)grid), dim3(256), lds, stream, (int64_t)s.T, s.N,
+                         s.M, s.k_per_group, logits, idx, gate, gidx, ggate);
+      return check_launch("route_select_kernel");
+    });
   } else if (s.dtype == MOGE_F32) {
-    const int64_t grid = ((int64_t)s.T + kF32Tokens - 1) / kF32Tokens;
-    hipLaunchKernelGGL(route_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (int64_t)s.T, s.d, s.N,
-                       n_groups, k, static_cast<const float*>(x), static_cast<const float*>(w_router), bias, logits,
-                       idx, gate);
-    st = check_launch("route_f32_kernel");
+    st = with_list_len(kl, [&](auto klc) {
+      constexpr int KL = decltype(klc)::value;
+      const int64_t grid = ((int64_t)s.T + kF32Tokens - 1) / kF32Tokens;
+      hipLaunchKernelGGL(route_f32_kernel<KL>, dim3((unsigned)grid), dim3(256), 0, stream, (int64_t)s.T, s.d, s.N,
+                         s.M, s.k_per_group, static_cast<const float*>(x), static_cast<const float*>(w_router), bias,
+                         logits, idx, gate, gidx, ggate);
+      return check_launch("route_f32_kernel");
+    });
+  } else if (s.N > 128) {
+    const int S = route_slices(s.T);
+    constexpr size_t lds = (size_t)kPartStages * (kPartTM + kPartNP) * 64;
+    st = raise_dynamic_lds(reinterpret_cast<const void*>(route_part_kernel), lds, "route_part_kernel");
+    if (st != MOGE_OK) return st;
+    const int64_t grid = ((int64_t)s.T + kPartTM - 1) / kPartTM * S;
+    float* part = static_cast<float*>(ws);
+    hipLaunchKernelGGL(route_part_kernel, dim3((unsigned)grid), dim3(512), lds, stream, (int64_t)s.T, s.d, s.N, S,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), part);
+    if ((st = check_launch("route_part_kernel")) != MOGE_OK) return st;
+    st = with_list_len(kl, [&](auto klc) {
+      constexpr int KL = decltype(klc)::value;
+      hipLaunchKernelGGL(route_reduce_kernel<KL>,
+                         dim3((unsigned)(((int64_t)s.T + kReduceTokens - 1) / kReduceTokens)), dim3(256), 0, stream,
+                         (int64_t)s.T, s.N, s.M, s.k_per_group, S, part, bias, logits, idx, gate, gidx, ggate);
+      return check_launch("route_reduce_kernel");
+    });
   } else {
-    // few tokens (fewer 128-token tiles than CUs) and N <= 128: the split-K kernel
+    // few tokens (fewer 128-token tiles than CUs): the split-K kernel
     const bool few = ((int64_t)s.T + 127) / 128 < 256;
-    if (few && s.N <= 64) {
-      hipLaunchKernelGGL(route_mfma_splitk_kernel<1>, dim3((unsigned)(((int64_t)s.T + 31) / 32)), dim3(256), 0,
-                         stream, (int64_t)s.T, s.d, s.N, n_groups, k, static_cast<const uint16_t*>(x),
-                         static_cast<const uint16_t*>(w_router), bias, logits, idx, gate);
-      st = check_launch("route_mfma_splitk_kernel");
-    } else if (few && s.N <= 128) {
-      hipLaunchKernelGGL(route_mfma_splitk_kernel<2>, dim3((unsigned)(((int64_t)s.T + 31) / 32)), dim3(256), 0,
-                         stream, (int64_t)s.T, s.d, s.N, n_groups, k, static_cast<const uint16_t*>(x),
-                         static_cast<const uint16_t*>(w_router), bias, logits, idx, gate);
-      st = check_launch("route_mfma_splitk_kernel");
+    const int64_t sgrid = ((int64_t)s.T + 31) / 32;
+    if (few) {
+      st = with_list_len(kl, [&](auto klc) {
+        constexpr int KL = decltype(klc)::value;
+        if (s.N <= 64)
+          hipLaunchKernelGGL((route_mfma_splitk_kernel<1, KL>), dim3((unsigned)sgrid), dim3(256), 0, stream,
+                             (int64_t)s.T, s.d, s.N, s.M, s.k_per_group, static_cast<const uint16_t*>(x),
+                             static_cast<const uint16_t*>(w_router), bias, logits, idx, gate, gidx, ggate);
+        else
+          hipLaunchKernelGGL((route_mfma_splitk_kernel<2, KL>), dim3((unsigned)sgrid), dim3(256), 0, stream,
+                             (int64_t)s.T, s.d, s.N, s.M, s.k_per_group, static_cast<const uint16_t*>(x),
+                             static_cast<const uint16_t*>(w_router), bias, logits, idx, gate, gidx, ggate);
+        return check_launch("route_mfma_splitk_kernel");
+      });
     } else if (s.N <= 64) {
-      st = launch_route_dma<128, 64, 6, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
-    } else if (s.N <= 128) {
-      st = launch_route_dma<64, 128, 6, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
-    } else if (logits) {  // N > 128 with the scores stored: the sliced scores pass, then the choice
-      st = launch_route_dma<64, 128, 8, 4, 2>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
-      if (st == MOGE_OK) st = select();
+      st = launch_route_dma<128, 64, 6, 4>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, stream);
     } else {
-      st = launch_route_dma<32, 256, 7, 4>(s, n_groups, k, x, w_router, bias, logits, idx, gate, stream);
+      st = launch_route_dma<64, 128, 6, 4>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, stream);
     }
   }
   return st == MOGE_OK ? ok() : st;
+}
+
+extern "C" moge_status_t moge_route(const moge_shape_t* shape, int32_t mode, const void* x, const void* w_router,
+                                    const float* bias, float* logits, int32_t* idx, float* gate, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (mode != MOGE_ROUTE_GROUPED && mode != MOGE_ROUTE_GLOBAL) {
+    const moge_status_t st = validate_shape(shape);
+    return st != MOGE_OK ? st : fail(MOGE_ERR_ARG, "unknown route mode");
+  }
+  if (!idx || !gate) {
+    const moge_status_t st = validate_shape(shape);
+    return st != MOGE_OK ? st : fail(MOGE_ERR_NULL, "idx and gate are required");
+  }
+  if (mode == MOGE_ROUTE_GROUPED)
+    return route_impl(shape, x, w_router, bias, logits, idx, gate, nullptr, nullptr, ws, ws_bytes, stream);
+  return route_impl(shape, x, w_router, bias, logits, nullptr, nullptr, idx, gate, ws, ws_bytes, stream);
+}
+
+extern "C" moge_status_t moge_route_pair(const moge_shape_t* shape, const void* x, const void* w_router,
+                                         const float* bias, float* logits, int32_t* idx, float* gate, int32_t* gidx,
+                                         float* ggate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!idx || !gate || !gidx || !ggate) {
+    const moge_status_t st = validate_shape(shape);
+    return st != MOGE_OK ? st : fail(MOGE_ERR_NULL, "idx, gate, gidx and ggate are required");
+  }
+  return route_impl(shape, x, w_router, bias, logits, idx, gate, gidx, ggate, ws, ws_bytes, stream);
 }

@@ -65,7 +65,7 @@ def route_and_score(cfg: StudyConfig, lg: torch.Tensor, mode: int, stream=None):
     gate = torch.empty(T, K, dtype=torch.float32, device=dev)
     group_load = torch.empty(cfg.batches, cfg.M, dtype=torch.int32, device=dev)
     is_raw = torch.empty(cfg.batches, dtype=torch.int32, device=dev)
-    L.route(shape, mode, None, None, None, lg, idx, gate, stream)
+    L.route(shape, mode, None, None, None, lg, idx, gate, None, stream)
     L.imbalance_batches(shape, idx, cfg.tokens, group_load, is_raw, stream)
     return idx, is_raw, group_load
 

@@ -3,7 +3,8 @@
 Order (Pangu Pro MoE, lsdiaocha.cn summary, section 1; Pangu Ultra MoE digests on
 reportify.cn for the shared expert):
 
-  1. moge_route GROUPED   scores (stored), softmax over all N, top-K' in every group
+  1. moge_route_pair     scores, softmax over all N, top-K' in every group (MoGE) and, from the
+                          same scores in the same pass, the conventional global top-K comparator
   2. moge_dispatch        counts, offsets, stable permutation of [e_lo, e_hi); the rows
                           themselves are copied (tiled x_perm, and the tiled x for the
                           shared expert) only where step 3 cannot read them from x
@@ -19,11 +20,13 @@ reportify.cn for the shared expert):
                           with K' = 1 and no shared expert GEMM 2 writes y itself
                           (moge_expert_down_combine)
   5. moge_imbalance       per-group load and imbalance score (0 by construction)
-  6. moge_route GLOBAL    the conventional top-K comparator from the stored scores,
-     moge_dispatch        its counts only, and moge_imbalance of that load -- with expert
-                          FFNs, on a second stream: it starts when step 1's scores exist and
-                          overlaps steps 2-5 (its calls are enqueued after step 2's, so the
-                          GPU never waits on them).
+  6. moge_dispatch        the comparator's counts only, and moge_imbalance of that load -- with
+     moge_imbalance       expert FFNs, on a second stream: it starts when step 1's choices exist
+                          and overlaps steps 2-5 (its calls are enqueued after step 2's, so the
+                          GPU never waits on them).  Without the comparator step 1 is moge_route.
+
+The scores themselves are stored only when asked for (``store_scores``): neither router needs them
+once step 1 has run.
 
 Buffers are allocated once here (torch supplies device memory); ``forward`` only issues
 library calls, so it allocates nothing and does not synchronise.  Expert weights are
@@ -39,7 +42,7 @@ from . import _lib as L
 class MoGELayer:
     def __init__(self, T: int, d: int, N: int, M: int, Kp: int, F: int, F_shared: int = 0, dtype: str = "bf16",
                  e_lo: int = 0, e_hi: int | None = None, device="cuda", comparator: bool = True,
-                 gather: bool | None = None, tiles: int = L.TILES_AUTO):
+                 gather: bool | None = None, tiles: int = L.TILES_AUTO, store_scores: bool = False):
         self.dtype_code = L.BF16 if dtype == "bf16" else L.F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.shape = L.Shape(T, d, N, M, Kp, F, self.dtype_code, tiles)
@@ -67,7 +70,9 @@ class MoGELayer:
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
         K = self.K
-        self.logits = torch.empty(T, N, **f32)
+        self.logits = torch.empty(T, N, **f32) if store_scores else None
+        rws = L.workspace_size(self.shape, L.STAGE_ROUTE)
+        self.rws = torch.empty(rws, dtype=torch.uint8, device=dev) if rws else None
         self.idx = torch.empty(T, K, **i32)
         self.gate = torch.empty(T, K, **f32)
         self.counts = torch.empty(N, **i32)
@@ -126,17 +131,20 @@ class MoGELayer:
         s = self.shape
         mk = mark if mark is not None else (lambda name: None)
         main = stream if stream is not None else torch.cuda.current_stream()
-        L.route(s, L.ROUTE_GROUPED, x, w_router, bias, self.logits, self.idx, self.gate, main)
+        if self.comparator:
+            L.route_pair(s, x, w_router, bias, self.logits, self.idx, self.gate, self.gidx, self.ggate, self.rws,
+                         main)
+        else:
+            L.route(s, L.ROUTE_GROUPED, x, w_router, bias, self.logits, self.idx, self.gate, self.rws, main)
         mk("route")
         def comparator(on):
-            # conventional global top-K on the same scores, its loads and imbalance
-            L.route(s, L.ROUTE_GLOBAL, None, None, None, self.logits, self.gidx, self.ggate, on)
+            # the conventional global top-K's loads (its choice came with the scores) and imbalance
             L.dispatch(s, L.ROUTE_GLOBAL, self.gidx, None, 0, self.N, 0, self.gcounts, self.goffsets, None, None,
                        None, self.gws, stream=on)
             L.imbalance(s, self.gcounts, self.g_group_load, self.g_is_raw, self.g_is_norm, on)
         side = self.side if self.comparator else None
         if side is not None:
-            self.route_done.record(main)  # the comparator needs only the scores
+            self.route_done.record(main)  # the comparator needs only its choice
 
         def side_comparator():
             # enqueued after the layer's own dispatch, so the GPU never waits on these host calls;
@@ -216,7 +224,9 @@ class MoGELayer:
 
     def check_scores(self, stream=None) -> None:
         """Raises MogeError (MOGE_ERR_NONFINITE) if the router scores of the last forward hold a NaN
-        or an infinity.  Waits for the stream."""
+        or an infinity.  Waits for the stream.  Needs the layer built with store_scores=True."""
+        if self.logits is None:
+            raise ValueError("the layer keeps no scores: build it with store_scores=True")
         if not hasattr(self, "check_ws"):
             self.check_ws = torch.empty(L.workspace_size(self.shape, L.STAGE_CHECK), dtype=torch.uint8,
                                         device=self.logits.device)

@@ -107,13 +107,23 @@ def test_null_and_argument_errors_before_any_launch():
     sp = ctypes.byref(s)
     P = ctypes.c_void_p
     fake = P(0x1000)  # never dereferenced: every case fails host validation first
-    lib.moge_route.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [P] * 7
-    assert lib.moge_route(None, 0, fake, fake, None, fake, fake, fake, None) == 3        # NULL shape
-    assert lib.moge_route(sp, 2, fake, fake, None, fake, fake, fake, None) == 1          # bad mode
-    assert lib.moge_route(sp, 0, fake, fake, None, fake, None, fake, None) == 3          # idx NULL
-    assert lib.moge_route(sp, 0, None, None, None, None, fake, fake, None) == 3          # no x, no logits
-    assert lib.moge_route(sp, 0, None, None, fake, fake, fake, fake, None) == 1          # bias with logits-in
-    assert lib.moge_route(sp, 0, fake, None, None, None, fake, fake, None) == 3          # x without w_router
+    lib.moge_route.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [P] * 7 + [ctypes.c_size_t, P]
+    assert lib.moge_route(None, 0, fake, fake, None, fake, fake, fake, None, 0, None) == 3    # NULL shape
+    assert lib.moge_route(sp, 2, fake, fake, None, fake, fake, fake, None, 0, None) == 1      # bad mode
+    assert lib.moge_route(sp, 0, fake, fake, None, fake, None, fake, None, 0, None) == 3      # idx NULL
+    assert lib.moge_route(sp, 0, None, None, None, None, fake, fake, None, 0, None) == 3      # no x, no logits
+    assert lib.moge_route(sp, 0, None, None, fake, fake, fake, fake, None, 0, None) == 1      # bias with logits-in
+    assert lib.moge_route(sp, 0, fake, None, None, None, fake, fake, None, 0, None) == 3      # x without w_router
+    # more than 128 experts from x: the split reduction's workspace is required
+    s256 = S(T=1000, N=256, M=8)
+    need = moge.workspace_size(s256, moge.STAGE_ROUTE)
+    assert need == 4 * 1000 * 256 * 4                                                      # 8 tiles: 4 slices
+    assert moge.workspace_size(S(), moge.STAGE_ROUTE) == 0
+    assert lib.moge_route(ctypes.byref(s256), 0, fake, fake, None, None, fake, fake, fake, need - 1, None) == 4
+    assert lib.moge_route(ctypes.byref(s256), 0, fake, fake, None, None, fake, fake, None, 0, None) == 4
+    lib.moge_route_pair.argtypes = [P] * 10 + [ctypes.c_size_t, P]
+    assert lib.moge_route_pair(sp, fake, fake, None, None, fake, fake, None, fake, None, 0, None) == 3  # gidx NULL
+    assert lib.moge_route_pair(sp, None, None, None, None, fake, fake, fake, fake, None, 0, None) == 3  # no input
     lib.moge_dispatch.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                   P, P, P, P, P, P, P, ctypes.c_size_t, P]
     ws = moge.workspace_size(s)

@@ -175,7 +175,9 @@ def test_layer_every_expert_chosen(gpu):
 
 def test_layer_check_scores(gpu):
     w = W.variant(W.decode(), name="check_T64", T=64, d=256, N=16, M=4, Kp=1, F=64)
-    layer, _ = check_layer(w)
+    layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, 0, "bf16", store_scores=True)
+    dv = packed_inputs(w, layer)
+    layer.forward(dv.x, dv.w_router, dv.bias, dv.w_gate, dv.w_up, dv.w_down)
     layer.check_scores()                         # finite scores pass
     layer.logits[3, 5] = float("nan")
     with pytest.raises(moge.MogeError, match="NONFINITE"):

@@ -23,14 +23,34 @@ def _route_dev(w, lg_np=None, x=None, wr=None, bias=None, mode=moge.ROUTE_GROUPE
     K = w.K
     idx = torch.full((w.T, K), -7, dtype=torch.int32, device="cuda")
     gate = torch.full((w.T, K), -1.0, dtype=torch.float32, device="cuda")
+    nws = moge.workspace_size(s, moge.STAGE_ROUTE)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
     if lg_np is not None:
         lg = torch.from_numpy(lg_np).cuda()
         moge.route(s, mode, None, None, None, lg, idx, gate)
     else:
         lg = torch.empty(w.T, w.N, dtype=torch.float32, device="cuda") if store_logits else None
-        moge.route(s, mode, x, wr, bias, lg, idx, gate)
+        moge.route(s, mode, x, wr, bias, lg, idx, gate, ws)
     torch.cuda.synchronize()
     return s, idx.cpu().numpy(), gate.cpu().numpy(), (lg.cpu().numpy() if lg is not None else None)
+
+
+def _route_pair_dev(w, lg_np=None, x=None, wr=None, bias=None):
+    """moge_route_pair: both routers from one pass; returns (idx, gate, gidx, ggate)."""
+    s = moge.Shape(w.T, w.d, w.N, w.M, w.Kp, w.F, moge.BF16 if w.dtype == "bf16" else moge.F32)
+    K = w.K
+    outs = [torch.full((w.T, K), -7, dtype=torch.int32, device="cuda"),
+            torch.full((w.T, K), -1.0, dtype=torch.float32, device="cuda"),
+            torch.full((w.T, K), -7, dtype=torch.int32, device="cuda"),
+            torch.full((w.T, K), -1.0, dtype=torch.float32, device="cuda")]
+    nws = moge.workspace_size(s, moge.STAGE_ROUTE)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    if lg_np is not None:
+        moge.route_pair(s, None, None, None, torch.from_numpy(lg_np).cuda(), *outs)
+    else:
+        moge.route_pair(s, x, wr, bias, None, *outs, ws)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
 
 
 def _counts_dev(s, idx_np, mode):
@@ -60,9 +80,12 @@ def test_route_on_oracle_scores_bitexact(gpu, w):
     print(f"[route logits-in] {w.name}", flush=True)
     h = H.HostInputs(w)
     lg = H.oracle_logits_all(h)
+    pair = _route_pair_dev(w, lg_np=lg)
     for mode, omode in ((moge.ROUTE_GROUPED, "grouped"), (moge.ROUTE_GLOBAL, "global")):
         s, idx, gate, _ = _route_dev(w, lg_np=lg, mode=mode)
         ridx, rgate, _ = oracle.route(lg, w.M, w.Kp, omode)
+        pi, pg = pair[0:2] if omode == "grouped" else pair[2:4]
+        assert (pi == ridx).all() and (np.abs(pg - rgate) <= 1e-5 * rgate + 1e-8).all()
         assert (idx == ridx).all(), f"{omode}: {(idx != ridx).any(1).sum()} tokens differ"
         assert (np.abs(gate - rgate) <= 1e-5 * rgate + 1e-8).all()
         counts, offsets = _counts_dev(s, idx, mode)
@@ -80,6 +103,16 @@ def test_route_from_x(gpu, w):
     lg_ref = H.oracle_logits_all(h)
     d = H.device_inputs(w)
     _, idx, gate, lg = _route_dev(w, x=d.x, wr=d.w_router, bias=d.bias, store_logits=True)
+    # both routers from one pass give exactly the grouped router's choice and, on the global
+    # side, the choice the global router makes on the same stored scores
+    pidx, pgate, pgidx, pggate = _route_pair_dev(w, x=d.x, wr=d.w_router, bias=d.bias)
+    _, gidx, ggate, _ = _route_dev(w, lg_np=lg, mode=moge.ROUTE_GLOBAL)
+    def _same(a, b, ga, gb, what):
+        bad = np.nonzero((a != b).any(1) | (ga != gb).any(1))[0]
+        assert bad.size == 0, (f"{what}: {bad.size} tokens differ, e.g. token {bad[0]}: {a[bad[0]]} {b[bad[0]]} "
+                               f"{ga[bad[0]]} {gb[bad[0]]}")
+    _same(pidx, idx, pgate, gate, "pair vs grouped")
+    _same(pgidx, gidx, pggate, ggate, "pair vs global")
     # scores: float32 accumulation vs the oracle's binary64 sum rounded once
     scale = 1.0 + np.abs(lg_ref).max()
     assert np.abs(lg - lg_ref).max() <= 1e-4 * scale
@@ -159,18 +192,26 @@ TIE_CASES = [(300, 128, 64, 8, 1, "bf16", True), (300, 128, 64, 8, 2, "bf16", Fa
 @pytest.mark.parametrize("T,d,N,M,Kp,dtype,store", TIE_CASES)
 def test_route_from_x_exact_ties(gpu, T, d, N, M, Kp, dtype, store):
     # integer scores are computed exactly on both sides, so the choice -- including every tie,
-    # broken by the lower expert id, and -0 == +0 -- must match the oracle bit for bit
+    # broken by the lower expert id, and -0 == +0 -- must match the oracle bit for bit, for each
+    # router alone and for both from one pass
     print(f"[route ties from x] T={T} d={d} N={N} M={M} K'={Kp} {dtype} store={store}", flush=True)
     xd, wd, bd, xh, wh, bh = _int_operands(T, d, N, seed=T + N + Kp, f32=dtype == "f32", zero_rows=(0, 1, T - 1))
     w = W.variant(W.routing(), T=T, d=d, N=N, M=M, Kp=Kp, dtype=dtype)
     lg_ref = oracle.logits(xh, wh, bh)
+    ref = {}
     for mode, omode in ((moge.ROUTE_GROUPED, "grouped"), (moge.ROUTE_GLOBAL, "global")):
         _, idx, gate, lg = _route_dev(w, x=xd, wr=wd, bias=bd, mode=mode, store_logits=store)
         if store:
             assert np.array_equal(lg, lg_ref)
         ridx, rgate, _ = oracle.route(lg_ref, M, Kp, omode)
+        ref[omode] = (ridx, rgate)
         assert (idx == ridx).all(), f"{omode}: {(idx != ridx).any(1).sum()} tokens differ"
         assert (np.abs(gate - rgate) <= 1e-5 * rgate + 1e-8).all()
+    idx, gate, gidx, ggate = _route_pair_dev(w, x=xd, wr=wd, bias=bd)
+    for (i, g), omode in (((idx, gate), "grouped"), ((gidx, ggate), "global")):
+        ridx, rgate = ref[omode]
+        assert (i == ridx).all(), f"pair {omode}: {(i != ridx).any(1).sum()} tokens differ"
+        assert (np.abs(g - rgate) <= 1e-5 * rgate + 1e-8).all()
 
 
 NAN_CASES = [(200, 64, 8, 1, moge.ROUTE_GROUPED), (200, 64, 8, 2, moge.ROUTE_GLOBAL),
