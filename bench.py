@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
+    p.add_argument("--blas-reference", action="store_true",
+                   help="only time the vendor GEMM library (torch.bmm, bf16) on dense batches shaped like "
+                        "the Ultra and one-group-share expert GEMMs, for comparison with the grouped kernels")
     return p.parse_args()
 
 
@@ -80,6 +83,39 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read_per_launch": n, "bytes_written_per_launch": n, "launches": 3}))
+
+
+def blas_reference():
+    """The vendor library on the expert GEMMs' shapes as dense batches (every expert the average row
+    count, contiguous operands, bf16 in and out): what a grouped kernel with ideal load balance and no
+    gather, SwiGLU or shared expert would be compared with.  Prints one JSON line."""
+    import torch
+
+    def run(name, E, m, k, n, reps=10):
+        a = torch.randn(E, m, k, device="cuda").to(torch.bfloat16)
+        b = torch.randn(E, k, n, device="cuda").to(torch.bfloat16)   # contiguous right operand
+        for _ in range(3):
+            torch.bmm(a, b)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            torch.bmm(a, b)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1000.0 / reps
+        flops = 2.0 * E * m * k * n
+        del a, b
+        torch.cuda.empty_cache()
+        return {"gemm": name, "batch": E, "m": m, "k": k, "n": n, "us": round(us, 1),
+                "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
+                "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    rows = [run("ultra gate/up (gate and up rows as one operand)", 256, 256, 7680, 4096),
+            run("ultra down", 256, 256, 2048, 7680),
+            run("group-0 share gate/up", 8, 8192, 4096, 2816),
+            run("group-0 share down", 8, 8192, 1408, 4096)]
+    print(json.dumps({"blas_reference": rows, "library": "torch.bmm (hipBLASLt) bf16"}), flush=True)
 
 
 def algorithmic_work(w, counts, fused_shared=False, gather=False, fused_combine=False):
@@ -315,6 +351,29 @@ def side_workload(w, steps, warmup, keys):
                          "global_topk_is_raw": int(layer.g_is_raw.item())}}
     if w.e_hi - w.e_lo == w.N:
         out["per_expert_share_global_topk"] = expert_share(layer.gcounts.cpu().numpy(), w)
+    if not w.F:
+        # the MoGE router alone (moge_route, no comparator, no stored scores): x read once, the
+        # choice written, between reads of a 512 MiB buffer so x comes from HBM each time
+        import mixture_grouped_experts_amd as moge
+
+        flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        ts = []
+        for rep in range(steps + warmup):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            moge.route(layer.shape, moge.ROUTE_GROUPED, dv.x, dv.w_router, dv.bias, None, layer.idx, layer.gate,
+                       layer.rws)
+            b.record()
+            torch.cuda.synchronize()
+            if rep >= warmup:
+                ts.append(a.elapsed_time(b) * 1000.0)
+        us = float(np.median(ts))
+        nbytes = w.T * w.d * 2 + w.N * w.d * 2 + w.T * w.K * 8
+        out["router_alone"] = {"us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                               "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes": nbytes}
+        del flush
     del layer, dv
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -330,6 +389,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.blas_reference:
+        blas_reference()
         return
 
     import numpy as np

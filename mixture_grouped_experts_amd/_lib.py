@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoge.so")
+# MOGE_LIB names another build of the same library (e.g. one with sanitized host code)
+LIB_PATH = os.environ.get("MOGE_LIB") or os.path.join(_HERE, "libmoge.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python __graft_entry__.py` (build()) first")
