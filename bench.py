@@ -397,6 +397,7 @@ def main():
     import numpy as np
     import torch
 
+    import mixture_grouped_experts_amd as moge
     from synth import workloads as W
 
     w = {"ultra": W.ultra, "group0": W.group0, "decode": W.decode, "routing": W.routing, "tiny": W.tiny,
@@ -481,8 +482,9 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "M": w.M, "k_per_group": w.Kp, "F": w.F,
                    "F_shared": w.F_shared, "experts_computed": [w.e_lo, w.e_hi], "seed": w.seed,
                    "rows": "gather" if layer.gather else "copy",
-                   "tiles": (args.tiles if args.tiles != "auto"
-                             else "wide" if w.T * w.M * w.Kp <= 64 * w.N else "tall")},
+                   "tiles": ({g: {moge.TILES_TALL: "tall", moge.TILES_WIDE: "wide"}.get(
+                                  moge.tile_choice(layer.shape, i, w.e_lo, w.e_hi, w.F_shared), "none")
+                              for i, g in ((1, "gate_up"), (2, "down"))} if w.F else None)},
         "roofline": roof,
         "stages": _stage_table(stage_us, work),
         "imbalance": {"moge_is_raw": int(layer.is_raw.item()),

@@ -75,10 +75,10 @@ typedef enum { MOGE_STAGE_DISPATCH = 1, MOGE_STAGE_CHECK = 2, MOGE_STAGE_ROUTE =
 
 /* Tile shape of the bf16 expert GEMMs (moge_shape_t.tiles).  Every output is
  * bit-identical under all of them (same reduction order per output element).
- *   MOGE_TILES_AUTO  the library's choice from the shape (the default, 0): its
- *                    table of tile shapes keyed by the rows per expert, which
- *                    plays the part of the grouped matmul's tiling cache and its
- *                    switch of mode by workload ([P1] section 3, SwiftGMM);
+ *   MOGE_TILES_AUTO  the library's choice for each GEMM from its shape (the
+ *                    default, 0): the tile table of moge_tile_choice, which plays
+ *                    the part of the grouped matmul's tiling cache and its switch
+ *                    of mode by workload ([P1] section 3, SwiftGMM);
  *   MOGE_TILES_TALL  320 token rows x 256 weight rows;
  *   MOGE_TILES_WIDE  96 token rows x 512 weight rows (few rows per expert). */
 #define MOGE_TILES_AUTO 0
@@ -410,6 +410,19 @@ moge_status_t moge_imbalance_batches(const moge_shape_t* shape, const int32_t* i
  */
 moge_status_t moge_check_finite(int32_t dtype, const void* a, int64_t n, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * moge_tile_choice -- the tile shape MOGE_TILES_AUTO gives one expert GEMM of a call
+ * with this shape: gemm 1 = gate/up (output width F), 2 = down (output width d), for
+ * the routed experts [e_lo, e_hi) and, when F_shared > 0, the shared expert's tiles in
+ * the same launch.  The table keys on the rows per expert under MoGE routing
+ * (T*K' / (N/M)), the experts, the output width and the device's CU count, and takes
+ * the shape whose busiest CU streams the fewest weight rows: ceil(tiles / CUs) times
+ * the tile's weight rows (the wide shape on a tie).  A forced shape.tiles is returned
+ * as is.  Host-only (the CU count is queried once; 256 without a device).
+ * Returns MOGE_TILES_TALL or MOGE_TILES_WIDE, or -1 for invalid arguments.
+ */
+int32_t moge_tile_choice(const moge_shape_t* shape, int32_t gemm, int32_t e_lo, int32_t e_hi, int32_t F_shared);
 
 /* Library version string and the calling thread's last error message. */
 const char* moge_version(void);

@@ -42,7 +42,8 @@ EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_
            "moge_grouped_ffn",
            "moge_expert_gate_up", "moge_expert_down", "moge_expert_gate_up_with_shared",
            "moge_expert_down_with_shared", "moge_expert_gate_up_gather", "moge_expert_down_combine",
-           "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_check_finite", "moge_version",
+           "moge_combine", "moge_imbalance", "moge_imbalance_batches", "moge_check_finite", "moge_tile_choice",
+           "moge_version",
            "moge_last_error", "moge_round_bf16")
 
 
@@ -118,6 +119,8 @@ _lib.moge_imbalance.argtypes = [_SP, _P, _P, _P, _P, _P]
 _lib.moge_imbalance.restype = ctypes.c_int
 _lib.moge_imbalance_batches.argtypes = [_SP, _P, _I64, _P, _P, _P]
 _lib.moge_imbalance_batches.restype = ctypes.c_int
+_lib.moge_tile_choice.argtypes = [_SP, _I32, _I32, _I32, _I32]
+_lib.moge_tile_choice.restype = ctypes.c_int32
 _lib.moge_version.argtypes = []
 _lib.moge_version.restype = ctypes.c_char_p
 _lib.moge_last_error.argtypes = []
@@ -197,6 +200,11 @@ def round_bf16(x, y, stream=None) -> None:
 
 def workspace_size(shape: Shape, stage: int = STAGE_DISPATCH) -> int:
     return int(_lib.moge_workspace_size(ctypes.byref(shape), stage))
+
+
+def tile_choice(shape: Shape, gemm: int, e_lo: int, e_hi: int, F_shared: int = 0) -> int:
+    """The tile shape (TILES_TALL or TILES_WIDE) the library uses for GEMM `gemm` (1 gate/up, 2 down)."""
+    return int(_lib.moge_tile_choice(ctypes.byref(shape), gemm, e_lo, e_hi, F_shared))
 
 
 def version() -> str:

@@ -814,18 +814,46 @@ static moge_status_t launch_ggemm_shape(const GemmOperands& p0, const int32_t* o
   return check_launch(SWIGLU ? "ggemm_bf16_kernel<gate_up>" : "ggemm_bf16_kernel<down>");
 }
 
-// The tile shape: the 96 x 512 tiles when the routed experts average at most 64 rows
-// (T K / N, exact per group under MoGE routing), else 320 x 256; or as the call's
-// shape.tiles asks.
-static bool wide_tiles(const moge_shape_t& s) {
+// The tile table ([P1] section 3: SwiftGMM picks its tiling from a cache keyed by the
+// problem and switches to a matrix-vector-like mode when the rows are few).  Here the
+// candidates are the two tile shapes and the key is the shape of the call: the rows per
+// expert expected under MoGE routing (every group receives exactly T K' rows, so an expert
+// averages T K' / (N / M)), the experts of the call, the output width and the CU count.
+// Few rows per expert make a GEMM a weight stream whose time is set by the CU that streams
+// the most weight rows: every tile streams its BW weight rows over the whole reduction, and
+// the persistent grid hands tile i to workgroup i mod CUs, so that CU streams
+// ceil(tiles / CUs) * BW rows.  The table takes the shape with the smaller figure, the wide
+// one on a tie (twice the weight bytes in flight per step).  Measured at 64-512 tokens x
+// 4096 x 64 experts over expert ranges of 16-64, this picks the faster shape of each GEMM
+// (e.g. gate/up at 256 tokens: 704 tall tiles = 3 rounds x 256 rows against 384 wide tiles
+// = 2 rounds x 512 rows, 289 against 300 us); many rows per expert give the tall shape
+// anyway (a wide tile then splits an expert into several m-tiles).
+static int64_t tile_rounds_rows(int bm, int bw, bool swiglu, int64_t rows_per_expert, int64_t E, int64_t nout,
+                                int64_t rows1, int64_t nout1, int64_t cus) {
+  const int64_t bno = swiglu ? bw / 2 : bw;
+  auto tiles_of = [&](int64_t rows, int64_t n) { return ((rows + bm - 1) / bm) * ((n + bno - 1) / bno); };
+  int64_t tiles = E * tiles_of(rows_per_expert > 0 ? rows_per_expert : 1, nout);
+  if (rows1 > 0) tiles += tiles_of(rows1, nout1);
+  return (tiles + cus - 1) / cus * bw;
+}
+
+static bool wide_tiles(const moge_shape_t& s, bool swiglu, int64_t E, int64_t nout, int64_t rows1, int64_t nout1) {
   if (s.tiles != MOGE_TILES_AUTO) return s.tiles == MOGE_TILES_WIDE;
-  return (int64_t)s.T * s.M * s.k_per_group <= (int64_t)64 * s.N;
+  const int64_t G = s.N / s.M;
+  const int64_t rows_per_expert = ((int64_t)s.T * s.k_per_group + G - 1) / G;
+  const int64_t cus = device_cus();
+  const int64_t tall = tile_rounds_rows(TileShape<2>::BM, TileShape<2>::BW, swiglu, rows_per_expert, E, nout, rows1,
+                                        nout1, cus);
+  const int64_t wide = tile_rounds_rows(TileShape<1>::BM, TileShape<1>::BW, swiglu, rows_per_expert, E, nout, rows1,
+                                        nout1, cus);
+  return wide <= tall;
 }
 
 template <bool SWIGLU>
 static moge_status_t launch_ggemm(const moge_shape_t& s, const GemmOperands& p0, const int32_t* offsets, int e_lo,
                                   int E, int64_t rows_cap, const GemmOperands& p1, int rows1, hipStream_t stream) {
-  if (wide_tiles(s)) return launch_ggemm_shape<SWIGLU, 1>(p0, offsets, e_lo, E, rows_cap, p1, rows1, stream);
+  if (wide_tiles(s, SWIGLU, E, p0.NOUT, rows1, p1.NOUT))
+    return launch_ggemm_shape<SWIGLU, 1>(p0, offsets, e_lo, E, rows_cap, p1, rows1, stream);
   return launch_ggemm_shape<SWIGLU, 2>(p0, offsets, e_lo, E, rows_cap, p1, rows1, stream);
 }
 
@@ -995,4 +1023,14 @@ extern "C" moge_status_t moge_expert_down_combine(const moge_shape_t* shape, con
   const GemmOperands none{};
   st = launch_ggemm<false>(s, p, offsets, e_lo, e_hi - e_lo, rows_cap, none, 0, stream);
   return st == MOGE_OK ? ok() : st;
+}
+
+extern "C" int32_t moge_tile_choice(const moge_shape_t* shape, int32_t gemm, int32_t e_lo, int32_t e_hi,
+                                    int32_t F_shared) {
+  if (validate_shape(shape) != MOGE_OK || shape->F <= 0) return -1;
+  if ((gemm != 1 && gemm != 2) || e_lo < 0 || e_hi > shape->N || e_lo >= e_hi || F_shared < 0) return -1;
+  const moge_shape_t& s = *shape;
+  const bool swiglu = gemm == 1;
+  const int64_t nout = swiglu ? s.F : s.d, nout1 = swiglu ? F_shared : s.d;
+  return wide_tiles(s, swiglu, e_hi - e_lo, nout, F_shared > 0 ? s.T : 0, nout1) ? MOGE_TILES_WIDE : MOGE_TILES_TALL;
 }

@@ -14,12 +14,13 @@
 //     and router rows go from global memory straight into a 6-stage LDS ring with
 //     direct-to-LDS loads, several 32-element steps ahead.  Few tokens (fewer 128-token
 //     tiles than CUs): a split-K kernel whose operands go straight into registers.
-//   * bf16 scores, 128 < N <= 256: split over the hidden dimension.  Workgroup b takes
-//     slice b % S of the reduction (S = 1..4, so that the token tiles times S fill the
-//     chip) of a 128-token x 256-expert tile; workgroup b runs on XCD b % 8, so an XCD
-//     only ever reads its slices of the router matrix, which stay in its L2, and x is
-//     read from HBM exactly once.  Slice partial sums go to the workspace; a second
-//     kernel adds them in slice order (deterministic), adds the bias and chooses.
+//   * bf16 scores, 128 < N <= 256, and few tokens (at most 4096) at any N: split over the
+//     hidden dimension.  Workgroup b takes slice b % S of the reduction (S chosen so the
+//     token tiles times S fill the chip: up to 4 for many tokens, up to 32 for few) of a
+//     128-token x 256-expert tile; workgroup b runs on XCD b % 8, so an XCD only ever
+//     reads its slices of the router matrix, which stay in its L2, and x is read from HBM
+//     exactly once.  Slice partial sums go to the workspace; a second kernel adds them in
+//     slice order (deterministic), adds the bias and chooses.
 //   * The choice (one epilogue for every kernel): the score tile sits in LDS; lane
 //     (token, group) keeps its group's best experts in a sorted register list; the
 //     token's softmax max and sum are butterflies over its lanes; MoGE takes the first
@@ -796,17 +797,19 @@ static moge_status_t launch_route_dma(const moge_shape_t& s, int kl, const void*
 }
 
 // ----------------------------------------------------------------------------
-// bf16 scores, 128 < N <= 256: split over the hidden dimension.  Workgroup b computes
-// slice b % S of the reduction (its steps k0 .. k1 - 1 of d / 32) for the 128-token x
-// 256-expert tile b / S, and stores the float32 partial sums to part[slice][t][e].
-// 8 waves; wave w owns tokens (w / 4) * 64 .. + 64 and experts (w % 4) * 64 .. + 64 as
-// 2 x 2 accumulators of 32 x 32 (v_mfma_f32_32x32x16_bf16).  Each step's 128 token rows
-// and 256 router rows (64 bytes of each) go straight into a 6-stage LDS ring (24 loads of
-// 16 rows per step, 3 per wave), 5 steps ahead, one barrier per step.  Workgroup b runs on
-// XCD b % 8 and S divides 8 (or is 1), so an XCD reads only its own slices of the router
-// matrix (at most 983 KB of a 256 x 7680 matrix), which stay in its L2, while x streams
-// from HBM once.  The last slice also takes the ragged tail of d (d % 32 columns).
+// bf16 scores split over the hidden dimension (128 < N <= 256, or few tokens at any N).
+// Workgroup b computes slice b % S of the reduction (its steps k0 .. k1 - 1 of d / 32) for
+// the 128-token x 256-expert tile b / S, and stores the float32 partial sums to
+// part[slice][t][e].  8 waves; wave w owns tokens (w / 4) * 64 .. + 64 and experts
+// (w % 4) * 64 .. + 64 as 2 x 2 accumulators of 32 x 32 (v_mfma_f32_32x32x16_bf16; experts
+// past N repeat the last router row and are not stored).  Each step's 128 token rows and 256
+// router rows (64 bytes of each) go straight into a 6-stage LDS ring (24 loads of 16 rows per
+// step, 3 per wave), 5 steps ahead, one barrier per step.  Workgroup b runs on XCD b % 8 and
+// S is a power of two, so an XCD reads only its own slices of the router matrix (at most
+// 983 KB of a 256 x 7680 matrix at S = 4), which stay in its L2, while x streams from HBM
+// once.  The last slice also takes the ragged tail of d (d % 32 columns).
 constexpr int kPartTM = 128, kPartNP = 256, kPartStages = 6;
+__host__ __forceinline__ int route_slices(int64_t T, int d);
 __global__ __launch_bounds__(512) void route_part_kernel(int64_t T, int d, int N, int S,
                                                          const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ w,
@@ -934,20 +937,30 @@ __global__ __launch_bounds__(512) void route_part_kernel(int64_t T, int d, int N
 }
 
 // Slices per token tile for the split kernel: enough that the token tiles times the slices
-// fill the 256 CUs, at most 4, and a divisor of 8 so each XCD holds whole slices.
-__host__ __forceinline__ int route_slices(int64_t T) {
+// fill the 256 CUs, at most 4 for many tokens (each XCD then holds whole slices of the router
+// matrix) and, for few tokens, up to 32 while every slice keeps at least 2 steps of 32.
+__host__ __forceinline__ int route_slices(int64_t T, int d) {
   const int64_t tiles = (T + kPartTM - 1) / kPartTM;
+  const int nkf = d / 32;
+  const int cap = tiles >= 16 ? 4 : 32;
   int S = 1;
-  while (S < 4 && tiles * S < 256) S <<= 1;
+  while (S < cap && tiles * S < 256 && nkf / (2 * S) >= 2) S <<= 1;
   return S;
+}
+
+// bf16 scores from x go through the split kernel and the reduction for more than 128
+// experts, and for few tokens (at most 32 token tiles) at any expert count: there the split
+// spreads the reduction over many workgroups instead of a handful.
+__host__ __forceinline__ bool route_split(const moge_shape_t& s) {
+  return s.dtype == MOGE_BF16 && (s.N > 128 || (int64_t)s.T <= 32 * kPartTM);
 }
 
 // The split kernel's partial sums -> scores -> the choices.  32 tokens per workgroup:
 // the S slices of each score are added in slice order (bit-identical results run to run),
 // plus the bias, into an LDS tile [32][N + 1]; then the common epilogue.
-constexpr int kReduceTokens = 32;
+constexpr int kReduceTokens = 32;  // at most, per workgroup (tpw: 8 for many slices, so more workgroups load)
 template <int KL>
-__global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int M, int k, int S,
+__global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int M, int k, int S, int tpw,
                                                            const float* __restrict__ part,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ logits_out, int32_t* __restrict__ idx,
@@ -955,23 +968,34 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int
                                                            float* __restrict__ ggate) {
   __shared__ float lt[kReduceTokens * (kMaxExperts + 1)];
   const int ld = N + 1;
-  const int64_t t0 = (int64_t)blockIdx.x * kReduceTokens;
-  const int64_t nrows = (T - t0) < kReduceTokens ? (T - t0) : kReduceTokens;
+  const int64_t t0 = (int64_t)blockIdx.x * tpw;
+  const int64_t nrows = (T - t0) < tpw ? (T - t0) : tpw;
   const int total = (int)nrows * N;
   const int64_t plane = T * N;
   const float* src = part + t0 * N;  // the tile's rows are contiguous in every slice
   if ((N & 3) == 0) {
-    // 16-byte loads, the four slices of 4 chunks all issued before any is added
+    // 16-byte loads: 4 chunks x up to 4 slices in flight per thread; each element adds its
+    // slices in slice order
     for (int i0 = threadIdx.x * 4; i0 < total; i0 += 256 * 4 * 4) {
-      f32x4_t v[4][4];
+      f32x4_t a[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 1024;
+      for (int u = 0; u < 4; ++u) a[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int p0 = 0; p0 < S; p0 += 4) {
+        f32x4_t v[4][4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          if (i < total && p < S) v[u][p] = *reinterpret_cast<const f32x4_t*>(src + p * plane + i);
-          else v[u][p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 1024;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            if (i < total && p0 + p < S) v[u][p] = *reinterpret_cast<const f32x4_t*>(src + (p0 + p) * plane + i);
+            else v[u][p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            if (p0 + p < S) a[u] = p0 + p == 0 ? v[u][p] : a[u] + v[u][p];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -979,13 +1003,7 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int
         if (i < total) {
           const int r = i / N, c = i - r * N;  // c % 4 == 0: the 4 values share a row
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float a = v[u][0][q];
-#pragma unroll
-            for (int p = 1; p < 4; ++p)
-              if (p < S) a += v[u][p][q];
-            lt[r * ld + c + q] = a + (bias ? bias[c + q] : 0.f);
-          }
+          for (int q = 0; q < 4; ++q) lt[r * ld + c + q] = a[u][q] + (bias ? bias[c + q] : 0.f);
         }
       }
     }
@@ -1147,8 +1165,8 @@ using namespace moge;
 // Bytes of workspace the scores need: the split kernel's partial sums for bf16 shapes with
 // more than 128 experts (x given), else none.
 size_t moge::route_workspace_bytes(const moge_shape_t& s) {
-  if (s.dtype != MOGE_BF16 || s.N <= 128) return 0;
-  return (size_t)route_slices(s.T) * (size_t)s.T * (size_t)s.N * sizeof(float);
+  if (!route_split(s)) return 0;
+  return (size_t)route_slices(s.T, s.d) * (size_t)s.T * (size_t)s.N * sizeof(float);
 }
 
 // Scores (from x, or the caller's) and the choices: MoGE into idx/gate when idx is set, the
@@ -1189,8 +1207,8 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
                          logits, idx, gate, gidx, ggate);
       return check_launch("route_f32_kernel");
     });
-  } else if (s.N > 128) {
-    const int S = route_slices(s.T);
+  } else if (route_split(s)) {
+    const int S = route_slices(s.T, s.d);
     constexpr size_t lds = (size_t)kPartStages * (kPartTM + kPartNP) * 64;
     st = raise_dynamic_lds(reinterpret_cast<const void*>(route_part_kernel), lds, "route_part_kernel");
     if (st != MOGE_OK) return st;
@@ -1199,15 +1217,16 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
     hipLaunchKernelGGL(route_part_kernel, dim3((unsigned)grid), dim3(512), lds, stream, (int64_t)s.T, s.d, s.N, S,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), part);
     if ((st = check_launch("route_part_kernel")) != MOGE_OK) return st;
+    const int tpw = S > 4 ? 8 : kReduceTokens;
     st = with_list_len(kl, [&](auto klc) {
       constexpr int KL = decltype(klc)::value;
       hipLaunchKernelGGL(route_reduce_kernel<KL>,
-                         dim3((unsigned)(((int64_t)s.T + kReduceTokens - 1) / kReduceTokens)), dim3(256), 0, stream,
-                         (int64_t)s.T, s.N, s.M, s.k_per_group, S, part, bias, logits, idx, gate, gidx, ggate);
+                         dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256), 0, stream,
+                         (int64_t)s.T, s.N, s.M, s.k_per_group, S, tpw, part, bias, logits, idx, gate, gidx, ggate);
       return check_launch("route_reduce_kernel");
     });
   } else {
-    // few tokens (fewer 128-token tiles than CUs): the split-K kernel
+    // fewer 128-token tiles than CUs (and more than the split path takes): the split-K kernel
     const bool few = ((int64_t)s.T + 127) / 128 < 256;
     const int64_t sgrid = ((int64_t)s.T + 31) / 32;
     if (few) {

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     with open(os.path.join(ROOT, "include", "moge.h")) as f:
         txt = f.read()
-    return sorted(set(re.findall(r"^\s*(?:moge_status_t|int64_t|size_t|const char\*)\s+(moge_\w+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:moge_status_t|int64_t|int32_t|size_t|const char\*)\s+(moge_\w+)\s*\(", txt, re.M)))
 
 
 def test_exports_every_declared_symbol():
@@ -117,8 +117,11 @@ def test_null_and_argument_errors_before_any_launch():
     # more than 128 experts from x: the split reduction's workspace is required
     s256 = S(T=1000, N=256, M=8)
     need = moge.workspace_size(s256, moge.STAGE_ROUTE)
-    assert need == 4 * 1000 * 256 * 4                                                      # 8 tiles: 4 slices
-    assert moge.workspace_size(S(), moge.STAGE_ROUTE) == 0
+    assert need == 2 * 1000 * 256 * 4          # 8 token tiles, d = 128: 4 steps of 32, 2 slices of 2 steps
+    assert moge.workspace_size(S(T=1000, d=7680, N=256, M=8), moge.STAGE_ROUTE) == 32 * 1000 * 256 * 4
+    assert moge.workspace_size(S(T=8192, d=7680, N=256, M=8), moge.STAGE_ROUTE) == 4 * 8192 * 256 * 4
+    assert moge.workspace_size(S(T=5000, N=64, M=8), moge.STAGE_ROUTE) == 0             # one pass, no split
+    assert moge.workspace_size(S(dt=moge.F32), moge.STAGE_ROUTE) == 0
     assert lib.moge_route(ctypes.byref(s256), 0, fake, fake, None, None, fake, fake, fake, need - 1, None) == 4
     assert lib.moge_route(ctypes.byref(s256), 0, fake, fake, None, None, fake, fake, None, 0, None) == 4
     lib.moge_route_pair.argtypes = [P] * 10 + [ctypes.c_size_t, P]
@@ -227,3 +230,33 @@ def test_dispatch_noalloc_refuses_shapes_past_its_scratch():
     assert moge.workspace_size(ok_shape) == 4 << 20                  # exactly the limit
     assert lib.moge_dispatch_noalloc(ctypes.byref(S()), 0, None, None, 0, 8, 0, fake, fake, None, None, None, None,
                                      None) == 3                       # idx NULL
+
+
+@pytest.mark.parametrize("T,e_hi,gemm,want", [
+    # 4096 hidden, 64 experts in 8 groups, K' = 2, F = 1408: rows per expert 2T/8; the expected
+    # choice of each case was also the faster shape when timed (64-512 tokens, 16-64 experts)
+    (256, 64, 1, "tall"),    # 704 tall tiles = 3 rounds x 256 rows < 384 wide tiles = 2 x 512
+    (256, 64, 2, "wide"),    # 1024 tall tiles = 4 x 256 == 512 wide tiles = 2 x 512: tie -> wide
+    (64, 64, 1, "tall"), (64, 64, 2, "wide"),
+    (512, 64, 1, "tall"), (512, 64, 2, "tall"),    # 128 rows: a wide tile splits each expert in two
+    (64, 43, 1, "tall"),     # 473 tall tiles = 2 x 256 < 258 wide tiles = 2 x 512
+    (64, 32, 1, "wide"),     # 352 tall = 2 x 256 == 192 wide = 1 x 512
+    (64, 16, 1, "tall"),     # 176 tall = 1 x 256 < 96 wide = 1 x 512
+])
+def test_tile_table(T, e_hi, gemm, want):
+    s = S(T=T, d=4096, N=64, M=8, Kp=2, F=1408)
+    got = moge.tile_choice(s, gemm, 0, e_hi)
+    assert got == {"tall": moge.TILES_TALL, "wide": moge.TILES_WIDE}[want]
+
+
+def test_tile_table_large_shapes_and_forced():
+    ultra = S(T=8192, d=7680, N=256, M=8, Kp=1, F=2048)
+    assert moge.tile_choice(ultra, 1, 0, 256, 2048) == moge.TILES_TALL
+    assert moge.tile_choice(ultra, 2, 0, 256, 2048) == moge.TILES_TALL
+    group0 = S(T=65536, d=4096, N=64, M=8, Kp=1, F=1408)
+    assert moge.tile_choice(group0, 1, 0, 8) == moge.TILES_TALL
+    forced = S(T=8192, d=7680, N=256, M=8, Kp=1, F=2048, tiles=moge.TILES_WIDE)
+    assert moge.tile_choice(forced, 1, 0, 256) == moge.TILES_WIDE
+    assert moge.tile_choice(ultra, 3, 0, 256) == -1 and moge.tile_choice(ultra, 1, 5, 5) == -1
+    assert moge.tile_choice(S(F=0), 1, 0, 8) == -1
+
