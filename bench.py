@@ -111,7 +111,8 @@ def blas_reference():
                 "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
                 "mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
-    rows = [run("ultra gate/up (gate and up rows as one operand)", 256, 256, 7680, 4096),
+    rows = [run("dense square (the library's best case)", 1, 8192, 8192, 8192),
+            run("ultra gate/up (gate and up rows as one operand)", 256, 256, 7680, 4096),
             run("ultra down", 256, 256, 2048, 7680),
             run("group-0 share gate/up", 8, 8192, 4096, 2816),
             run("group-0 share down", 8, 8192, 1408, 4096)]

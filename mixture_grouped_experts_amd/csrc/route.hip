@@ -955,18 +955,21 @@ __host__ __forceinline__ bool route_split(const moge_shape_t& s) {
   return s.dtype == MOGE_BF16 && (s.N > 128 || (int64_t)s.T <= 32 * kPartTM);
 }
 
-// The split kernel's partial sums -> scores -> the choices.  32 tokens per workgroup:
-// the S slices of each score are added in slice order (bit-identical results run to run),
-// plus the bias, into an LDS tile [32][N + 1]; then the common epilogue.
-constexpr int kReduceTokens = 32;  // at most, per workgroup (tpw: 8 for many slices, so more workgroups load)
+// The split kernel's partial sums -> scores -> the choices.  8 tokens per workgroup (many
+// workgroups, so every CU has several tiles' loads in flight): the S slices of each score
+// are added in slice order (bit-identical results run to run), plus the bias, into an LDS
+// tile [8][N + 1]; then the common epilogue.
+constexpr int kReduceTokens = 8;
 template <int KL>
-__global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int M, int k, int S, int tpw,
+__global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int M, int k, int S,
                                                            const float* __restrict__ part,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ logits_out, int32_t* __restrict__ idx,
                                                            float* __restrict__ gate, int32_t* __restrict__ gidx,
                                                            float* __restrict__ ggate) {
-  __shared__ float lt[kReduceTokens * (kMaxExperts + 1)];
+  constexpr int tpw = kReduceTokens;
+  constexpr int PU = 16;  // slices of one chunk in flight together
+  __shared__ float lt[tpw * (kMaxExperts + 1)];
   const int ld = N + 1;
   const int64_t t0 = (int64_t)blockIdx.x * tpw;
   const int64_t nrows = (T - t0) < tpw ? (T - t0) : tpw;
@@ -974,38 +977,21 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int
   const int64_t plane = T * N;
   const float* src = part + t0 * N;  // the tile's rows are contiguous in every slice
   if ((N & 3) == 0) {
-    // 16-byte loads: 4 chunks x up to 4 slices in flight per thread; each element adds its
-    // slices in slice order
-    for (int i0 = threadIdx.x * 4; i0 < total; i0 += 256 * 4 * 4) {
-      f32x4_t a[4];
+    // 16-byte chunks, one per thread at a time, with up to 16 of its slices loaded together
+    for (int i = threadIdx.x * 4; i < total; i += 256 * 4) {
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+      for (int p0 = 0; p0 < S; p0 += PU) {
+        f32x4_t v[PU];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      for (int p0 = 0; p0 < S; p0 += 4) {
-        f32x4_t v[4][4];
+        for (int p = 0; p < PU; ++p)
+          v[p] = p0 + p < S ? *reinterpret_cast<const f32x4_t*>(src + (p0 + p) * plane + i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * 1024;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            if (i < total && p0 + p < S) v[u][p] = *reinterpret_cast<const f32x4_t*>(src + (p0 + p) * plane + i);
-            else v[u][p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            if (p0 + p < S) a[u] = p0 + p == 0 ? v[u][p] : a[u] + v[u][p];
+        for (int p = 0; p < PU; ++p)
+          if (p0 + p < S) a = p0 + p == 0 ? v[p] : a + v[p];
       }
+      const int r = i / N, c = i - r * N;  // c % 4 == 0: the 4 values share a row
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 1024;
-        if (i < total) {
-          const int r = i / N, c = i - r * N;  // c % 4 == 0: the 4 values share a row
-#pragma unroll
-          for (int q = 0; q < 4; ++q) lt[r * ld + c + q] = a[u][q] + (bias ? bias[c + q] : 0.f);
-        }
-      }
+      for (int q = 0; q < 4; ++q) lt[r * ld + c + q] = a[q] + (bias ? bias[c + q] : 0.f);
     }
   } else {
     for (int i = threadIdx.x; i < total; i += 256) {
@@ -1217,12 +1203,12 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
     hipLaunchKernelGGL(route_part_kernel, dim3((unsigned)grid), dim3(512), lds, stream, (int64_t)s.T, s.d, s.N, S,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), part);
     if ((st = check_launch("route_part_kernel")) != MOGE_OK) return st;
-    const int tpw = S > 4 ? 8 : kReduceTokens;
+    const int tpw = kReduceTokens;
     st = with_list_len(kl, [&](auto klc) {
       constexpr int KL = decltype(klc)::value;
       hipLaunchKernelGGL(route_reduce_kernel<KL>,
                          dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256), 0, stream,
-                         (int64_t)s.T, s.N, s.M, s.k_per_group, S, tpw, part, bias, logits, idx, gate, gidx, ggate);
+                         (int64_t)s.T, s.N, s.M, s.k_per_group, S, part, bias, logits, idx, gate, gidx, ggate);
       return check_launch("route_reduce_kernel");
     });
   } else {
