@@ -145,9 +145,9 @@ def test_route_ties_and_edge_shapes(gpu):
                                             (64, 8, 8, 520, True), (256, 8, 1, 7680, False), (192, 8, 2, 200, True),
                                             (256, 4, 1, 264, False)])
 def test_route_from_x_shapes(gpu, N, M, Kp, d, store):
-    # other expert counts (one, two and four 64-expert column groups; above 128 the stored-scores path
-    # splits the experts in halves over the XCDs and chooses in a second pass, the other path keeps the
-    # whole score row in one workgroup), ragged hidden sizes
+    # other expert counts (one, two and four 64-expert column groups; 300 tokens take the router split
+    # over slices of d, whose partial sums are added in a second pass that also makes the choice),
+    # ragged hidden sizes
     w = W.variant(W.decode(), T=300, d=d, N=N, M=M, Kp=Kp, std_bias=1.0)
     h = H.HostInputs(w)
     lg_ref = H.oracle_logits_all(h)
