@@ -625,7 +625,7 @@ static moge_status_t with_list_len(int kl, Fn&& f) {
 // of loads in flight per workgroup and no staging registers; x is read exactly
 // once.  One barrier per step.  The epilogue keeps the TM x NP score tile in LDS
 // for the softmax and the choices.
-template <int TM, int NP, int S, int WV, int KL>
+template <int TM, int NP, int S, int WV, int CB, int KL>
 __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, int N, int n_groups, int k,
                                                         const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ w,
@@ -640,7 +640,7 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   constexpr int CL = NI / WV;             // loads per step of the other waves
   constexpr int STAGE = ROWS * 64;
   constexpr int TB = TM / 32;        // token blocks; wave = token block + TB * expert slice
-  static_assert(TM * NP == 2048 * WV && S >= 4, "route tile: one 32 x 64 block per wave");
+  static_assert(TM * NP == 1024 * CB * WV && S >= 4, "route tile: one 32 x (32 CB) block per wave");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -699,26 +699,26 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
 
   const int kc = lane >> 5;
   const int arow = tb * 32 + (lane & 31);
-  int brow[2];
+  int brow[CB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) brow[cb] = TM + es * 64 + cb * 32 + (lane & 31);
-  auto frag = [&](int stage, int kk, bf16x8_t& a, bf16x8_t (&b)[2]) {
+  for (int cb = 0; cb < CB; ++cb) brow[cb] = TM + es * 32 * CB + cb * 32 + (lane & 31);
+  auto frag = [&](int stage, int kk, bf16x8_t& a, bf16x8_t (&b)[CB]) {
     const char* st = lds + stage * STAGE;
     const int c = kk * 2 + kc;
     a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + arow * 64 + ((c ^ lds_swz(arow)) << 4)));
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
       b[cb] = __builtin_bit_cast(bf16x8_t,
                                  *reinterpret_cast<const u32x4_t*>(st + brow[cb] * 64 + ((c ^ lds_swz(brow[cb])) << 4)));
   };
-  f32x16_t acc[2];
+  f32x16_t acc[CB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-  auto mfma = [&](const bf16x8_t& a, const bf16x8_t (&b)[2]) {
+  auto mfma = [&](const bf16x8_t& a, const bf16x8_t (&b)[CB]) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[cb], acc[cb], 0, 0, 0);
+    for (int cb = 0; cb < CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[cb], acc[cb], 0, 0, 0);
   };
 
   // prologue: steps 0 .. S-2 in flight; steps 0 and 1 landed
@@ -726,7 +726,7 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   for (int s = 0; s < S - 1; ++s) issue(s);
   wait_steps(nkf >= S - 1 ? S - 3 : 0, false);
   __syncthreads();
-  bf16x8_t a0, b0[2], a1, b1[2];
+  bf16x8_t a0, b0[CB], a1, b1[CB];
   frag(0, 0, a0, b0);
   for (int ks = 0; ks < nkf; ++ks) {
     issue(ks + S - 1);  // into stage (ks - 1) % S, last read before the previous barrier
@@ -763,8 +763,8 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   constexpr int LD = NP + 1;
   float* lt = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int col = es * 64 + cb * 32 + (lane & 31);
+  for (int cb = 0; cb < CB; ++cb) {
+    const int col = es * 32 * CB + cb * 32 + (lane & 31);
     const float b = (bias && col < N) ? bias[col] : 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -776,7 +776,7 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   tile_epilogue<KL>(lt, LD, TM, t0, T, N, n_groups, k, logits_out, idx, gate, gidx, ggate);
 }
 
-template <int TM, int NP, int S, int WV>
+template <int TM, int NP, int S, int WV, int CB>
 static moge_status_t launch_route_dma(const moge_shape_t& s, int kl, const void* x, const void* w, const float* bias,
                                       float* logits, int32_t* idx, float* gate, int32_t* gidx, float* ggate,
                                       hipStream_t stream) {
@@ -785,11 +785,11 @@ static moge_status_t launch_route_dma(const moge_shape_t& s, int kl, const void*
     constexpr size_t ring = (size_t)S * (TM + NP) * 64;
     constexpr size_t tile = (size_t)TM * (NP + 1) * 4;
     constexpr size_t lds = ring > tile ? ring : tile;
-    const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV, KL>);
+    const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV, CB, KL>);
     moge_status_t st = raise_dynamic_lds(kern, lds, "route_dma_kernel");
     if (st != MOGE_OK) return st;
     const int64_t grid = ((int64_t)s.T + TM - 1) / TM;
-    hipLaunchKernelGGL((route_dma_kernel<TM, NP, S, WV, KL>), dim3((unsigned)grid), dim3(64 * WV), lds, stream,
+    hipLaunchKernelGGL((route_dma_kernel<TM, NP, S, WV, CB, KL>), dim3((unsigned)grid), dim3(64 * WV), lds, stream,
                        (int64_t)s.T, s.d, s.N, s.M, s.k_per_group, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(w), bias, logits, idx, gate, gidx, ggate);
     return check_launch("route_dma_kernel");
@@ -1229,9 +1229,9 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
         return check_launch("route_mfma_splitk_kernel");
       });
     } else if (s.N <= 64) {
-      st = launch_route_dma<128, 64, 6, 4>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, stream);
+      st = launch_route_dma<128, 64, 6, 8, 1>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, stream);
     } else {
-      st = launch_route_dma<64, 128, 6, 4>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, stream);
+      st = launch_route_dma<64, 128, 6, 4, 2>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, stream);
     }
   }
   return st == MOGE_OK ? ok() : st;
