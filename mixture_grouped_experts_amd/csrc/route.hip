@@ -8,9 +8,9 @@
 // group are kept, which puts exactly K' of the token's assignments on each device.
 //
 // gfx950 design
-//   * bf16 scores, N <= 128: x [T][d] is streamed from HBM once.  A workgroup of 4
-//     waves owns TM tokens x NP experts (128 x 64 or 64 x 128), each wave a 32-token x
-//     64-expert block accumulated with v_mfma_f32_32x32x16_bf16 (float32).  Token rows
+//   * bf16 scores, N <= 128: x [T][d] is streamed from HBM once.  A workgroup owns TM
+//     tokens x NP experts (128 x 64 with 8 waves of one 32 x 32 block each, or 64 x 128
+//     with 4 waves of 32 x 64), accumulated with v_mfma_f32_32x32x16_bf16 (float32).  Token rows
 //     and router rows go from global memory straight into a 6-stage LDS ring with
 //     direct-to-LDS loads, several 32-element steps ahead.  Few tokens (fewer 128-token
 //     tiles than CUs): a split-K kernel whose operands go straight into registers.
@@ -616,9 +616,10 @@ static moge_status_t with_list_len(int kl, Fn&& f) {
 }
 
 // ----------------------------------------------------------------------------
-// bf16 scores, many tokens, N <= 128.  A workgroup of 4 waves owns TM tokens x NP experts
-// (NP = N rounded up to 64 or 128 and TM = 8192 / NP, so every wave owns one
-// 32-token x 64-expert block: two 32x32 accumulators).  The token rows and the
+// bf16 scores, many tokens, N <= 128.  A workgroup of WV waves owns TM tokens x NP experts
+// (NP = N rounded up to 64 or 128, TM = 8192 / NP), every wave one 32-token x 32 CB-expert
+// block of CB 32x32 accumulators: 8 waves of one block for 64 experts (twice the waves
+// to interleave the choice epilogue), 4 waves of two blocks for 128.  The token rows and the
 // router rows of each 32-element step go from global memory straight into an
 // S-stage LDS ring (global_load_lds_dwordx4, 16 rows of 64 bytes per instruction,
 // XOR-swizzled rows), S - 1 steps ahead, so x streams from HBM with several steps

@@ -187,7 +187,8 @@ TIE_CASES = [(300, 128, 64, 8, 1, "bf16", True), (300, 128, 64, 8, 2, "bf16", Fa
              (300, 128, 128, 4, 2, "bf16", True), (32832, 64, 128, 4, 2, "bf16", False),
              (520, 128, 256, 8, 1, "bf16", True), (520, 128, 256, 8, 1, "bf16", False),
              (300, 96, 16, 4, 1, "bf16", True), (64, 128, 8, 4, 1, "f32", True),
-             (5000, 64, 64, 8, 1, "bf16", False), (5000, 64, 128, 4, 2, "bf16", True)]
+             (5000, 64, 64, 8, 1, "bf16", False), (5000, 64, 128, 4, 2, "bf16", True),
+             (32832, 64, 16, 4, 1, "bf16", True), (32832, 96, 40, 5, 2, "bf16", False)]   # N < 64, one pass
 
 
 @pytest.mark.parametrize("T,d,N,M,Kp,dtype,store", TIE_CASES)
