@@ -88,10 +88,37 @@ def oracle_logits_all(h: HostInputs) -> np.ndarray:
     return oracle.logits(h.x_all(), h.w_router(), h.bias())
 
 
-def compare_routing(w: W.Workload, gpu_idx: np.ndarray, ref_idx: np.ndarray, ref_gap: np.ndarray):
-    """Returns (n_near_tie, flipped_token_ids, hard_failures)."""
+def order_gap(lg: np.ndarray, M: int, Kp: int, mode: str = "grouped") -> np.ndarray:
+    """Per token, the smallest softmax-probability gap between adjacent ranks 1 .. k + 1 inside
+    any group (k = K'; in global mode one group of all N experts with k = M K').  The slot order
+    of the chosen experts is their rank order, so where two chosen experts are this close,
+    float32 scores summed in another order may list them in the other order."""
+    l = lg.astype(np.float64)
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    T, N = p.shape
+    groups, k = (M, Kp) if mode == "grouped" else (1, M * Kp)
+    q = -np.sort(-p.reshape(T, groups, N // groups), axis=2)[:, :, :k + 1]
+    if q.shape[2] < 2:
+        return np.full(T, np.inf)
+    return (q[:, :, :-1] - q[:, :, 1:]).min(axis=(1, 2))
+
+
+def compare_routing(w: W.Workload, gpu_idx: np.ndarray, ref_idx: np.ndarray, ref_gap: np.ndarray,
+                    ord_gap: np.ndarray = None, mode: str = "grouped"):
+    """Returns (n_near_tie, flipped_token_ids, hard_failures).  A token may route differently
+    only when its K'-th vs (K'+1)-th in-group gap is a near-tie; with ord_gap (order_gap of the
+    same scores) it may also list the same experts of every group in another slot order when
+    that order rests on a near-tie between chosen experts."""
     diff = np.any(gpu_idx != ref_idx, axis=1)
     near = ref_gap < NEAR_TIE
-    flipped = np.nonzero(diff & near)[0]
-    hard = np.nonzero(diff & ~near)[0]
+    ok = near.copy()
+    if ord_gap is not None:
+        groups = w.M if mode == "grouped" else 1
+        T = gpu_idx.shape[0]
+        same_sets = np.all(np.sort(gpu_idx.reshape(T, groups, -1), axis=2) ==
+                           np.sort(ref_idx.reshape(T, groups, -1), axis=2), axis=(1, 2))
+        ok |= same_sets & (ord_gap < NEAR_TIE)
+    flipped = np.nonzero(diff & ok)[0]
+    hard = np.nonzero(diff & ~ok)[0]
     return int(near.sum()), flipped, hard

@@ -43,7 +43,7 @@ def check_layer(w, n_sample=None):
     lg = H.oracle_logits_all(hi)
     ridx, rgate, rgap = oracle.route(lg, w.M, w.Kp, "grouped")
     gidx = layer.idx.cpu().numpy()
-    n_near, flipped, hard = H.compare_routing(w, gidx, ridx, rgap)
+    n_near, flipped, hard = H.compare_routing(w, gidx, ridx, rgap, H.order_gap(lg, w.M, w.Kp))
     print(f"  near-tie {n_near}, flipped {len(flipped)}", flush=True)
     assert hard.size == 0
     # imbalance: MoGE 0 by construction, group loads T*K'; the global comparator on the same scores
@@ -182,3 +182,35 @@ def test_layer_check_scores(gpu):
     layer.logits[3, 5] = float("nan")
     with pytest.raises(moge.MogeError, match="NONFINITE"):
         layer.check_scores()
+
+
+def _random_shapes(n, seed):
+    """Seeded layer shapes across the validated range: N up to 256 with every group size,
+    K' from 1 to the group size, hidden sizes on and off the 32-column grid (the gathered and
+    the copied token rows), narrow and ragged expert widths, routing-only layers, shared experts,
+    expert ranges, both dtypes and a skewing router bias."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.choice([1, 8, 12, 16, 40, 64, 96, 128, 200, 256]))
+        divs = [m for m in range(1, min(N, 8) + 1) if N % m == 0]
+        M = int(rng.choice(divs))
+        Kp = int(rng.integers(1, min(N // M, 4) + 1))
+        T = int(rng.choice([1, 7, 63, 300, 777, 1500]))
+        d = int(8 * rng.integers(1, 65))                      # 8 .. 512
+        F = int(rng.choice([0, 8 * int(rng.integers(1, 49))]))  # routing only, or 8 .. 384
+        dtype = "f32" if rng.random() < 0.2 else "bf16"
+        Fs = int(8 * rng.integers(1, 33)) if F and rng.random() < 0.3 else 0
+        lo = int(rng.integers(0, N))
+        hi = int(rng.integers(lo + 1, N + 1))
+        out.append(W.variant(W.decode(), name=f"rand{seed}_{i}_T{T}_d{d}_N{N}_M{M}_K{Kp}_F{F}_S{Fs}_{dtype}_{lo}_{hi}",
+                             T=T, d=d, N=N, M=M, Kp=Kp, F=F, F_shared=Fs, dtype=dtype,
+                             std_bias=float(rng.choice([0.0, 1.0, 3.0])), std_shared_down=0.02 if Fs else 0.0,
+                             e_lo=lo, e_hi=hi, seed=int(seed * 100 + i)))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_shapes(16, 7), ids=lambda w: w.name)
+def test_layer_random_shapes(gpu, w):
+    # every token against the oracle on seeded shapes drawn across the validated range
+    check_layer(w)

@@ -117,7 +117,7 @@ def test_route_from_x(gpu, w):
     scale = 1.0 + np.abs(lg_ref).max()
     assert np.abs(lg - lg_ref).max() <= 1e-4 * scale
     ridx, rgate, rgap = oracle.route(lg_ref, w.M, w.Kp, "grouped")
-    n_near, flipped, hard = H.compare_routing(w, idx, ridx, rgap)
+    n_near, flipped, hard = H.compare_routing(w, idx, ridx, rgap, H.order_gap(lg_ref, w.M, w.Kp))
     print(f"  near-tie tokens {n_near}, flipped {len(flipped)}", flush=True)
     assert hard.size == 0, f"{hard.size} non-near-tie tokens routed differently"
     same = np.all(idx == ridx, axis=1)
@@ -156,7 +156,7 @@ def test_route_from_x_shapes(gpu, N, M, Kp, d, store):
     if store:
         assert np.abs(lg - lg_ref).max() <= 1e-4 * (1.0 + np.abs(lg_ref).max())
     ridx, _, rgap = oracle.route(lg_ref, M, Kp, "grouped")
-    _, _, hard = H.compare_routing(w, idx, ridx, rgap)
+    _, _, hard = H.compare_routing(w, idx, ridx, rgap, H.order_gap(lg_ref, M, Kp))
     assert hard.size == 0
 
 
