@@ -210,7 +210,7 @@ def _random_shapes(n, seed):
     return out
 
 
-@pytest.mark.parametrize("w", _random_shapes(16, 7), ids=lambda w: w.name)
+@pytest.mark.parametrize("w", _random_shapes(16, 7) + _random_shapes(16, 11), ids=lambda w: w.name)
 def test_layer_random_shapes(gpu, w):
     # every token against the oracle on seeded shapes drawn across the validated range
     check_layer(w)
