@@ -474,6 +474,22 @@ __device__ __forceinline__ void choose_g8(const float* __restrict__ lt, int ld, 
       key[i] = order_key(key[i]);
       id[i] = own ? g * 8 + i : 0x7FFFFFFF;
     }
+    const int64_t t = t0 + r;
+    if (!gidx && k == 1) {  // MoGE alone with one expert per group: the group's best, no sort
+      float bk = key[0];
+      int bid = id[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {  // ids ascend, so a later equal score never wins
+        const bool take = key[i] > bk;
+        bk = take ? key[i] : bk;
+        bid = take ? id[i] : bid;
+      }
+      if (own) {
+        idx[t * K + g] = bid;
+        gate[t * K + g] = prob(bk);
+      }
+      continue;
+    }
     auto ce = [&](int a, int b) {  // a before b: higher score, then lower id
       const bool keep = key[a] > key[b] || (key[a] == key[b] && id[a] < id[b]);
       const float ka = key[a], kb = key[b];
@@ -489,7 +505,6 @@ __device__ __forceinline__ void choose_g8(const float* __restrict__ lt, int ld, 
     ce(2, 4); ce(3, 5);
     ce(1, 4); ce(3, 6);
     ce(1, 2); ce(3, 4); ce(5, 6);
-    const int64_t t = t0 + r;
     if (idx && own) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
