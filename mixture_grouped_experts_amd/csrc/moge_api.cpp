@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <map>
+#include <utility>
 #include <mutex>
 #include <string>
 
@@ -49,10 +50,13 @@ moge_status_t validate_shape(const moge_shape_t* s) {
 }
 
 moge_status_t raise_dynamic_lds(const void* kernel, size_t bytes, const char* what) {
+  // the attribute is set once per (device, kernel): a process may drive several GPUs
   static std::mutex mu;
-  static std::map<const void*, size_t> done;
+  static std::map<std::pair<int, const void*>, size_t> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOGE_ERR_HIP, std::string(what) + ": no current device");
   std::lock_guard<std::mutex> lock(mu);
-  size_t& have = done[kernel];
+  size_t& have = done[{dev, kernel}];
   if (bytes <= have) return MOGE_OK;
   const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess)
