@@ -12,15 +12,15 @@
 //     tokens x NP experts (128 x 64 with 8 waves of one 32 x 32 block each, or 64 x 128
 //     with 4 waves of 32 x 64), accumulated with v_mfma_f32_32x32x16_bf16 (float32).  Token rows
 //     and router rows go from global memory straight into a 6-stage LDS ring with
-//     direct-to-LDS loads, several 32-element steps ahead.  Few tokens (fewer 128-token
-//     tiles than CUs): a split-K kernel whose operands go straight into registers.
-//   * bf16 scores, 128 < N <= 256, and few tokens (at most 4096) at any N: split over the
-//     hidden dimension.  Workgroup b takes slice b % S of the reduction (S chosen so the
-//     token tiles times S fill the chip: up to 4 for many tokens, up to 32 for few) of a
-//     128-token x 256-expert tile; workgroup b runs on XCD b % 8, so an XCD only ever
-//     reads its slices of the router matrix, which stay in its L2, and x is read from HBM
-//     exactly once.  Slice partial sums go to the workspace; a second kernel adds them in
-//     slice order (deterministic), adds the bias and chooses.
+//     direct-to-LDS loads, several 32-element steps ahead.  With fewer token tiles than
+//     CUs the same kernel runs in slices of the hidden dimension (workgroup b: slice
+//     b % S of token tile b / S) and writes partial sums instead of choosing.
+//   * bf16 scores, 128 < N <= 256: split over the hidden dimension too, with a
+//     128-token x 256-expert tile (S up to 4 for many tokens, up to 32 for few);
+//     workgroup b runs on XCD b % 8, so an XCD only ever reads its slices of the router
+//     matrix, which stay in its L2, and x is read from HBM exactly once.
+//   * Slice partial sums go to the workspace; a second kernel adds them in slice order
+//     (deterministic), adds the bias and chooses.
 //   * The choice (one epilogue for every kernel): the score tile sits in LDS; lane
 //     (token, group) keeps its group's best experts in a sorted register list; the
 //     token's softmax max and sum are butterflies over its lanes; MoGE takes the first
@@ -648,7 +648,7 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ logits_out, int32_t* __restrict__ idx,
                                                         float* __restrict__ gate, int32_t* __restrict__ gidx,
-                                                        float* __restrict__ ggate) {
+                                                        float* __restrict__ ggate, int nsl, float* __restrict__ part) {
   constexpr int ROWS = TM + NP;      // stage rows of 64 bytes: tokens, then experts
   constexpr int NI = ROWS / 16;      // load instructions per step
   constexpr int NJ = (NI + WV - 1) / WV;  // per wave, at most
@@ -661,14 +661,20 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tb = wave % TB, es = wave / TB;
-  const int64_t t0 = (int64_t)blockIdx.x * TM;
+  // nsl > 1: the slice mode -- workgroup b computes slice b % nsl of the reduction (steps
+  // k0 .. k1 - 1 of d / 32) for token tile b / nsl and writes the float32 partial sums to
+  // part[slice][t][e] (the reduction kernel adds them and chooses); nsl == 1: one pass
+  const int slice = (int)(blockIdx.x % nsl);
+  const int64_t t0 = (int64_t)(blockIdx.x / nsl) * TM;
   const int nkf = d / 32;                        // full steps; a ragged tail follows the loop
+  const int k0 = (int)((int64_t)nkf * slice / nsl);
+  const int nks = (int)((int64_t)nkf * (slice + 1) / nsl) - k0;  // this workgroup's steps
   // token tiles start at different steps (and wrap around), so the workgroups do not all
   // read the same column range of their rows at once: each tile walks 64-byte pieces of
   // rows 8 KiB apart, and in a plain streaming probe of that pattern the staggered start
   // reads 9% faster (router -11% on 65536 tokens x 4096).  The order of the float32
   // accumulation over k then depends on the tile; scores stay within the tolerance.
-  const int krot = nkf > 0 ? (int)(((t0 / TM) * 37) % nkf) : 0;
+  const int krot = nks > 0 ? (int)(((t0 / TM) * 37) % nks) : 0;
   const bool many = (NI % WV == 0) || wave < (NI % WV);  // this wave issues CH loads per step, else CL
 
   // load j of this wave moves stage rows 16 i .. 16 i + 15 with i = wave + WV j
@@ -689,12 +695,12 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   }
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int ks) {
-    if (ks >= nkf) return;
+    if (ks >= nks) return;
     const uint32_t st = lds0 + (uint32_t)((ks % S) * STAGE);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       if (wave + WV * j < NI) {
-        const int kk = ks + krot < nkf ? ks + krot : ks + krot - nkf;
+        const int kk = k0 + (ks + krot < nks ? ks + krot : ks + krot - nks);
         dma_16x64(src[j] + kk * 32, st + (uint32_t)(16 * (wave + WV * j) * 64));
       }
   };
@@ -740,21 +746,21 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   // prologue: steps 0 .. S-2 in flight; steps 0 and 1 landed
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s);
-  wait_steps(nkf >= S - 1 ? S - 3 : 0, false);
+  wait_steps(nks >= S - 1 ? S - 3 : 0, false);
   __syncthreads();
   bf16x8_t a0, b0[CB], a1, b1[CB];
   frag(0, 0, a0, b0);
-  for (int ks = 0; ks < nkf; ++ks) {
+  for (int ks = 0; ks < nks; ++ks) {
     issue(ks + S - 1);  // into stage (ks - 1) % S, last read before the previous barrier
     frag(ks % S, 1, a1, b1);
     mfma(a0, b0);
     frag((ks + 1) % S, 0, a0, b0);  // read-ahead (unused after the last step)
     mfma(a1, b1);
     // step ks + 2 landed (every step is waited for once the tail issues no more)
-    wait_steps(ks + S - 1 < nkf ? S - 3 : 0, true);
+    wait_steps(ks + S - 1 < nks ? S - 3 : 0, true);
     __syncthreads();
   }
-  if (d % 32) {
+  if ((d % 32) && slice == nsl - 1) {
     // ragged tail: one step through registers, columns at or past d are zero
     const int kt = nkf * 32;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
@@ -775,6 +781,19 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
     __syncthreads();
   }
 
+  if (nsl > 1) {  // partial sums of this slice (no bias: the reduction adds it once)
+    float* dst = part + (int64_t)slice * T * N;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = es * 32 * CB + cb * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = t0 + tb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (col < N && row < T) dst[row * N + col] = acc[cb][r];
+      }
+    }
+    return;
+  }
   // scores -> LDS tile [TM][NP + 1] (odd row stride); padded experts get -inf
   constexpr int LD = NP + 1;
   float* lt = reinterpret_cast<float*>(lds);
@@ -795,7 +814,7 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
 template <int TM, int NP, int S, int WV, int CB>
 static moge_status_t launch_route_dma(const moge_shape_t& s, int kl, const void* x, const void* w, const float* bias,
                                       float* logits, int32_t* idx, float* gate, int32_t* gidx, float* ggate,
-                                      hipStream_t stream) {
+                                      int nsl, float* part, hipStream_t stream) {
   return with_list_len(kl, [&](auto klc) {
     constexpr int KL = decltype(klc)::value;
     constexpr size_t ring = (size_t)S * (TM + NP) * 64;
@@ -804,16 +823,16 @@ static moge_status_t launch_route_dma(const moge_shape_t& s, int kl, const void*
     const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV, CB, KL>);
     moge_status_t st = raise_dynamic_lds(kern, lds, "route_dma_kernel");
     if (st != MOGE_OK) return st;
-    const int64_t grid = ((int64_t)s.T + TM - 1) / TM;
+    const int64_t grid = ((int64_t)s.T + TM - 1) / TM * nsl;
     hipLaunchKernelGGL((route_dma_kernel<TM, NP, S, WV, CB, KL>), dim3((unsigned)grid), dim3(64 * WV), lds, stream,
                        (int64_t)s.T, s.d, s.N, s.M, s.k_per_group, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(w), bias, logits, idx, gate, gidx, ggate);
+                       static_cast<const uint16_t*>(w), bias, logits, idx, gate, gidx, ggate, nsl, part);
     return check_launch("route_dma_kernel");
   });
 }
 
 // ----------------------------------------------------------------------------
-// bf16 scores split over the hidden dimension (128 < N <= 256, or few tokens at any N).
+// bf16 scores split over the hidden dimension, 128 < N <= 256.
 // Workgroup b computes slice b % S of the reduction (its steps k0 .. k1 - 1 of d / 32) for
 // the 128-token x 256-expert tile b / S, and stores the float32 partial sums to
 // part[slice][t][e].  8 waves; wave w owns tokens (w / 4) * 64 .. + 64 and experts
@@ -964,11 +983,31 @@ __host__ __forceinline__ int route_slices(int64_t T, int d) {
   return S;
 }
 
-// bf16 scores from x go through the split kernel and the reduction for more than 128
-// experts, and for few tokens (at most 32 token tiles) at any expert count: there the split
-// spreads the reduction over many workgroups instead of a handful.
-__host__ __forceinline__ bool route_split(const moge_shape_t& s) {
-  return s.dtype == MOGE_BF16 && (s.N > 128 || (int64_t)s.T <= 32 * kPartTM);
+// How bf16 scores from x are computed: kind 0 one pass (the one-pass kernel, or its
+// token tiles fill the CUs); kind 1 the one-pass kernel in slices of d plus the reduction
+// (N <= 128 with fewer token tiles than CUs); kind 2 the 256-expert split kernel plus the
+// reduction (N > 128).
+struct RoutePlan {
+  int kind;
+  int S;  // slices of d (1 for one pass)
+};
+__host__ __forceinline__ int dma_tile_tokens(int N) { return N <= 64 ? 128 : 64; }
+// Slices for the one-pass kernel's slice mode: until the token tiles times the slices give
+// two 72 KiB workgroups per CU, at most 32, every slice keeping at least 2 steps of 32.
+__host__ __forceinline__ int dma_slices(int64_t T, int d, int N) {
+  const int64_t tiles = (T + dma_tile_tokens(N) - 1) / dma_tile_tokens(N);
+  const int nkf = d / 32;
+  int S = 1;
+  while (S < 32 && tiles * S < 512 && nkf / (2 * S) >= 2) S <<= 1;
+  return S;
+}
+__host__ __forceinline__ RoutePlan route_plan(const moge_shape_t& s) {
+  if (s.dtype != MOGE_BF16) return RoutePlan{0, 1};
+  if (s.N > 128) return RoutePlan{2, route_slices(s.T, s.d)};
+  const int64_t tiles = ((int64_t)s.T + dma_tile_tokens(s.N) - 1) / dma_tile_tokens(s.N);
+  if (tiles >= 256) return RoutePlan{0, 1};
+  const int S = dma_slices(s.T, s.d, s.N);
+  return S > 1 ? RoutePlan{1, S} : RoutePlan{0, 1};
 }
 
 // The split kernel's partial sums -> scores -> the choices.  8 tokens per workgroup (many
@@ -1021,83 +1060,6 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int
   tile_epilogue<KL>(lt, ld, (int)nrows, t0, T, N, M, k, logits_out, idx, gate, gidx, ggate);
 }
 
-// ----------------------------------------------------------------------------
-// bf16 scores for few tokens: 32 tokens per workgroup; the 4 waves split the
-// experts (WC column groups of 64) and the hidden dimension (4/WC parts), so a
-// small batch still spreads over many waves.  Operands are read straight from
-// global memory in MFMA layout; the partial sums meet in LDS and are added in a
-// fixed order (deterministic).
-template <int WC, int KL>
-__global__ __launch_bounds__(256) void route_mfma_splitk_kernel(int64_t T, int d, int N, int n_groups, int k,
-                                                                const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ w,
-                                                                const float* __restrict__ bias,
-                                                                float* __restrict__ logits_out,
-                                                                int32_t* __restrict__ idx, float* __restrict__ gate,
-                                                                int32_t* __restrict__ gidx,
-                                                                float* __restrict__ ggate) {
-  constexpr int KS = 4 / WC;
-  constexpr int NP = 64 * WC;
-  constexpr int TM = 32;
-  __shared__ __attribute__((aligned(16))) float part[KS * TM * NP];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wc = wave % WC, q = wave / WC;
-  const int64_t t0 = (int64_t)blockIdx.x * TM;
-  int64_t arow = t0 + (lane & 31);
-  if (arow > T - 1) arow = T - 1;
-  const uint16_t* ap = x + arow * d + (lane >> 5) * 8;
-  const uint16_t* bp[2];
-  bool bval[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int col = wc * 64 + cb * 32 + (lane & 31);
-    bval[cb] = col < N;
-    bp[cb] = w + (int64_t)(col < N ? col : 0) * d + (lane >> 5) * 8;
-  }
-  f32x16_t acc[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-  const int nk = (d + 63) / 64;
-  for (int ks = q; ks < nk; ks += KS) {
-    u32x4_t a[4], b[2][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = ks * 64 + j * 16 + (lane >> 5) * 8;
-      const u32x4_t zero = {0u, 0u, 0u, 0u};
-      a[j] = kk < d ? *reinterpret_cast<const u32x4_t*>(ap + ks * 64 + j * 16) : zero;
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        b[cb][j] = (kk < d && bval[cb]) ? *reinterpret_cast<const u32x4_t*>(bp[cb] + ks * 64 + j * 16) : zero;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
-                                                          __builtin_bit_cast(bf16x8_t, b[cb][j]), acc[cb], 0, 0, 0);
-  }
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int col = wc * 64 + cb * 32 + (lane & 31);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      part[(q * TM + row) * NP + col] = acc[cb][r];
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < TM * NP; i += 256) {
-    const int col = i % NP;
-    float v = part[i];
-#pragma unroll
-    for (int p = 1; p < KS; ++p) v += part[p * TM * NP + i];
-    part[i] = col < N ? v + (bias ? bias[col] : 0.f) : -INFINITY;
-  }
-  __syncthreads();
-  tile_epilogue<KL>(part, NP, TM, t0, T, N, n_groups, k, logits_out, idx, gate, gidx, ggate);
-}
 
 // ----------------------------------------------------------------------------
 // float32 scores on the vector ALUs (small shapes).  16 tokens per workgroup.
@@ -1164,11 +1126,12 @@ __global__ __launch_bounds__(256) void route_select_kernel(int64_t T, int N, int
 
 using namespace moge;
 
-// Bytes of workspace the scores need: the split kernel's partial sums for bf16 shapes with
-// more than 128 experts (x given), else none.
+// Bytes of workspace the scores need: the partial sums of a reduction split over slices of d
+// (bf16 scores from x, plan kinds 1 and 2), else none.
 size_t moge::route_workspace_bytes(const moge_shape_t& s) {
-  if (!route_split(s)) return 0;
-  return (size_t)route_slices(s.T, s.d) * (size_t)s.T * (size_t)s.N * sizeof(float);
+  const RoutePlan pl = route_plan(s);
+  if (pl.kind == 0) return 0;
+  return (size_t)pl.S * (size_t)s.T * (size_t)s.N * sizeof(float);
 }
 
 // Scores (from x, or the caller's) and the choices: MoGE into idx/gate when idx is set, the
@@ -1209,45 +1172,33 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
                          logits, idx, gate, gidx, ggate);
       return check_launch("route_f32_kernel");
     });
-  } else if (route_split(s)) {
-    const int S = route_slices(s.T, s.d);
-    constexpr size_t lds = (size_t)kPartStages * (kPartTM + kPartNP) * 64;
-    st = raise_dynamic_lds(reinterpret_cast<const void*>(route_part_kernel), lds, "route_part_kernel");
-    if (st != MOGE_OK) return st;
-    const int64_t grid = ((int64_t)s.T + kPartTM - 1) / kPartTM * S;
-    float* part = static_cast<float*>(ws);
-    hipLaunchKernelGGL(route_part_kernel, dim3((unsigned)grid), dim3(512), lds, stream, (int64_t)s.T, s.d, s.N, S,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), part);
-    if ((st = check_launch("route_part_kernel")) != MOGE_OK) return st;
-    const int tpw = kReduceTokens;
-    st = with_list_len(kl, [&](auto klc) {
-      constexpr int KL = decltype(klc)::value;
-      hipLaunchKernelGGL(route_reduce_kernel<KL>,
-                         dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256), 0, stream,
-                         (int64_t)s.T, s.N, s.M, s.k_per_group, S, part, bias, logits, idx, gate, gidx, ggate);
-      return check_launch("route_reduce_kernel");
-    });
   } else {
-    // fewer 128-token tiles than CUs (and more than the split path takes): the split-K kernel
-    const bool few = ((int64_t)s.T + 127) / 128 < 256;
-    const int64_t sgrid = ((int64_t)s.T + 31) / 32;
-    if (few) {
+    const RoutePlan pl = route_plan(s);
+    float* part = static_cast<float*>(ws);
+    if (pl.kind == 2) {
+      constexpr size_t lds = (size_t)kPartStages * (kPartTM + kPartNP) * 64;
+      st = raise_dynamic_lds(reinterpret_cast<const void*>(route_part_kernel), lds, "route_part_kernel");
+      if (st != MOGE_OK) return st;
+      const int64_t grid = ((int64_t)s.T + kPartTM - 1) / kPartTM * pl.S;
+      hipLaunchKernelGGL(route_part_kernel, dim3((unsigned)grid), dim3(512), lds, stream, (int64_t)s.T, s.d, s.N,
+                         pl.S, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), part);
+      st = check_launch("route_part_kernel");
+    } else if (s.N <= 64) {
+      st = launch_route_dma<128, 64, 6, 8, 1>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, pl.S, part,
+                                              stream);
+    } else {
+      st = launch_route_dma<64, 128, 6, 4, 2>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, pl.S, part,
+                                              stream);
+    }
+    if (st == MOGE_OK && pl.kind != 0) {  // the slices' partial sums -> scores -> the choices
+      const int tpw = kReduceTokens;
       st = with_list_len(kl, [&](auto klc) {
         constexpr int KL = decltype(klc)::value;
-        if (s.N <= 64)
-          hipLaunchKernelGGL((route_mfma_splitk_kernel<1, KL>), dim3((unsigned)sgrid), dim3(256), 0, stream,
-                             (int64_t)s.T, s.d, s.N, s.M, s.k_per_group, static_cast<const uint16_t*>(x),
-                             static_cast<const uint16_t*>(w_router), bias, logits, idx, gate, gidx, ggate);
-        else
-          hipLaunchKernelGGL((route_mfma_splitk_kernel<2, KL>), dim3((unsigned)sgrid), dim3(256), 0, stream,
-                             (int64_t)s.T, s.d, s.N, s.M, s.k_per_group, static_cast<const uint16_t*>(x),
-                             static_cast<const uint16_t*>(w_router), bias, logits, idx, gate, gidx, ggate);
-        return check_launch("route_mfma_splitk_kernel");
+        hipLaunchKernelGGL(route_reduce_kernel<KL>, dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256), 0,
+                           stream, (int64_t)s.T, s.N, s.M, s.k_per_group, pl.S, part, bias, logits, idx, gate, gidx,
+                           ggate);
+        return check_launch("route_reduce_kernel");
       });
-    } else if (s.N <= 64) {
-      st = launch_route_dma<128, 64, 6, 8, 1>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, stream);
-    } else {
-      st = launch_route_dma<64, 128, 6, 4, 2>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, stream);
     }
   }
   return st == MOGE_OK ? ok() : st;

@@ -120,7 +120,12 @@ def test_null_and_argument_errors_before_any_launch():
     assert need == 2 * 1000 * 256 * 4          # 8 token tiles, d = 128: 4 steps of 32, 2 slices of 2 steps
     assert moge.workspace_size(S(T=1000, d=7680, N=256, M=8), moge.STAGE_ROUTE) == 32 * 1000 * 256 * 4
     assert moge.workspace_size(S(T=8192, d=7680, N=256, M=8), moge.STAGE_ROUTE) == 4 * 8192 * 256 * 4
-    assert moge.workspace_size(S(T=5000, N=64, M=8), moge.STAGE_ROUTE) == 0             # one pass, no split
+    # up to 128 experts: the one-pass kernel, in slices of d while its token tiles do not fill the CUs
+    assert moge.workspace_size(S(T=65536, d=4096, N=64, M=8), moge.STAGE_ROUTE) == 0    # 512 tiles: one pass
+    assert moge.workspace_size(S(T=5000, N=64, M=8), moge.STAGE_ROUTE) == 2 * 5000 * 64 * 4   # d = 128: 2 slices
+    assert moge.workspace_size(S(T=8192, d=5120, N=64, M=8), moge.STAGE_ROUTE) == 8 * 8192 * 64 * 4
+    assert moge.workspace_size(S(T=5000, d=64, N=64, M=8), moge.STAGE_ROUTE) == 0      # 2 steps: no split
+    assert moge.workspace_size(S(T=16384, d=4096, N=128, M=8), moge.STAGE_ROUTE) == 0  # 256 tiles of 64
     assert moge.workspace_size(S(dt=moge.F32), moge.STAGE_ROUTE) == 0
     assert lib.moge_route(ctypes.byref(s256), 0, fake, fake, None, None, fake, fake, fake, need - 1, None) == 4
     assert lib.moge_route(ctypes.byref(s256), 0, fake, fake, None, None, fake, fake, None, 0, None) == 4
