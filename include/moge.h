@@ -21,7 +21,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates or frees device memory and keeps no state between calls
  *     (every setting, such as the expert GEMMs' tile shape, travels with the
- *     call in moge_shape_t).
+ *     call in moge_shape_t).  The one exception is moge_dispatch_noalloc's fixed
+ *     device array, described there.
  *   - Tensors are contiguous.  x, logits, idx, gate, inv, the expert outputs
  *     and y are row-major; the operands of the expert GEMMs use the tiled
  *     layout described at moge_tiled_elems.  Weights come in the
@@ -37,7 +38,8 @@
  *   - Every call validates its arguments on the host BEFORE any launch and
  *     returns a status; on error nothing is launched and moge_last_error()
  *     (per thread) describes the problem.  On success the work is enqueued on
- *     `stream` and the call returns without waiting for it.
+ *     `stream` and the call returns without waiting for it (moge_check_finite,
+ *     a checking call, is the one that waits).
  *   - Calls on different streams are independent; the library is re-entrant.
  */
 #ifndef MOGE_H
