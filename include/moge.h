@@ -180,8 +180,10 @@ moge_status_t moge_round_bf16(const float* x, uint16_t* y, int64_t n, hipStream_
  *            over all N scores (not renormalised over the chosen experts).
  *   ws       device workspace of moge_workspace_size(shape, MOGE_STAGE_ROUTE)
  *            bytes: the partial sums of a reduction split over slices of d, for
- *            bf16 scores from x with N > 128 or T <= 4096; 0 bytes (NULL allowed)
- *            for every other call.  MOGE_ERR_WORKSPACE if missing or too small.
+ *            bf16 scores from x with N > 128, or with N <= 128, d >= 128 and
+ *            fewer than 256 token tiles (tiles of 128 tokens for N <= 64, of 64
+ *            for N <= 128: T <= 32640 or T <= 16320); 0 bytes (NULL allowed) for
+ *            every other call.  MOGE_ERR_WORKSPACE if missing or too small.
  * Slot order: GROUPED -> slot = g*K' + rank inside group g; GLOBAL -> slot = rank.
  * rank orders experts by score, higher first, equal scores -> lower expert id
  * (-0 and +0 are equal).

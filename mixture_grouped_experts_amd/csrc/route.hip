@@ -564,6 +564,88 @@ __device__ __forceinline__ void choose_g8(const float* __restrict__ lt, int ld, 
   }
 }
 
+// At most 64 experts, one wave per token, lane e owning expert e: every choice is the rank
+// definition itself, counted.  rank_key packs (score, id) into one 64-bit integer ordered as
+// the choice orders experts -- higher score first, then lower id; NaN ranks as -inf, -0
+// equals +0 -- so rank(e) = #{e' : key(e') > key(e)}, over the token for the global top-K
+// (slot rank) and over e's group for MoGE (slot g*k + rank).  The keys go through a
+// 64-entry LDS row per wave.  Unique ranks, so the same choices as the lists, and the
+// gates in the lists' arithmetic: the softmax denominator sums each group's exponentials
+// in id order, then the groups' sums pairwise (g with g ^ 1, then g ^ 2, ...), so a gate
+// is bit-identical to the one the lists give from the same scores.  For few tokens per
+// workgroup (the reduction after a split), where the lists' serial rounds would keep all
+// but one wave of the workgroup idle.
+constexpr int kListRank = 65;  // the host's code for this form
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  uint32_t u = __builtin_bit_cast(uint32_t, order_key(v));
+  if (u == 0x80000000u) u = 0u;                    // -0 -> +0
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // float order -> unsigned order
+  return ((uint64_t)u << 32) | (uint32_t)(63 - e); // equal scores: the lower id is the larger key
+}
+__device__ __forceinline__ void choose_rank64(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
+                                              int N, int M, int k, int32_t* __restrict__ idx,
+                                              float* __restrict__ gate, int32_t* __restrict__ gidx,
+                                              float* __restrict__ ggate, uint64_t* __restrict__ keys) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int G = N / M, K = M * k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const bool own = lane < N;
+  const int g = own ? lane / G : 0;
+  const int j = lane - g * G;  // the lane's place in its group (own lanes)
+  int Mp = 1;
+  while (Mp < M) Mp <<= 1;
+  uint64_t* kw = keys + wave * 64;
+  for (int r = wave; r < rows; r += nw) {  // wave-uniform
+    const int64_t t = t0 + r;
+    if (t >= T) break;
+    const float* row = lt + r * ld;
+    const float v = own ? row[lane] : -INFINITY;
+    float m = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, partner_f(m, off));
+    const float ml = m * kLog2e;
+    float z = 0.f;
+    if (own) {
+      for (int i = 0; i < G; ++i) z += __builtin_amdgcn_exp2f(__builtin_fmaf(row[g * G + i], kLog2e, -ml));
+    }
+    for (int off = 1; off < Mp; off <<= 1) {  // every lane takes part in the exchange
+      const int pg = g ^ off;
+      const float o = __shfl(z, (pg < M ? pg : g) * G + j, 64);
+      z += pg < M ? o : 0.f;  // a group past M adds nothing, as its empty lane does in the lists
+    }
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(order_key(v), kLog2e, -ml)) * __builtin_amdgcn_rcpf(z);
+    const uint64_t key = rank_key(v, lane);
+    kw[lane] = key;
+    // the row's keys are read by every lane of this wave only: LDS runs one wave's
+    // accesses in order, the fences keep the compiler from moving them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (idx) {
+      const int base = g * G;
+      int rank = 0;
+      for (int i = 0; i < G; ++i) rank += kw[base + i] > key ? 1 : 0;
+      if (own && rank < k) {
+        idx[t * K + g * k + rank] = lane;
+        gate[t * K + g * k + rank] = p;
+      }
+    }
+    if (gidx) {
+      int rank = 0;
+#pragma unroll 8
+      for (int e = 0; e < N; ++e) rank += kw[e] > key ? 1 : 0;
+      if (own && rank < K) {
+        gidx[t * K + rank] = lane;
+        ggate[t * K + rank] = p;
+      }
+    }
+    // every lane's reads of this row come before the next row's writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // The choices of the older per-mode forms, for shapes past the lists' limits: lane-parallel
 // rank rounds per (token, group) or one wave per token.
 __device__ __forceinline__ void choose_fallback(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
@@ -585,21 +667,25 @@ __device__ __forceinline__ void choose_fallback(const float* __restrict__ lt, in
 // into idx/gate when idx is set, the global top-K into gidx/ggate when gidx is set.  KL is
 // lane_list_len of the call (the host picks the kernel instance): the lists' length, or 0
 // for the fallback forms.  (all threads of the block call it)
+// The scores go out with the non-temporal hint: every tile writes them at the same time
+// at the end of the kernel, and streamed past the L2 they no longer wait there for the
+// kernel's final write-back (the route kernel at 65536 tokens x 4096 x 64 experts was 4%
+// faster).
+__device__ __forceinline__ void store_scores(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
+                                             int N, float* __restrict__ logits_out) {
+  if (!logits_out) return;
+  for (int i = threadIdx.x; i < rows * N; i += blockDim.x) {
+    const int r = i / N, c = i - r * N;
+    if (t0 + r < T) __builtin_nontemporal_store(lt[r * ld + c], logits_out + (t0 + r) * N + c);
+  }
+}
+
 template <int KL>
 __device__ __forceinline__ void tile_epilogue(const float* __restrict__ lt, int ld, int rows, int64_t t0, int64_t T,
                                               int N, int M, int k, float* __restrict__ logits_out,
                                               int32_t* __restrict__ idx, float* __restrict__ gate,
                                               int32_t* __restrict__ gidx, float* __restrict__ ggate) {
-  // The scores go out with the non-temporal hint: every tile writes them at the same
-  // time at the end of the kernel, and streamed past the L2 they no longer wait there
-  // for the kernel's final write-back (the route kernel at 65536 tokens x 4096 x 64
-  // experts was 4% faster).
-  if (logits_out) {
-    for (int i = threadIdx.x; i < rows * N; i += blockDim.x) {
-      const int r = i / N, c = i - r * N;
-      if (t0 + r < T) __builtin_nontemporal_store(lt[r * ld + c], logits_out + (t0 + r) * N + c);
-    }
-  }
+  store_scores(lt, ld, rows, t0, T, N, logits_out);
   if constexpr (KL == kListG8) {
     if (M <= 1) choose_g8<1>(lt, ld, rows, t0, T, M, k, idx, gate, gidx, ggate);
     else if (M <= 2) choose_g8<2>(lt, ld, rows, t0, T, M, k, idx, gate, gidx, ggate);
@@ -1013,7 +1099,8 @@ __host__ __forceinline__ RoutePlan route_plan(const moge_shape_t& s) {
 // The split kernel's partial sums -> scores -> the choices.  8 tokens per workgroup (many
 // workgroups, so every CU has several tiles' loads in flight): the S slices of each score
 // are added in slice order (bit-identical results run to run), plus the bias, into an LDS
-// tile [8][N + 1]; then the common epilogue.
+// tile [8][N + 1]; then the choice: the rank count (KL = kListRank, at most 64 experts: each
+// of the 4 waves takes 2 of the tokens) or the common epilogue.
 constexpr int kReduceTokens = 8;
 template <int KL>
 __global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int M, int k, int S,
@@ -1057,7 +1144,13 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int
     }
   }
   __syncthreads();
-  tile_epilogue<KL>(lt, ld, (int)nrows, t0, T, N, M, k, logits_out, idx, gate, gidx, ggate);
+  if constexpr (KL == kListRank) {
+    __shared__ uint64_t keys[4 * 64];  // one row per wave (256 threads)
+    store_scores(lt, ld, (int)nrows, t0, T, N, logits_out);
+    choose_rank64(lt, ld, (int)nrows, t0, T, N, M, k, idx, gate, gidx, ggate, keys);
+  } else {
+    tile_epilogue<KL>(lt, ld, (int)nrows, t0, T, N, M, k, logits_out, idx, gate, gidx, ggate);
+  }
 }
 
 
@@ -1190,7 +1283,13 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
       st = launch_route_dma<64, 128, 6, 4, 2>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, pl.S, part,
                                               stream);
     }
-    if (st == MOGE_OK && pl.kind != 0) {  // the slices' partial sums -> scores -> the choices
+    if (st == MOGE_OK && pl.kind != 0 && s.N <= 64 && kl != 0) {  // the slices' sum, the rank-count choice
+      const int tpw = kReduceTokens;
+      hipLaunchKernelGGL(route_reduce_kernel<kListRank>, dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256),
+                         0, stream, (int64_t)s.T, s.N, s.M, s.k_per_group, pl.S, part, bias, logits, idx, gate, gidx,
+                         ggate);
+      st = check_launch("route_reduce_kernel");
+    } else if (st == MOGE_OK && pl.kind != 0) {  // the slices' partial sums -> scores -> the choices
       const int tpw = kReduceTokens;
       st = with_list_len(kl, [&](auto klc) {
         constexpr int KL = decltype(klc)::value;

@@ -178,17 +178,19 @@ def _int_operands(T, d, N, seed, f32=False, zero_rows=()):
     return xd, wd, bias.cuda(), host(x), host(wr), bias.numpy()
 
 
-# (T, d, N, M, Kp, dtype, store): every router kernel -- the split reduction and its choice
-# kernel (up to 4096 tokens at any N, and N > 128), the few-token split-K kernel (4096 < T <
-# 32768, N <= 64 and <= 128), the streaming kernel (N = 64, 128), the float32 kernel -- with
-# the sorting-network choice (groups of 8), the list choice (other groups), both routers
+# (T, d, N, M, Kp, dtype, store): every router path -- the one-pass kernel whole (token tiles
+# that fill the CUs, or d < 128) and in slices of d (2, 8 and 16 slices, the last two with a
+# ragged tail of d in the last slice) with the reduction that makes the choice, the 256-expert
+# split kernel, the float32 kernel -- with the sorting-network choice (groups of 8), the list
+# choice (other groups), both routers
 TIE_CASES = [(300, 128, 64, 8, 1, "bf16", True), (300, 128, 64, 8, 2, "bf16", False),
              (32832, 128, 64, 8, 1, "bf16", True), (32832, 64, 64, 8, 2, "bf16", False),
              (300, 128, 128, 4, 2, "bf16", True), (32832, 64, 128, 4, 2, "bf16", False),
              (520, 128, 256, 8, 1, "bf16", True), (520, 128, 256, 8, 1, "bf16", False),
              (300, 96, 16, 4, 1, "bf16", True), (64, 128, 8, 4, 1, "f32", True),
              (5000, 64, 64, 8, 1, "bf16", False), (5000, 64, 128, 4, 2, "bf16", True),
-             (32832, 64, 16, 4, 1, "bf16", True), (32832, 96, 40, 5, 2, "bf16", False)]   # N < 64, one pass
+             (32832, 64, 16, 4, 1, "bf16", True), (32832, 96, 40, 5, 2, "bf16", False),   # N < 64, one pass
+             (1000, 1000, 64, 8, 2, "bf16", True), (2000, 2056, 128, 4, 1, "bf16", False)]
 
 
 @pytest.mark.parametrize("T,d,N,M,Kp,dtype,store", TIE_CASES)
