@@ -53,8 +53,9 @@ def parse():
     p.add_argument("--workload", default="ultra", choices=["ultra", "group0", "decode", "routing", "tiny", "pro"])
     p.add_argument("--rows", default="auto", choices=["auto", "gather", "copy"],
                    help="gate/up token rows: read from x through perm, or copied by dispatch (auto: the layer's choice)")
-    p.add_argument("--tiles", default="auto", choices=["auto", "tall", "wide"],
-                   help="expert-GEMM tile shape: 320x256 (tall), 96x512 (wide), or the library's choice")
+    p.add_argument("--tiles", default="auto", choices=["auto", "tall", "wide", "balanced"],
+                   help="expert-GEMM tile shape: 320x256 (tall), 96x512 (wide), tall with gate/up's columns in "
+                        "balanced 128/96-column tiles (balanced), or the library's choice")
     p.add_argument("--tokens", type=int, default=0,
                    help="run the workload's shape with this many tokens instead (its name records the count)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -271,7 +272,8 @@ def _layer(w, rows="auto", tiles="auto"):
     dv = device_inputs(w)
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi,
                       gather={"auto": None, "gather": True, "copy": False}[rows],
-                      tiles={"auto": moge.TILES_AUTO, "tall": moge.TILES_TALL, "wide": moge.TILES_WIDE}[tiles])
+                      tiles={"auto": moge.TILES_AUTO, "tall": moge.TILES_TALL, "wide": moge.TILES_WIDE,
+                             "balanced": moge.TILES_BALANCED}[tiles])
     if w.F:
         # expert weights are packed once, at load time (outside the timed steps)
         (pg, pu, pd), ps = layer.pack_expert_weights(dv.w_gate, dv.w_up, dv.w_down, dv.shared)
@@ -483,7 +485,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "M": w.M, "k_per_group": w.Kp, "F": w.F,
                    "F_shared": w.F_shared, "experts_computed": [w.e_lo, w.e_hi], "seed": w.seed,
                    "rows": "gather" if layer.gather else "copy",
-                   "tiles": ({g: {moge.TILES_TALL: "tall", moge.TILES_WIDE: "wide"}.get(
+                   "tiles": ({g: {moge.TILES_TALL: "tall", moge.TILES_WIDE: "wide",
+                                  moge.TILES_BALANCED: "balanced"}.get(
                                   moge.tile_choice(layer.shape, i, w.e_lo, w.e_hi, w.F_shared), "none")
                               for i, g in ((1, "gate_up"), (2, "down"))} if w.F else None)},
         "roofline": roof,

@@ -82,10 +82,16 @@ typedef enum { MOGE_STAGE_DISPATCH = 1, MOGE_STAGE_CHECK = 2, MOGE_STAGE_ROUTE =
  *                    the part of the grouped matmul's tiling cache and its switch
  *                    of mode by workload ([P1] section 3, SwiftGMM);
  *   MOGE_TILES_TALL  320 token rows x 256 weight rows;
- *   MOGE_TILES_WIDE  96 token rows x 512 weight rows (few rows per expert). */
+ *   MOGE_TILES_WIDE  96 token rows x 512 weight rows (few rows per expert);
+ *   MOGE_TILES_BALANCED  the tall tiles, with the gate/up GEMM's columns of each
+ *                    routed expert split into tiles of 128 and 96 columns (256
+ *                    and 192 weight rows) so that the tiles fill whole rounds of
+ *                    the CUs (few rows per expert, e.g. 1408 columns as 8 x 128 +
+ *                    4 x 96); the down GEMM as MOGE_TILES_TALL. */
 #define MOGE_TILES_AUTO 0
 #define MOGE_TILES_TALL 1
 #define MOGE_TILES_WIDE 2
+#define MOGE_TILES_BALANCED 3
 
 /*
  * Layer shape.  Rules checked by moge_validate():
@@ -93,7 +99,8 @@ typedef enum { MOGE_STAGE_DISPATCH = 1, MOGE_STAGE_CHECK = 2, MOGE_STAGE_ROUTE =
  *   1 <= k_per_group (K') <= N/M; K = M*K' slots per token (so K <= N);
  *   F expert width: F == 0 (routing only) or F >= 8 with F % 8 == 0;
  *   T*K < 2^31;  N <= 256 (both dtypes);  dtype in moge_dtype_t;
- *   tiles: MOGE_TILES_AUTO, _TALL or _WIDE (a zero-initialised struct: AUTO).
+ *   tiles: MOGE_TILES_AUTO, _TALL, _WIDE or _BALANCED (a zero-initialised
+ *   struct: AUTO).
  * Groups are contiguous blocks of expert ids: group(e) = e / (N/M).
  */
 typedef struct {
@@ -423,9 +430,13 @@ moge_status_t moge_check_finite(int32_t dtype, const void* a, int64_t n, void* w
  * the same launch.  The table keys on the rows per expert under MoGE routing
  * (T*K' / (N/M)), the experts, the output width and the device's CU count, and takes
  * the shape whose busiest CU streams the fewest weight rows: ceil(tiles / CUs) times
- * the tile's weight rows (the wide shape on a tie).  A forced shape.tiles is returned
- * as is.  Host-only (the CU count is queried once; 256 without a device).
- * Returns MOGE_TILES_TALL or MOGE_TILES_WIDE, or -1 for invalid arguments.
+ * the tile's weight rows (the wide shape on a tie).  For gate/up with the tall shape
+ * and at most 64 rows per expert it also weighs the balanced column splits (each
+ * tile i on CU i mod CUs) and takes one that lowers the busiest CU's weight rows.  A
+ * forced shape.tiles is returned as the shape that GEMM runs (BALANCED forced on the
+ * down GEMM: TALL).  Host-only (the CU count is queried once; 256 without a device).
+ * Returns MOGE_TILES_TALL, MOGE_TILES_WIDE or MOGE_TILES_BALANCED, or -1 for invalid
+ * arguments.
  */
 int32_t moge_tile_choice(const moge_shape_t* shape, int32_t gemm, int32_t e_lo, int32_t e_hi, int32_t F_shared);
 

@@ -35,6 +35,7 @@ STAGE_ROUTE = 3
 TILES_AUTO = 0
 TILES_TALL = 1
 TILES_WIDE = 2
+TILES_BALANCED = 3
 
 EXPORTS = ("moge_validate", "moge_rows_bound", "moge_tiled_elems", "moge_packed_weight_elems",
            "moge_workspace_size", "moge_pack_weights", "moge_route", "moge_route_pair", "moge_dispatch",
@@ -203,7 +204,8 @@ def workspace_size(shape: Shape, stage: int = STAGE_DISPATCH) -> int:
 
 
 def tile_choice(shape: Shape, gemm: int, e_lo: int, e_hi: int, F_shared: int = 0) -> int:
-    """The tile shape (TILES_TALL or TILES_WIDE) the library uses for GEMM `gemm` (1 gate/up, 2 down)."""
+    """The tile shape (TILES_TALL, TILES_WIDE or TILES_BALANCED) the library uses for GEMM `gemm`
+    (1 gate/up, 2 down)."""
     return int(_lib.moge_tile_choice(ctypes.byref(shape), gemm, e_lo, e_hi, F_shared))
 
 

@@ -44,8 +44,9 @@ moge_status_t validate_shape(const moge_shape_t* s) {
     return fail(MOGE_ERR_SHAPE, "F must be 0 (routing only) or a positive multiple of 8");
   const int64_t K = (int64_t)s->M * s->k_per_group;
   if ((int64_t)s->T * K >= (int64_t(1) << 31)) return fail(MOGE_ERR_SHAPE, "T*K must be < 2^31");
-  if (s->tiles != MOGE_TILES_AUTO && s->tiles != MOGE_TILES_TALL && s->tiles != MOGE_TILES_WIDE)
-    return fail(MOGE_ERR_ARG, "tiles must be MOGE_TILES_AUTO, MOGE_TILES_TALL or MOGE_TILES_WIDE");
+  if (s->tiles != MOGE_TILES_AUTO && s->tiles != MOGE_TILES_TALL && s->tiles != MOGE_TILES_WIDE &&
+      s->tiles != MOGE_TILES_BALANCED)
+    return fail(MOGE_ERR_ARG, "tiles must be MOGE_TILES_AUTO, _TALL, _WIDE or _BALANCED");
   return MOGE_OK;
 }
 

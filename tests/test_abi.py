@@ -39,7 +39,8 @@ def S(T=64, d=128, N=8, M=4, Kp=1, F=64, dt=moge.BF16, tiles=moge.TILES_AUTO):
     (S(), 0), (S(dt=moge.F32), 0), (S(F=0), 0), (S(M=1, Kp=8), 0), (S(N=256, M=8, Kp=32), 0),
     (S(T=0), 2), (S(d=100), 2), (S(d=0), 2), (S(M=3), 2), (S(M=16), 2), (S(Kp=0), 2), (S(Kp=3), 2),
     (S(F=12), 2), (S(F=-8), 2), (S(N=512, M=8), 2), (S(dt=7), 5), (S(T=2 ** 28, M=8, N=64, Kp=1), 2),
-    (S(tiles=moge.TILES_TALL), 0), (S(tiles=moge.TILES_WIDE), 0), (S(tiles=3), 1), (S(tiles=-1), 1),
+    (S(tiles=moge.TILES_TALL), 0), (S(tiles=moge.TILES_WIDE), 0), (S(tiles=moge.TILES_BALANCED), 0),
+    (S(tiles=4), 1), (S(tiles=-1), 1),
     (S(N=256, M=8, Kp=32), 0), (S(N=256, M=1, Kp=256), 0),                  # K = N: every expert chosen
 ])
 def test_validate(shape, code):
@@ -239,19 +240,22 @@ def test_dispatch_noalloc_refuses_shapes_past_its_scratch():
 
 @pytest.mark.parametrize("T,e_hi,gemm,want", [
     # 4096 hidden, 64 experts in 8 groups, K' = 2, F = 1408: rows per expert 2T/8; the expected
-    # choice of each case was also the faster shape when timed (64-512 tokens, 16-64 experts)
-    (256, 64, 1, "tall"),    # 704 tall tiles = 3 rounds x 256 rows < 384 wide tiles = 2 x 512
+    # shape of each case was also the faster one when timed (64-512 tokens, 16-64 experts)
+    # 704 tall tiles = 3 rounds x 256 rows < 384 wide tiles = 2 x 512; with each expert's 1408
+    # columns in 12 tiles of 128 and 96 the busiest CU streams 2 x 256 + 192 = 704 rows
+    (256, 64, 1, "balanced"),
     (256, 64, 2, "wide"),    # 1024 tall tiles = 4 x 256 == 512 wide tiles = 2 x 512: tie -> wide
-    (64, 64, 1, "tall"), (64, 64, 2, "wide"),
-    (512, 64, 1, "tall"), (512, 64, 2, "tall"),    # 128 rows: a wide tile splits each expert in two
-    (64, 43, 1, "tall"),     # 473 tall tiles = 2 x 256 < 258 wide tiles = 2 x 512
+    (64, 64, 1, "balanced"), (64, 64, 2, "wide"),
+    (512, 64, 1, "tall"), (512, 64, 2, "tall"),    # 128 rows: a wide tile splits each expert in two,
+                                                   # and a column split no longer pays
+    (64, 43, 1, "tall"),     # 473 tall tiles = 2 x 256 < 258 wide tiles = 2 x 512; no split does better
     (64, 32, 1, "wide"),     # 352 tall = 2 x 256 == 192 wide = 1 x 512
     (64, 16, 1, "tall"),     # 176 tall = 1 x 256 < 96 wide = 1 x 512
 ])
 def test_tile_table(T, e_hi, gemm, want):
     s = S(T=T, d=4096, N=64, M=8, Kp=2, F=1408)
     got = moge.tile_choice(s, gemm, 0, e_hi)
-    assert got == {"tall": moge.TILES_TALL, "wide": moge.TILES_WIDE}[want]
+    assert got == {"tall": moge.TILES_TALL, "wide": moge.TILES_WIDE, "balanced": moge.TILES_BALANCED}[want]
 
 
 def test_tile_table_large_shapes_and_forced():
@@ -262,6 +266,11 @@ def test_tile_table_large_shapes_and_forced():
     assert moge.tile_choice(group0, 1, 0, 8) == moge.TILES_TALL
     forced = S(T=8192, d=7680, N=256, M=8, Kp=1, F=2048, tiles=moge.TILES_WIDE)
     assert moge.tile_choice(forced, 1, 0, 256) == moge.TILES_WIDE
+    balanced = S(T=8192, d=7680, N=256, M=8, Kp=1, F=2048, tiles=moge.TILES_BALANCED)
+    assert moge.tile_choice(balanced, 1, 0, 256) == moge.TILES_BALANCED    # 64 units: 17+ tiles of 4 and 3
+    assert moge.tile_choice(balanced, 2, 0, 256) == moge.TILES_TALL        # the down GEMM runs tall
+    narrow = S(T=8192, d=7680, N=256, M=8, Kp=1, F=64, tiles=moge.TILES_BALANCED)
+    assert moge.tile_choice(narrow, 1, 0, 256) == moge.TILES_TALL          # 2 units: no split of 3 or 4
     assert moge.tile_choice(ultra, 3, 0, 256) == -1 and moge.tile_choice(ultra, 1, 5, 5) == -1
     assert moge.tile_choice(S(F=0), 1, 0, 8) == -1
 

@@ -332,9 +332,12 @@ def test_down_combine_bitexact(gpu, w):
     W.variant(MID, name="tiles_shared_T333", F_shared=136, std_shared_down=0.02, T=333),
     W.variant(MID, name="tiles_range_T700", T=700, e_lo=3, e_hi=11, F=1408),
     W.variant(MID, name="tiles_group_fused", T=333, Kp=1, e_lo=4, e_hi=8),
+    # split columns with a ragged width (1400 = 43.75 units) and the shared expert in the same launch
+    W.variant(MID, name="tiles_split_ragged_shared", T=400, F=1400, F_shared=136, std_shared_down=0.02),
 ], ids=lambda w: w.name)
 def test_tile_shapes_bitexact(gpu, w):
-    # the 320 x 256 and the 96 x 512 tiles compute every output element identically
+    # the 320 x 256 tiles, the 96 x 512 tiles and the tall tiles with gate/up's columns split
+    # into 128- and 96-column tiles compute every output element identically
     dv = H.device_inputs(w)
     hi = H.HostInputs(w)
     idx, gate, _ = oracle.route(H.oracle_logits_all(hi), w.M, w.Kp, "grouped")
@@ -353,7 +356,7 @@ def test_tile_shapes_bitexact(gpu, w):
     g = torch.from_numpy(gate.astype(np.float32)).cuda()
     fused = w.Kp == 1 and not Fs and w.e_hi - w.e_lo == w.N // w.M and w.e_lo % (w.N // w.M) == 0
     outs = []
-    for tiles in (moge.TILES_TALL, moge.TILES_WIDE):
+    for tiles in (moge.TILES_TALL, moge.TILES_WIDE, moge.TILES_BALANCED):
         s.tiles = tiles
         if True:
             h = torch.zeros(moge.tiled_elems(cap, w.F), **bf)
@@ -370,6 +373,7 @@ def test_tile_shapes_bitexact(gpu, w):
                 moge.expert_down_combine(s, h, offsets, w.e_lo, w.e_hi, cap, pd, perm, g, y)
             torch.cuda.synchronize()
             outs.append((h, o, hs, so, y))
-    for a, b in zip(*outs):
-        if a is not None:
-            assert H.same_bits(a, b)
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            if a is not None:
+                assert H.same_bits(a, b)
