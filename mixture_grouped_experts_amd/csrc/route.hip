@@ -11,8 +11,8 @@
 //   * bf16 scores, N <= 128: x [T][d] is streamed from HBM once.  A workgroup owns TM
 //     tokens x NP experts (128 x 64 with 8 waves of one 32 x 32 block each, or 64 x 128
 //     with 4 waves of 32 x 64), accumulated with v_mfma_f32_32x32x16_bf16 (float32).  Token rows
-//     and router rows go from global memory straight into a 6-stage LDS ring with
-//     direct-to-LDS loads, several 32-element steps ahead.  With fewer token tiles than
+//     and router rows go from global memory straight into a 3-stage LDS ring with
+//     direct-to-LDS loads of whole 128-byte lines, two 64-element steps ahead.  With fewer token tiles than
 //     CUs the same kernel runs in slices of the hidden dimension (workgroup b: slice
 //     b % S of token tile b / S) and writes partial sums instead of choosing.
 //   * bf16 scores, 128 < N <= 256: split over the hidden dimension too, with a
@@ -41,6 +41,14 @@ namespace moge {
 // on finite scores only; with this key every group still yields exactly k distinct
 // experts of its own, whatever the scores (moge_check_finite reports non-finite ones).
 __device__ __forceinline__ float order_key(float v) { return v == v ? v : -INFINITY; }
+
+// The bf16 routers stage 64-element steps of every token row and router row: 128-byte LDS
+// rows, whose 16-byte chunk c lives in slot c ^ route_swz(row).  Rows r and r + 2 share a
+// bank line, so this swizzle puts the 16 rows that one 16-byte fragment read touches per
+// clock on all 64 banks.
+constexpr int kRouteBK = 64;
+constexpr int kRouteRowB = kRouteBK * 2;
+__device__ __forceinline__ int route_swz(int r) { return (r >> 1) & 7; }
 
 // Softmax over the token's N scores (LDS row `l`) and the per-group choice.
 // One full wave per token; lane owns experts lane, lane+64, lane+128, lane+192.
@@ -720,13 +728,14 @@ static moge_status_t with_list_len(int kl, Fn&& f) {
 // bf16 scores, many tokens, N <= 128.  A workgroup of WV waves owns TM tokens x NP experts
 // (NP = N rounded up to 64 or 128, TM = 8192 / NP), every wave one 32-token x 32 CB-expert
 // block of CB 32x32 accumulators: 8 waves of one block for 64 experts (twice the waves
-// to interleave the choice epilogue), 4 waves of two blocks for 128.  The token rows and the
-// router rows of each 32-element step go from global memory straight into an
-// S-stage LDS ring (global_load_lds_dwordx4, 16 rows of 64 bytes per instruction,
-// XOR-swizzled rows), S - 1 steps ahead, so x streams from HBM with several steps
-// of loads in flight per workgroup and no staging registers; x is read exactly
-// once.  One barrier per step.  The epilogue keeps the TM x NP score tile in LDS
-// for the softmax and the choices.
+// to interleave the choice epilogue), 4 waves of two blocks for 128.  A step is 64
+// elements: every token row and router row contributes 128 bytes, one whole cache line
+// (the L2 delivers whole lines at about 1.4 times the rate of half lines), moved from
+// global memory straight into an S-stage LDS ring (global_load_lds_dwordx4, 8 rows of
+// 128 bytes per instruction, chunks XOR-swizzled by (row / 2) % 8), S - 1 steps ahead, so
+// x streams from HBM with two steps of loads in flight per workgroup and no staging
+// registers; x is read exactly once.  One barrier per step.  The epilogue keeps the
+// TM x NP score tile in LDS for the softmax and the choices.
 template <int TM, int NP, int S, int WV, int CB, int KL>
 __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, int N, int n_groups, int k,
                                                         const uint16_t* __restrict__ x,
@@ -735,40 +744,41 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
                                                         float* __restrict__ logits_out, int32_t* __restrict__ idx,
                                                         float* __restrict__ gate, int32_t* __restrict__ gidx,
                                                         float* __restrict__ ggate, int nsl, float* __restrict__ part) {
-  constexpr int ROWS = TM + NP;      // stage rows of 64 bytes: tokens, then experts
-  constexpr int NI = ROWS / 16;      // load instructions per step
+  constexpr int RB = kRouteRowB;
+  constexpr int ROWS = TM + NP;      // stage rows of 128 bytes: tokens, then experts
+  constexpr int NI = ROWS / 8;       // load instructions per step (8 rows each)
   constexpr int NJ = (NI + WV - 1) / WV;  // per wave, at most
   constexpr int CH = NJ;                  // loads per step of waves 0 .. NI%WV - 1 (all when NI%WV == 0)
   constexpr int CL = NI / WV;             // loads per step of the other waves
-  constexpr int STAGE = ROWS * 64;
+  constexpr int STAGE = ROWS * RB;
   constexpr int TB = TM / 32;        // token blocks; wave = token block + TB * expert slice
-  static_assert(TM * NP == 1024 * CB * WV && S >= 4, "route tile: one 32 x (32 CB) block per wave");
+  static_assert(TM * NP == 1024 * CB * WV && S >= 3 && ROWS % 8 == 0, "route tile: one 32 x (32 CB) block per wave");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tb = wave % TB, es = wave / TB;
   // nsl > 1: the slice mode -- workgroup b computes slice b % nsl of the reduction (steps
-  // k0 .. k1 - 1 of d / 32) for token tile b / nsl and writes the float32 partial sums to
+  // k0 .. k1 - 1 of d / 64) for token tile b / nsl and writes the float32 partial sums to
   // part[slice][t][e] (the reduction kernel adds them and chooses); nsl == 1: one pass
   const int slice = (int)(blockIdx.x % nsl);
   const int64_t t0 = (int64_t)(blockIdx.x / nsl) * TM;
-  const int nkf = d / 32;                        // full steps; a ragged tail follows the loop
+  const int nkf = d / kRouteBK;                  // full steps; a ragged tail follows the loop
   const int k0 = (int)((int64_t)nkf * slice / nsl);
   const int nks = (int)((int64_t)nkf * (slice + 1) / nsl) - k0;  // this workgroup's steps
   // token tiles start at different steps (and wrap around), so the workgroups do not all
-  // read the same column range of their rows at once: each tile walks 64-byte pieces of
-  // rows 8 KiB apart, and in a plain streaming probe of that pattern the staggered start
-  // reads 9% faster (router -11% on 65536 tokens x 4096).  The order of the float32
-  // accumulation over k then depends on the tile; scores stay within the tolerance.
+  // read the same column range of their rows at once (router -11% on 65536 tokens x 4096
+  // when it was measured).  The order of the float32 accumulation over k then depends on
+  // the tile; scores stay within the tolerance.
   const int krot = nks > 0 ? (int)(((t0 / TM) * 37) % nks) : 0;
   const bool many = (NI % WV == 0) || wave < (NI % WV);  // this wave issues CH loads per step, else CL
 
-  // load j of this wave moves stage rows 16 i .. 16 i + 15 with i = wave + WV j
+  // load j of this wave moves stage rows 8 i .. 8 i + 7 with i = wave + WV j; lane l brings
+  // physical chunk l % 8 of row 8 i + l / 8
   const uint16_t* src[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int srow = 16 * (wave + WV * j) + (lane >> 2);
-    const int c = (lane & 3) ^ lds_swz(srow);
+    const int srow = 8 * (wave + WV * j) + (lane >> 3);
+    const int c = (lane & 7) ^ route_swz(srow);
     if (srow < TM) {
       int64_t t = t0 + srow;
       if (t > T - 1) t = T - 1;
@@ -783,26 +793,10 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   auto issue = [&](int ks) {
     if (ks >= nks) return;
     const uint32_t st = lds0 + (uint32_t)((ks % S) * STAGE);
+    const int kk = k0 + (ks + krot < nks ? ks + krot : ks + krot - nks);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      if (wave + WV * j < NI) {
-        const int kk = k0 + (ks + krot < nks ? ks + krot : ks + krot - nks);
-        dma_16x64(src[j] + kk * 32, st + (uint32_t)(16 * (wave + WV * j) * 64));
-      }
-  };
-  // at most `steps` steps of this wave's loads still in flight (and, with lgkm, no LDS reads)
-  auto wait_steps = [&](int steps_left_ok, bool lgkm) {
-    // steps_left_ok is S - 3 (steady state) or 0 (prologue / tail); both branches are immediates
-    if (steps_left_ok == 0) {
-      if (lgkm) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    } else if (many) {
-      if (lgkm) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((S - 3) * CH));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * CH));
-    } else {
-      if (lgkm) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((S - 3) * CL));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * CL));
-    }
+      if (wave + WV * j < NI) dma_16x64(src[j] + kk * kRouteBK, st + (uint32_t)((wave + WV * j) * 1024));
   };
 
   const int kc = lane >> 5;
@@ -810,14 +804,15 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
   int brow[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) brow[cb] = TM + es * 32 * CB + cb * 32 + (lane & 31);
+  // fragments of 16-element sub-step kk (0 .. 3) of the step in `stage`
   auto frag = [&](int stage, int kk, bf16x8_t& a, bf16x8_t (&b)[CB]) {
     const char* st = lds + stage * STAGE;
     const int c = kk * 2 + kc;
-    a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + arow * 64 + ((c ^ lds_swz(arow)) << 4)));
+    a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + arow * RB + ((c ^ route_swz(arow)) << 4)));
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       b[cb] = __builtin_bit_cast(bf16x8_t,
-                                 *reinterpret_cast<const u32x4_t*>(st + brow[cb] * 64 + ((c ^ lds_swz(brow[cb])) << 4)));
+                                 *reinterpret_cast<const u32x4_t*>(st + brow[cb] * RB + ((c ^ route_swz(brow[cb])) << 4)));
   };
   f32x16_t acc[CB];
 #pragma unroll
@@ -828,42 +823,48 @@ __global__ __launch_bounds__(64 * WV) void route_dma_kernel(int64_t T, int d, in
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[cb], acc[cb], 0, 0, 0);
   };
+  auto step = [&](int stage) {
+    bf16x8_t a0, b0[CB], a1, b1[CB];
+    frag(stage, 0, a0, b0);
+    frag(stage, 1, a1, b1);
+    mfma(a0, b0);
+    frag(stage, 2, a0, b0);
+    mfma(a1, b1);
+    frag(stage, 3, a1, b1);
+    mfma(a0, b0);
+    mfma(a1, b1);
+  };
 
-  // prologue: steps 0 .. S-2 in flight; steps 0 and 1 landed
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s);
-  wait_steps(nks >= S - 1 ? S - 3 : 0, false);
-  __syncthreads();
-  bf16x8_t a0, b0[CB], a1, b1[CB];
-  frag(0, 0, a0, b0);
   for (int ks = 0; ks < nks; ++ks) {
-    issue(ks + S - 1);  // into stage (ks - 1) % S, last read before the previous barrier
-    frag(ks % S, 1, a1, b1);
-    mfma(a0, b0);
-    frag((ks + 1) % S, 0, a0, b0);  // read-ahead (unused after the last step)
-    mfma(a1, b1);
-    // step ks + 2 landed (every step is waited for once the tail issues no more)
-    wait_steps(ks + S - 1 < nks ? S - 3 : 0, true);
+    // step ks landed for every wave (this wave's later steps, S - 2 of them, may be in flight)
+    if (ks + S - 2 < nks) {
+      if (many) __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * CH));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * CL));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
     __syncthreads();
+    issue(ks + S - 1);  // into stage (ks - 1) % S, whose reads all finished before the barrier
+    step(ks % S);
   }
-  if ((d % 32) && slice == nsl - 1) {
-    // ragged tail: one step through registers, columns at or past d are zero
-    const int kt = nkf * 32;
+  __syncthreads();  // every wave is done with the ring (the tail and the score tile reuse it)
+  if ((d % kRouteBK) && slice == nsl - 1) {
+    // ragged tail: one step through registers into stage 0, columns at or past d are zero
+    const int kt = nkf * kRouteBK;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (wave + WV * j < NI) {
-        const int srow = 16 * (wave + WV * j) + (lane >> 2);
-        const int c = (lane & 3) ^ lds_swz(srow);
+        const int srow = 8 * (wave + WV * j) + (lane >> 3);
+        const int c = (lane & 7) ^ route_swz(srow);
         const u32x4_t v = (kt + c * 8 < d) ? *reinterpret_cast<const u32x4_t*>(src[j] + kt) : zero;
-        *reinterpret_cast<u32x4_t*>(lds + 16 * (wave + WV * j) * 64 + lane * 16) = v;
+        *reinterpret_cast<u32x4_t*>(lds + (wave + WV * j) * 1024 + lane * 16) = v;
       }
     }
     __syncthreads();
-    frag(0, 0, a0, b0);
-    frag(0, 1, a1, b1);
-    mfma(a0, b0);
-    mfma(a1, b1);
+    step(0);
     __syncthreads();
   }
 
@@ -903,7 +904,7 @@ static moge_status_t launch_route_dma(const moge_shape_t& s, int kl, const void*
                                       int nsl, float* part, hipStream_t stream) {
   return with_list_len(kl, [&](auto klc) {
     constexpr int KL = decltype(klc)::value;
-    constexpr size_t ring = (size_t)S * (TM + NP) * 64;
+    constexpr size_t ring = (size_t)S * (TM + NP) * kRouteRowB;
     constexpr size_t tile = (size_t)TM * (NP + 1) * 4;
     constexpr size_t lds = ring > tile ? ring : tile;
     const void* kern = reinterpret_cast<const void*>(route_dma_kernel<TM, NP, S, WV, CB, KL>);
@@ -919,43 +920,49 @@ static moge_status_t launch_route_dma(const moge_shape_t& s, int kl, const void*
 
 // ----------------------------------------------------------------------------
 // bf16 scores split over the hidden dimension, 128 < N <= 256.
-// Workgroup b computes slice b % S of the reduction (its steps k0 .. k1 - 1 of d / 32) for
+// Workgroup b computes slice b % S of the reduction (its steps k0 .. k1 - 1 of d / 64) for
 // the 128-token x 256-expert tile b / S, and stores the float32 partial sums to
 // part[slice][t][e].  8 waves; wave w owns tokens (w / 4) * 64 .. + 64 and experts
 // (w % 4) * 64 .. + 64 as 2 x 2 accumulators of 32 x 32 (v_mfma_f32_32x32x16_bf16; experts
-// past N repeat the last router row and are not stored).  Each step's 128 token rows and 256
-// router rows (64 bytes of each) go straight into a 6-stage LDS ring (24 loads of 16 rows per
-// step, 3 per wave), 5 steps ahead, one barrier per step.  Workgroup b runs on XCD b % 8 and
-// S is a power of two, so an XCD reads only its own slices of the router matrix (at most
-// 983 KB of a 256 x 7680 matrix at S = 4), which stay in its L2, while x streams from HBM
-// once.  The last slice also takes the ragged tail of d (d % 32 columns).
-constexpr int kPartTM = 128, kPartNP = 256, kPartStages = 6;
+// past N repeat the last router row and are not stored).  A step is 64 elements: each of its
+// 128 token rows and 256 router rows contributes 128 bytes, one whole cache line, which the
+// L2 delivers at about 1.4 times the rate of the half lines a 32-element step takes (measured
+// with the loads alone on this tile: 20.8 against 29.7 us at 8192 tokens x 7680).  The
+// stage rows go straight into a 3-stage LDS ring (48 loads of 8 rows x 128 bytes per step,
+// 6 per wave), two steps ahead, one barrier per step; the 16-byte chunks of a row are
+// XOR-swizzled by (row / 2) % 8, so the 16 rows a fragment read touches per clock cover all
+// 64 banks.  Workgroup b runs on XCD b % 8 and S is a power of two, so an XCD reads only
+// its own slices of the router matrix (at most 983 KB of a 256 x 7680 matrix at S = 4),
+// which stay in its L2, while x streams from HBM once.  The last slice also takes the
+// ragged tail of d (d % 64 columns, a multiple of 8) through registers.
+constexpr int kPartTM = 128, kPartNP = 256, kPartStages = 3;
 __host__ __forceinline__ int route_slices(int64_t T, int d);
 __global__ __launch_bounds__(512) void route_part_kernel(int64_t T, int d, int N, int S,
                                                          const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ w,
                                                          float* __restrict__ part) {
-  constexpr int TM = kPartTM, NP = kPartNP, SG = kPartStages;
-  constexpr int ROWS = TM + NP;       // 384 stage rows of 64 bytes
-  constexpr int STAGE = ROWS * 64;    // 24 KiB
+  constexpr int TM = kPartTM, NP = kPartNP, SG = kPartStages, RB = kRouteRowB;
+  constexpr int ROWS = TM + NP;           // 384 stage rows of 128 bytes
+  constexpr int STAGE = ROWS * RB;        // 48 KiB
+  constexpr int PW = ROWS / 8 / 8;        // loads per wave per step (8 rows each): 6
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave >> 2, wc = wave & 3;
   const int slice = (int)(blockIdx.x % S);
   const int64_t t0 = (int64_t)(blockIdx.x / S) * TM;
-  const int nkf = d / 32;
+  const int nkf = d / kRouteBK;
   const int k0 = (int)((int64_t)nkf * slice / S), k1 = (int)((int64_t)nkf * (slice + 1) / S);
   const int nks = k1 - k0;
   // token tiles start their slice at staggered steps (as the one-pass kernel does)
   const int krot = nks > 0 ? (int)(((t0 / TM) * 37) % nks) : 0;
-  // load j of this wave moves stage rows 16 i .. 16 i + 15, i = wave + 8 j: j = 0 token
-  // rows, j = 1, 2 router rows
-  const uint16_t* src[3];
+  // load j of this wave moves stage rows 8 i .. 8 i + 7, i = wave + 8 j (j = 0, 1: token
+  // rows; j = 2 .. 5: router rows); lane l brings physical chunk l % 8 of row 8 i + l / 8
+  const uint16_t* src[PW];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int srow = 16 * (wave + 8 * j) + (lane >> 2);
-    const int c = (lane & 3) ^ lds_swz(srow);
+  for (int j = 0; j < PW; ++j) {
+    const int srow = 8 * (wave + 8 * j) + (lane >> 3);
+    const int c = (lane & 7) ^ route_swz(srow);
     if (srow < TM) {
       int64_t t = t0 + srow;
       if (t > T - 1) t = T - 1;
@@ -973,7 +980,7 @@ __global__ __launch_bounds__(512) void route_part_kernel(int64_t T, int d, int N
     const int kr = ks + krot < nks ? ks + krot : ks + krot - nks;
     const int kk = k0 + kr;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) dma_16x64(src[j] + kk * 32, st + (uint32_t)(16 * (wave + 8 * j) * 64));
+    for (int j = 0; j < PW; ++j) dma_16x64(src[j] + kk * kRouteBK, st + (uint32_t)((wave + 8 * j) * 1024));
   };
   const int kc = lane >> 5;
   int arow[2], brow[2];
@@ -982,15 +989,16 @@ __global__ __launch_bounds__(512) void route_part_kernel(int64_t T, int d, int N
     arow[i] = wr * 64 + i * 32 + (lane & 31);
     brow[i] = TM + wc * 64 + i * 32 + (lane & 31);
   }
+  // fragments of 16-element sub-step kk (0 .. 3) of the step in `stage`
   auto frag = [&](int stage, int kk, bf16x8_t (&a)[2], bf16x8_t (&b)[2]) {
     const char* st = lds + stage * STAGE;
     const int c = kk * 2 + kc;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       a[i] = __builtin_bit_cast(bf16x8_t,
-                                *reinterpret_cast<const u32x4_t*>(st + arow[i] * 64 + ((c ^ lds_swz(arow[i])) << 4)));
+                                *reinterpret_cast<const u32x4_t*>(st + arow[i] * RB + ((c ^ route_swz(arow[i])) << 4)));
       b[i] = __builtin_bit_cast(bf16x8_t,
-                                *reinterpret_cast<const u32x4_t*>(st + brow[i] * 64 + ((c ^ lds_swz(brow[i])) << 4)));
+                                *reinterpret_cast<const u32x4_t*>(st + brow[i] * RB + ((c ^ route_swz(brow[i])) << 4)));
     }
   };
   f32x16_t acc[2][2];
@@ -1006,42 +1014,41 @@ __global__ __launch_bounds__(512) void route_part_kernel(int64_t T, int d, int N
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
+  auto step = [&](int stage) {
+    bf16x8_t a0[2], b0[2], a1[2], b1[2];
+    frag(stage, 0, a0, b0);
+    frag(stage, 1, a1, b1);
+    mfma(a0, b0);
+    frag(stage, 2, a0, b0);
+    mfma(a1, b1);
+    frag(stage, 3, a1, b1);
+    mfma(a0, b0);
+    mfma(a1, b1);
+  };
 #pragma unroll
   for (int s = 0; s < SG - 1; ++s) issue(s);
-  // steps 0 and 1 landed (3 loads per step per wave; at most SG - 3 later steps in flight):
-  // the first iteration reads step 0 and, ahead, the first half of step 1
-  if (nks >= SG - 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm((SG - 3) * 3));
-  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
-  bf16x8_t a0[2], b0[2], a1[2], b1[2];
-  if (nks > 0) frag(0, 0, a0, b0);
   for (int ks = 0; ks < nks; ++ks) {
-    issue(ks + SG - 1);  // into stage (ks - 1) % SG, last read before the previous barrier
-    frag(ks % SG, 1, a1, b1);
-    mfma(a0, b0);
-    frag((ks + 1) % SG, 0, a0, b0);  // read-ahead (unused after the last step)
-    mfma(a1, b1);
-    // step ks + 2 landed (once the tail issues no more, everything is waited for)
-    if (ks + SG - 1 < nks) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((SG - 3) * 3));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
+    // step ks landed (this wave's loads of step ks + 1 may still be in flight), for every wave
+    if (ks + 1 < nks) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
+    issue(ks + SG - 1);  // into stage (ks - 1) % SG, whose reads all finished before the barrier
+    step(ks % SG);
   }
-  if (slice == S - 1 && (d % 32)) {
-    // ragged tail: one step through registers, columns at or past d are zero
-    const int kt = nkf * 32;
+  if (slice == S - 1 && (d % kRouteBK)) {
+    // ragged tail: one step through registers into stage 0, columns at or past d are zero
+    __syncthreads();  // every wave's reads of the last step are done
+    const int kt = nkf * kRouteBK;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int srow = 16 * (wave + 8 * j) + (lane >> 2);
-      const int c = (lane & 3) ^ lds_swz(srow);
+    for (int j = 0; j < PW; ++j) {
+      const int srow = 8 * (wave + 8 * j) + (lane >> 3);
+      const int c = (lane & 7) ^ route_swz(srow);
       const u32x4_t v = (kt + c * 8 < d) ? *reinterpret_cast<const u32x4_t*>(src[j] + kt) : zero;
-      *reinterpret_cast<u32x4_t*>(lds + 16 * (wave + 8 * j) * 64 + lane * 16) = v;
+      *reinterpret_cast<u32x4_t*>(lds + (wave + 8 * j) * 1024 + lane * 16) = v;
     }
     __syncthreads();
-    frag(0, 0, a0, b0);
-    frag(0, 1, a1, b1);
-    mfma(a0, b0);
-    mfma(a1, b1);
+    step(0);
   }
   float* dst = part + (int64_t)slice * T * N;
 #pragma unroll
@@ -1059,13 +1066,13 @@ __global__ __launch_bounds__(512) void route_part_kernel(int64_t T, int d, int N
 
 // Slices per token tile for the split kernel: enough that the token tiles times the slices
 // fill the 256 CUs, at most 4 for many tokens (each XCD then holds whole slices of the router
-// matrix) and, for few tokens, up to 32 while every slice keeps at least 2 steps of 32.
+// matrix) and, for few tokens, up to 32 while every slice keeps at least 2 steps of 64.
 __host__ __forceinline__ int route_slices(int64_t T, int d) {
   const int64_t tiles = (T + kPartTM - 1) / kPartTM;
-  const int nkf = d / 32;
+  const int nkf = d / kRouteBK;
   const int cap = tiles >= 16 ? 4 : 32;
   int S = 1;
-  while (S < cap && tiles * S < 256 && nkf / (2 * S) >= 2) S <<= 1;
+  while (S < cap && tiles * S < 256 && nkf / (2 * S) >= 1) S <<= 1;
   return S;
 }
 
@@ -1079,12 +1086,12 @@ struct RoutePlan {
 };
 __host__ __forceinline__ int dma_tile_tokens(int N) { return N <= 64 ? 128 : 64; }
 // Slices for the one-pass kernel's slice mode: until the token tiles times the slices give
-// two 72 KiB workgroups per CU, at most 32, every slice keeping at least 2 steps of 32.
+// two 72 KiB workgroups per CU, at most 32, every slice keeping at least 2 steps of 64.
 __host__ __forceinline__ int dma_slices(int64_t T, int d, int N) {
   const int64_t tiles = (T + dma_tile_tokens(N) - 1) / dma_tile_tokens(N);
-  const int nkf = d / 32;
+  const int nkf = d / kRouteBK;
   int S = 1;
-  while (S < 32 && tiles * S < 512 && nkf / (2 * S) >= 2) S <<= 1;
+  while (S < 32 && tiles * S < 512 && nkf / (2 * S) >= 1) S <<= 1;
   return S;
 }
 __host__ __forceinline__ RoutePlan route_plan(const moge_shape_t& s) {
@@ -1269,7 +1276,7 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
     const RoutePlan pl = route_plan(s);
     float* part = static_cast<float*>(ws);
     if (pl.kind == 2) {
-      constexpr size_t lds = (size_t)kPartStages * (kPartTM + kPartNP) * 64;
+      constexpr size_t lds = (size_t)kPartStages * (kPartTM + kPartNP) * kRouteRowB;
       st = raise_dynamic_lds(reinterpret_cast<const void*>(route_part_kernel), lds, "route_part_kernel");
       if (st != MOGE_OK) return st;
       const int64_t grid = ((int64_t)s.T + kPartTM - 1) / kPartTM * pl.S;
@@ -1277,10 +1284,10 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
                          pl.S, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), part);
       st = check_launch("route_part_kernel");
     } else if (s.N <= 64) {
-      st = launch_route_dma<128, 64, 6, 8, 1>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, pl.S, part,
+      st = launch_route_dma<128, 64, 3, 8, 1>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, pl.S, part,
                                               stream);
     } else {
-      st = launch_route_dma<64, 128, 6, 4, 2>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, pl.S, part,
+      st = launch_route_dma<64, 128, 3, 4, 2>(s, kl, x, w_router, bias, logits, idx, gate, gidx, ggate, pl.S, part,
                                               stream);
     }
     if (st == MOGE_OK && pl.kind != 0 && s.N <= 64 && kl != 0) {  // the slices' sum, the rank-count choice
