@@ -179,8 +179,8 @@ def _int_operands(T, d, N, seed, f32=False, zero_rows=()):
 
 
 # (T, d, N, M, Kp, dtype, store): every router path -- the one-pass kernel whole (token tiles
-# that fill the CUs, or d < 128) and in slices of d (2, 8 and 16 slices, the last two with a
-# ragged tail of d in the last slice) with the reduction that makes the choice (rank count at
+# that fill the CUs, or d < 128) and in slices of d (2, 8 and 16 slices, with ragged tails of d
+# in the last slice) with the reduction that makes the choice (rank count at
 # N <= 64, the lists above), the 256-expert split kernel, the float32 kernel -- with the
 # sorting-network choice (groups of 8), the list choice (other groups: 8, 16, 32 experts at
 # N = 128 and 256), both routers
@@ -192,7 +192,13 @@ TIE_CASES = [(300, 128, 64, 8, 1, "bf16", True), (300, 128, 64, 8, 2, "bf16", Fa
              (5000, 64, 64, 8, 1, "bf16", False), (5000, 64, 128, 4, 2, "bf16", True),
              (32832, 64, 16, 4, 1, "bf16", True), (32832, 96, 40, 5, 2, "bf16", False),   # N < 64, one pass
              (1000, 1000, 64, 8, 2, "bf16", True), (2000, 2056, 128, 4, 1, "bf16", False),
-             (300, 128, 128, 16, 1, "bf16", True), (300, 128, 256, 16, 2, "bf16", False)]  # groups of 8, 16
+             (300, 128, 128, 16, 1, "bf16", True), (300, 128, 256, 16, 2, "bf16", False),  # groups of 8, 16
+             # ragged tails of 16 to 56 columns past the last 64-column step: one pass (N = 64 and
+             # 128), its slice mode, and the 256-expert split with one or several steps per slice
+             (32832, 120, 64, 8, 1, "bf16", True), (5000, 1048, 128, 4, 2, "bf16", True),
+             (2000, 4112, 64, 8, 1, "bf16", True), (520, 184, 256, 8, 1, "bf16", True),
+             (300, 7720, 256, 8, 1, "bf16", True),
+             (300, 40, 64, 8, 1, "bf16", True), (300, 56, 256, 8, 1, "bf16", False)]  # d below one step
 
 
 @pytest.mark.parametrize("T,d,N,M,Kp,dtype,store", TIE_CASES)
