@@ -53,9 +53,10 @@ def parse():
     p.add_argument("--workload", default="ultra", choices=["ultra", "group0", "decode", "routing", "tiny", "pro"])
     p.add_argument("--rows", default="auto", choices=["auto", "gather", "copy"],
                    help="gate/up token rows: read from x through perm, or copied by dispatch (auto: the layer's choice)")
-    p.add_argument("--tiles", default="auto", choices=["auto", "tall", "wide", "balanced"],
+    p.add_argument("--tiles", default="auto", choices=["auto", "tall", "wide", "balanced", "tuned"],
                    help="expert-GEMM tile shape: 320x256 (tall), 96x512 (wide), tall with gate/up's columns in "
-                        "balanced 128/96-column tiles (balanced), or the library's choice")
+                        "balanced 128/96-column tiles (balanced), the library's choice (auto), or each GEMM's "
+                        "fastest measured on the workload before the timed steps (tuned)")
     p.add_argument("--tokens", type=int, default=0,
                    help="run the workload's shape with this many tokens instead (its name records the count)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -273,12 +274,14 @@ def _layer(w, rows="auto", tiles="auto"):
     layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi,
                       gather={"auto": None, "gather": True, "copy": False}[rows],
                       tiles={"auto": moge.TILES_AUTO, "tall": moge.TILES_TALL, "wide": moge.TILES_WIDE,
-                             "balanced": moge.TILES_BALANCED}[tiles])
+                             "balanced": moge.TILES_BALANCED, "tuned": moge.TILES_AUTO}[tiles])
     if w.F:
         # expert weights are packed once, at load time (outside the timed steps)
         (pg, pu, pd), ps = layer.pack_expert_weights(dv.w_gate, dv.w_up, dv.w_down, dv.shared)
         dv = dataclasses.replace(dv, w_gate=pg, w_up=pu, w_down=pd, shared=ps)
         torch.cuda.synchronize()
+        if tiles == "tuned":  # measured once per shape, before any timed step
+            layer.tune_tiles(dv.x, dv.w_router, dv.bias, dv.w_gate, dv.w_up, dv.w_down, dv.shared)
     return layer, dv
 
 
@@ -490,8 +493,9 @@ def main():
                    "rows": "gather" if layer.gather else "copy",
                    "tiles": ({g: {moge.TILES_TALL: "tall", moge.TILES_WIDE: "wide",
                                   moge.TILES_BALANCED: "balanced"}.get(
-                                  moge.tile_choice(layer.shape, i, w.e_lo, w.e_hi, w.F_shared), "none")
-                              for i, g in ((1, "gate_up"), (2, "down"))} if w.F else None)},
+                                  moge.tile_choice(shp, i, w.e_lo, w.e_hi, w.F_shared), "none")
+                              for i, g, shp in ((1, "gate_up", layer.shape_up), (2, "down", layer.shape_down))}
+                             if w.F else None)},
         "roofline": roof,
         "stages": _stage_table(stage_us, work),
         "imbalance": {"moge_is_raw": int(layer.is_raw.item()),

@@ -28,6 +28,14 @@ reportify.cn for the shared expert):
 The scores themselves are stored only when asked for (``store_scores``): neither router needs them
 once step 1 has run.
 
+Tile shapes of the two expert GEMMs: the library picks them from the call's shape (a cost table,
+``moge_tile_choice``) unless the call's ``tiles`` field forces one.  ``tune_tiles`` replaces the
+table by measurement, as the grouped matmul of the pages does (Pangu Pro MoE, lsdiaocha.cn summary,
+section 3: tilings cached per shape from profiling, and a switch of mode by workload): it times each
+GEMM of this layer under every tile shape on the real routed rows and keeps the fastest, per
+process, keyed by the layer's shape.  All tile shapes give bit-identical outputs, so tuning changes
+time only.
+
 Buffers are allocated once here (torch supplies device memory); ``forward`` only issues
 library calls, so it allocates nothing and does not synchronise.  Expert weights are
 passed packed (``pack_expert_weights``, once, when they are loaded).
@@ -38,6 +46,10 @@ import torch
 
 from . import _lib as L
 
+# Measured tile shapes, keyed by everything that decides a layer's GEMM problems and the device:
+# (T, d, N, M, K', F, F_shared, dtype, e_lo, e_hi, gather, device name, CUs) -> (gate/up, down).
+_TILE_CACHE: dict = {}
+
 
 class MoGELayer:
     def __init__(self, T: int, d: int, N: int, M: int, Kp: int, F: int, F_shared: int = 0, dtype: str = "bf16",
@@ -46,6 +58,9 @@ class MoGELayer:
         self.dtype_code = L.BF16 if dtype == "bf16" else L.F32
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.shape = L.Shape(T, d, N, M, Kp, F, self.dtype_code, tiles)
+        # the two expert GEMMs' calls carry their own tile shape (tune_tiles may set them apart)
+        self.shape_up = L.Shape(T, d, N, M, Kp, F, self.dtype_code, tiles)
+        self.shape_down = L.Shape(T, d, N, M, Kp, F, self.dtype_code, tiles)
         st = L.validate(self.shape)
         if st != 0:
             raise L.MogeError("moge_validate", st, L.last_error())
@@ -164,19 +179,19 @@ class MoGELayer:
                 mk("dispatch")
                 side_comparator()
                 Fs = self.F_shared
-                L.expert_gate_up_gather(s, x, self.perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate,
-                                        w_up, self.h, Fs, shared[0] if Fs else None, shared[1] if Fs else None,
-                                        self.sh if Fs else None, stream)
+                L.expert_gate_up_gather(self.shape_up, x, self.perm, self.offsets, self.e_lo, self.e_hi,
+                                        self.rows_cap, w_gate, w_up, self.h, Fs, shared[0] if Fs else None,
+                                        shared[1] if Fs else None, self.sh if Fs else None, stream)
                 mk("gate_up")
                 if Fs:
-                    L.expert_down_with_shared(s, Fs, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down,
-                                              self.o, self.sh, shared[2], self.so, stream)
+                    L.expert_down_with_shared(self.shape_down, Fs, self.h, self.offsets, self.e_lo, self.e_hi,
+                                              self.rows_cap, w_down, self.o, self.sh, shared[2], self.so, stream)
                 elif self.fuse_combine:
-                    L.expert_down_combine(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down,
-                                          self.perm, self.gate, self.y, stream)
+                    L.expert_down_combine(self.shape_down, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap,
+                                          w_down, self.perm, self.gate, self.y, stream)
                 else:
-                    L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o,
-                                  stream)
+                    L.expert_down(self.shape_down, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down,
+                                  self.o, stream)
                 mk("down")
             else:
                 L.dispatch(s, L.ROUTE_GROUPED, self.idx, x, self.e_lo, self.e_hi, self.rows_cap, self.counts,
@@ -186,23 +201,24 @@ class MoGELayer:
                 side_comparator()
                 if self.F_shared and self.fuse_shared:
                     # routed and shared experts in the same two launches
-                    L.expert_gate_up_with_shared(s, self.F_shared, self.x_perm, self.offsets, self.e_lo,
-                                                 self.e_hi, self.rows_cap, w_gate, w_up, self.h, self.x_tiled,
-                                                 shared[0], shared[1], self.sh, stream)
+                    L.expert_gate_up_with_shared(self.shape_up, self.F_shared, self.x_perm, self.offsets,
+                                                 self.e_lo, self.e_hi, self.rows_cap, w_gate, w_up, self.h,
+                                                 self.x_tiled, shared[0], shared[1], self.sh, stream)
                     mk("gate_up")
-                    L.expert_down_with_shared(s, self.F_shared, self.h, self.offsets, self.e_lo, self.e_hi,
-                                              self.rows_cap, w_down, self.o, self.sh, shared[2], self.so, stream)
+                    L.expert_down_with_shared(self.shape_down, self.F_shared, self.h, self.offsets, self.e_lo,
+                                              self.e_hi, self.rows_cap, w_down, self.o, self.sh, shared[2], self.so,
+                                              stream)
                     mk("down")
                 else:
-                    L.expert_gate_up(s, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_gate,
-                                     w_up, self.h, stream)
+                    L.expert_gate_up(self.shape_up, self.x_perm, self.offsets, self.e_lo, self.e_hi, self.rows_cap,
+                                     w_gate, w_up, self.h, stream)
                     mk("gate_up")
                     if self.fuse_combine:
-                        L.expert_down_combine(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down,
-                                              self.perm, self.gate, self.y, stream)
+                        L.expert_down_combine(self.shape_down, self.h, self.offsets, self.e_lo, self.e_hi,
+                                              self.rows_cap, w_down, self.perm, self.gate, self.y, stream)
                     else:
-                        L.expert_down(s, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap, w_down, self.o,
-                                      stream)
+                        L.expert_down(self.shape_down, self.h, self.offsets, self.e_lo, self.e_hi, self.rows_cap,
+                                      w_down, self.o, stream)
                     mk("down")
                     if self.F_shared:
                         L.grouped_ffn(self.sshape, self.x_tiled, self.soffsets, 0, 1, self.T, shared[0], shared[1],
@@ -221,6 +237,52 @@ class MoGELayer:
                 comparator(main)
             mk("global_comparator")
         return None if self.routing_only else self.y
+
+    def tune_tiles(self, x, w_router, bias, w_gate, w_up, w_down, shared=None, reps: int = 5) -> tuple:
+        """Sets the gate/up and down GEMMs' tile shapes to the fastest measured on these inputs
+        (bf16 layers with expert FFNs; others keep the library's choice) and returns them.  Each
+        candidate runs ``reps`` whole forwards; a GEMM's time is the median between its stream
+        events.  The result is cached per process under the layer's shape and device, so another
+        layer of the same shape reuses it without timing.  Synchronises; not for graph capture."""
+        if self.routing_only or self.dtype_code != L.BF16:
+            return (self.shape_up.tiles, self.shape_down.tiles)
+        dev = self.idx.device
+        props = torch.cuda.get_device_properties(dev)
+        key = (self.T, self.d, self.N, self.M, self.Kp, self.F, self.F_shared, self.dtype_code, self.e_lo,
+               self.e_hi, self.gather, props.name, props.multi_processor_count)
+        if key not in _TILE_CACHE:
+            stream = torch.cuda.current_stream(dev)
+
+            def gemm_us(name):
+                ts = []
+                for _ in range(reps):
+                    marks = []
+
+                    def rec(n):
+                        ev = torch.cuda.Event(enable_timing=True)
+                        ev.record(stream)
+                        marks.append((n, ev))
+                    self.forward(x, w_router, bias, w_gate, w_up, w_down, shared, mark=rec)
+                    torch.cuda.synchronize(dev)
+                    names = [n for n, _ in marks]
+                    i = names.index(name)
+                    ts.append(marks[i - 1][1].elapsed_time(marks[i][1]))
+                return sorted(ts)[len(ts) // 2]
+
+            best = []
+            for shp, name, cands in ((self.shape_up, "gate_up", (L.TILES_TALL, L.TILES_WIDE, L.TILES_BALANCED)),
+                                     (self.shape_down, "down", (L.TILES_TALL, L.TILES_WIDE))):
+                keep = shp.tiles
+                times = {}
+                for c in cands:
+                    shp.tiles = c
+                    self.forward(x, w_router, bias, w_gate, w_up, w_down, shared)  # warm-up of this shape
+                    times[c] = gemm_us(name)
+                shp.tiles = keep
+                best.append(min(times, key=times.get))
+            _TILE_CACHE[key] = tuple(best)
+        self.shape_up.tiles, self.shape_down.tiles = _TILE_CACHE[key]
+        return _TILE_CACHE[key]
 
     def check_scores(self, stream=None) -> None:
         """Raises MogeError (MOGE_ERR_NONFINITE) if the router scores of the last forward hold a NaN

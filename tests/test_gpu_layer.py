@@ -214,3 +214,35 @@ def _random_shapes(n, seed):
 def test_layer_random_shapes(gpu, w):
     # every token against the oracle on seeded shapes drawn across the validated range
     check_layer(w)
+
+
+TUNE_CASES = [W.variant(W.decode(), name="tune_T300_d256_shared", T=300, d=256, N=32, M=4, Kp=1, F=136, F_shared=264,
+                        std_shared_down=0.02),
+              W.variant(W.decode(), name="tune_T200_d264_copy", T=200, d=264, N=16, M=4, Kp=2, F=200)]
+
+
+@pytest.mark.parametrize("w", TUNE_CASES, ids=lambda w: w.name)
+def test_tune_tiles_measured_choice(gpu, w):
+    # the measured tile choice (per GEMM, cached per shape) changes the kernels' tiles only: y stays
+    # bit-identical to the library's own choice, and a second layer of the shape reuses the result
+    import mixture_grouped_experts_amd.layer as layer_mod
+    print(f"[tune tiles] {w.name}", flush=True)
+    _, ref_layer, y_ref = run_layer(w)
+    layer = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi)
+    dv = packed_inputs(w, layer)
+    args = (dv.x, dv.w_router, dv.bias, dv.w_gate, dv.w_up, dv.w_down, dv.shared)
+    before = len(layer_mod._TILE_CACHE)
+    up, down = layer.tune_tiles(*args, reps=3)
+    assert up in (moge.TILES_TALL, moge.TILES_WIDE, moge.TILES_BALANCED)
+    assert down in (moge.TILES_TALL, moge.TILES_WIDE)
+    assert (layer.shape_up.tiles, layer.shape_down.tiles) == (up, down)
+    assert len(layer_mod._TILE_CACHE) == before + 1
+    y = layer.forward(*args)
+    torch.cuda.synchronize()
+    assert H.same_bits(y, y_ref)
+    other = MoGELayer(w.T, w.d, w.N, w.M, w.Kp, w.F, w.F_shared, w.dtype, w.e_lo, w.e_hi)
+    calls = []
+    real_forward = other.forward
+    other.forward = lambda *a, **k: (calls.append(1), real_forward(*a, **k))[1]
+    assert other.tune_tiles(*args) == (up, down) and not calls      # cached: nothing is timed again
+    assert len(layer_mod._TILE_CACHE) == before + 1
