@@ -369,6 +369,13 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
   // epilogue (rows of dead blocks are never stored).  GEMM 1 writes the tiled h
   // (NPAD = F rounded up to 32 columns; its padding columns come out as zeros from
   // the zero rows of the packed weights); GEMM 2 writes row-major [row][NOUT].
+  // h leaves with the non-temporal hint: its writes, spread over the kernel, otherwise
+  // break up the weight read stream (measured, same box: 256-token decode gate/up 279 ->
+  // 257 us, 8192-token Ultra 4.47 -> 4.36 ms; h stores aimed at one L2-resident block
+  // gave the same time as the hinted ones, so the cost was the DRAM writes, not the
+  // instructions).  GEMM 2's expert outputs take the hint only in the wide shape (few
+  // rows per expert, a weight stream, decode down 148 -> 134 us): with the tall shape
+  // the combine that reads them slowed (Ultra 244 -> 266 us) more than the GEMM gained.
   if (!SWIGLU && !op.Y && (NOUT & 7) == 0) {
     // GEMM 2 through LDS (the ring is idle now): each wave writes its 64 columns of up
     // to kPassBlocks row blocks into its own 10 KiB of LDS as 128-byte rows (16-byte
@@ -401,7 +408,11 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wl + r * 128 + ((c8 ^ (r & 7)) << 4));
         const int trow = (wm + WMG * (p0 + (r >> 4))) * 16 + (r & 15);
         const int col = n0 + wn * 64 + c8 * 8;
-        if (trow < mrows && col < NOUT) *reinterpret_cast<u32x4_t*>(C + (row0 + trow) * NOUT + col) = v;
+        if (trow < mrows && col < NOUT) {
+          u32x4_t* dst = reinterpret_cast<u32x4_t*>(C + (row0 + trow) * NOUT + col);
+          if (WMG == 1) __builtin_nontemporal_store(v, dst);  // the wide shape: a weight stream (see below)
+          else *dst = v;
+        }
       }
       __builtin_amdgcn_s_waitcnt(lgkm0_imm());
       __builtin_amdgcn_wave_barrier();
@@ -447,7 +458,8 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
           const u32x4_t v =
               *reinterpret_cast<const u32x4_t*>(wl + (t - p0) * 1024 + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
           const int trow = (wm + WMG * t) * 16 + r;
-          if (trow < mrows) *reinterpret_cast<u32x4_t*>(C + tiled_index(row0 + trow, col0 + c * 8, NPAD)) = v;
+          if (trow < mrows)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(C + tiled_index(row0 + trow, col0 + c * 8, NPAD)));
         }
         __builtin_amdgcn_s_waitcnt(lgkm0_imm());
         __builtin_amdgcn_wave_barrier();
