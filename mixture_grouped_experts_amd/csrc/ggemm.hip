@@ -410,7 +410,7 @@ __device__ __forceinline__ void tile_compute(const GemmOperands& op, char* __res
         const int col = n0 + wn * 64 + c8 * 8;
         if (trow < mrows && col < NOUT) {
           u32x4_t* dst = reinterpret_cast<u32x4_t*>(C + (row0 + trow) * NOUT + col);
-          if (WMG == 1) __builtin_nontemporal_store(v, dst);  // the wide shape: a weight stream (see below)
+          if (WMG == 1) __builtin_nontemporal_store(v, dst);  // the wide shape: a weight stream (note above)
           else *dst = v;
         }
       }
