@@ -1103,20 +1103,23 @@ __host__ __forceinline__ RoutePlan route_plan(const moge_shape_t& s) {
   return S > 1 ? RoutePlan{1, S} : RoutePlan{0, 1};
 }
 
-// The split kernel's partial sums -> scores -> the choices.  8 tokens per workgroup (many
+// The split kernel's partial sums -> scores -> the choices.  TPW tokens per workgroup (many
 // workgroups, so every CU has several tiles' loads in flight): the S slices of each score
 // are added in slice order (bit-identical results run to run), plus the bias, into an LDS
-// tile [8][N + 1]; then the choice: the rank count (KL = kListRank, at most 64 experts: each
-// of the 4 waves takes 2 of the tokens) or the common epilogue.
+// tile [TPW][N + 1]; then the choice: the rank count (KL = kListRank, at most 64 experts: the
+// 4 waves take the tokens in turn) or the common epilogue.  TPW = 8, or 2 for the rank count
+// on small batches, whose few workgroups otherwise wait on their loads one after another.
 constexpr int kReduceTokens = 8;
-template <int KL>
+constexpr int kReduceTokensSmall = 2;
+constexpr int64_t kReduceSmallT = 2048;  // batches up to this many tokens take kReduceTokensSmall
+template <int KL, int TPW>
 __global__ __launch_bounds__(256) void route_reduce_kernel(int64_t T, int N, int M, int k, int S,
                                                            const float* __restrict__ part,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ logits_out, int32_t* __restrict__ idx,
                                                            float* __restrict__ gate, int32_t* __restrict__ gidx,
                                                            float* __restrict__ ggate) {
-  constexpr int tpw = kReduceTokens;
+  constexpr int tpw = TPW;
   constexpr int PU = 16;  // slices of one chunk in flight together
   __shared__ float lt[tpw * (kMaxExperts + 1)];
   const int ld = N + 1;
@@ -1291,16 +1294,24 @@ static moge_status_t route_impl(const moge_shape_t* shape, const void* x, const 
                                               stream);
     }
     if (st == MOGE_OK && pl.kind != 0 && s.N <= 64 && kl != 0) {  // the slices' sum, the rank-count choice
-      const int tpw = kReduceTokens;
-      hipLaunchKernelGGL(route_reduce_kernel<kListRank>, dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256),
-                         0, stream, (int64_t)s.T, s.N, s.M, s.k_per_group, pl.S, part, bias, logits, idx, gate, gidx,
-                         ggate);
+      if (s.T <= kReduceSmallT) {
+        const int tpw = kReduceTokensSmall;
+        hipLaunchKernelGGL((route_reduce_kernel<kListRank, kReduceTokensSmall>),
+                           dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256), 0, stream, (int64_t)s.T, s.N,
+                           s.M, s.k_per_group, pl.S, part, bias, logits, idx, gate, gidx, ggate);
+      } else {
+        const int tpw = kReduceTokens;
+        hipLaunchKernelGGL((route_reduce_kernel<kListRank, kReduceTokens>),
+                           dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256), 0, stream, (int64_t)s.T, s.N,
+                           s.M, s.k_per_group, pl.S, part, bias, logits, idx, gate, gidx, ggate);
+      }
       st = check_launch("route_reduce_kernel");
     } else if (st == MOGE_OK && pl.kind != 0) {  // the slices' partial sums -> scores -> the choices
       const int tpw = kReduceTokens;
       st = with_list_len(kl, [&](auto klc) {
         constexpr int KL = decltype(klc)::value;
-        hipLaunchKernelGGL(route_reduce_kernel<KL>, dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)), dim3(256), 0,
+        hipLaunchKernelGGL((route_reduce_kernel<KL, kReduceTokens>), dim3((unsigned)(((int64_t)s.T + tpw - 1) / tpw)),
+                           dim3(256), 0,
                            stream, (int64_t)s.T, s.N, s.M, s.k_per_group, pl.S, part, bias, logits, idx, gate, gidx,
                            ggate);
         return check_launch("route_reduce_kernel");
